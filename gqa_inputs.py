@@ -1,0 +1,142 @@
+"""Seeded synthetic inputs for the grouped-query attention forward pass.
+
+This module is shared by the CPU oracle's tests, the GPU parity tests, the
+smoke check and the benchmark. It draws random numbers and names workload
+shapes; it holds none of the attention arithmetic.
+
+Recipe: every tensor (q=0, k=1, v=2) of every batch element b has its own
+CPU generator seeded with ``seed * 1_000_000 + tensor * 100_000 + b``. A
+draw is ``randn([S, H, d], float32)`` rounded to bfloat16 (round to nearest
+even). Any batch element can therefore be regenerated on its own, which is
+what the full-size parity checks do.
+
+The workload shapes follow the pages: Hq=6/Hk=2 is the worked head-grouping
+example (Stable-Diffusion GQA guide, "core principle" section; batch-sensitivity
+article, "technical principle" section), Hq=32/Hk=8/d=128 is the Llama-2 GQA
+configuration (Llama-2 GQA article, section 3.1) and the H100 batch sweep
+(GQA throughput rise-and-fall article, "symptom" table), length 77 with batch
+16384 // 77 = 212 is the text-encoder case of the batch formula
+(Stable-Diffusion GQA guide, "dynamic batch scheduling" section).
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import Iterable, Optional, Sequence
+
+import torch
+
+TENSOR_Q, TENSOR_K, TENSOR_V = 0, 1, 2
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    Sq: int
+    Sk: int
+    Hq: int
+    Hk: int
+    d: int
+    causal: bool
+    seed: int
+    # (pack_gqa, num_splits) variants the parity tests run on this workload
+    variants: tuple = field(default=((1, 1), (0, 1)))
+
+    @property
+    def scale(self) -> float:
+        """Default softmax scale 1/sqrt(d), rounded to fp32 (the ABI passes fp32)."""
+        return fp32(1.0 / math.sqrt(self.d))
+
+    @property
+    def flops(self) -> float:
+        """4*B*Hq*Sq*Sk*d, halved when causal (the metric's formula)."""
+        f = 4.0 * self.B * self.Hq * self.Sq * self.Sk * self.d
+        return f / 2 if self.causal else f
+
+    @property
+    def io_bytes(self) -> int:
+        """Q + K + V + O (bf16) + LSE (fp32), each touched once."""
+        q = self.B * self.Sq * self.Hq * self.d * 2
+        kv = 2 * self.B * self.Sk * self.Hk * self.d * 2
+        lse = self.B * self.Hq * self.Sq * 4
+        return 2 * q + kv + lse
+
+    def with_(self, **kw) -> "Workload":
+        d = dict(self.__dict__)
+        d.update(kw)
+        return Workload(**d)
+
+
+def fp32(x: float) -> float:
+    """Round a Python float to the nearest fp32 value."""
+    return float(torch.tensor(x, dtype=torch.float32).item())
+
+
+# The five workloads: tiny, Llama-2-7B prefill, the batch sweep, short ragged
+# sequences and split-KV decode.
+TINY = Workload("tiny_hq6_hk2_d64_s128", 1, 128, 128, 6, 2, 64, True, 1001,
+                ((1, 1), (0, 1), (1, 2), (0, 2)))
+LLAMA_PREFILL = Workload("llama2_prefill_b4_s2048", 4, 2048, 2048, 32, 8, 128, True, 2001,
+                         ((1, 1), (0, 1)))
+
+
+def sweep(B: int) -> Workload:
+    return Workload(f"sweep_b{B}_s2048", B, 2048, 2048, 32, 8, 128, True, 3000 + B,
+                    ((1, 1), (0, 4)))
+
+
+SWEEP_BATCHES = (16, 64, 128, 256)
+RAGGED = Workload("ragged_b212_s77", 212, 77, 77, 6, 2, 64, False, 4001, ((1, 1), (0, 1)))
+DECODE = Workload("decode_b64_sk8192", 64, 1, 8192, 32, 8, 128, False, 5001,
+                  ((1, 1), (1, 4), (1, 8), (0, 4)))
+
+ALL = [TINY, TINY.with_(causal=False, name="tiny_hq6_hk2_d64_s128_noncausal"), LLAMA_PREFILL] + \
+      [sweep(b) for b in SWEEP_BATCHES] + [RAGGED, DECODE]
+
+
+def _gen(seed: int, tensor: int, b: int, shape: Sequence[int], std: float = 1.0) -> torch.Tensor:
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed * 1_000_000 + tensor * 100_000 + b)
+    x = torch.randn(list(shape), generator=g, dtype=torch.float32)
+    if std != 1.0:
+        x = x * std
+    return x.to(torch.bfloat16)
+
+
+def batch_slice(seed: int, b: int, Sq: int, Sk: int, Hq: int, Hk: int, d: int, std: float = 1.0):
+    """q [Sq,Hq,d], k [Sk,Hk,d], v [Sk,Hk,d] bf16 CPU tensors of batch element b."""
+    q = _gen(seed, TENSOR_Q, b, (Sq, Hq, d), std)
+    k = _gen(seed, TENSOR_K, b, (Sk, Hk, d), std)
+    v = _gen(seed, TENSOR_V, b, (Sk, Hk, d))
+    return q, k, v
+
+
+def make_qkv(w: Workload, batches: Optional[Iterable[int]] = None, std: float = 1.0):
+    """Full bf16 CPU tensors q [B,Sq,Hq,d], k/v [B,Sk,Hk,d] (or only the listed batches)."""
+    bs = list(range(w.B)) if batches is None else list(batches)
+    q = torch.empty((len(bs), w.Sq, w.Hq, w.d), dtype=torch.bfloat16)
+    k = torch.empty((len(bs), w.Sk, w.Hk, w.d), dtype=torch.bfloat16)
+    v = torch.empty((len(bs), w.Sk, w.Hk, w.d), dtype=torch.bfloat16)
+    for i, b in enumerate(bs):
+        q[i], k[i], v[i] = batch_slice(w.seed, b, w.Sq, w.Sk, w.Hq, w.Hk, w.d, std)
+    return q, k, v
+
+
+def make_qkv_device(w: Workload, device, std: float = 1.0):
+    """Generate batch by batch on the CPU and copy into device tensors."""
+    q = torch.empty((w.B, w.Sq, w.Hq, w.d), dtype=torch.bfloat16, device=device)
+    k = torch.empty((w.B, w.Sk, w.Hk, w.d), dtype=torch.bfloat16, device=device)
+    v = torch.empty((w.B, w.Sk, w.Hk, w.d), dtype=torch.bfloat16, device=device)
+    for b in range(w.B):
+        qb, kb, vb = batch_slice(w.seed, b, w.Sq, w.Sk, w.Hq, w.Hk, w.d, std)
+        q[b].copy_(qb)
+        k[b].copy_(kb)
+        v[b].copy_(vb)
+    return q, k, v
+
+
+def random_bf16(seed: int, shape: Sequence[int], std: float = 1.0) -> torch.Tensor:
+    """One seeded bf16 tensor of any shape (edge-case tests)."""
+    return _gen(seed, 0, 0, shape, std)
