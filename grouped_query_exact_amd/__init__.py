@@ -1,0 +1,140 @@
+"""Exact grouped-query attention forward pass on AMD MI355X (gfx950).
+
+A thin ctypes binding over the C-ABI library ``libgqa_attn.so`` built from
+``csrc/`` (declared in ``include/gqa_attn.h``). The functions keep the C
+names; they only turn torch tensors into pointers and sizes. Every step of
+the computation runs in the library's HIP kernels: there is no fallback, and
+a missing library raises at the first call.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+__all__ = ["GqaAttnError", "gqa_attn_fwd", "gqa_attn_func", "gqa_attn_choose", "gqa_attn_plan",
+           "gqa_attn_strerror", "library_path", "load_library",
+           "GQA_OK", "GQA_ERR_INVALID_ARG", "GQA_ERR_UNSUPPORTED", "GQA_ERR_NOMEM", "GQA_ERR_HIP"]
+
+GQA_OK = 0
+GQA_ERR_INVALID_ARG = -1
+GQA_ERR_UNSUPPORTED = -2
+GQA_ERR_NOMEM = -3
+GQA_ERR_HIP = -4
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, "libgqa_attn.so")
+
+
+class _Plan(ctypes.Structure):
+    _fields_ = [("pack_gqa", ctypes.c_int), ("num_splits", ctypes.c_int), ("block_m", ctypes.c_int),
+                ("block_n", ctypes.c_int), ("row_tiles", ctypes.c_int), ("key_tiles", ctypes.c_int),
+                ("grid", ctypes.c_longlong), ("combine_grid", ctypes.c_longlong),
+                ("workspace_bytes", ctypes.c_longlong)]
+
+
+class GqaAttnError(RuntimeError):
+    def __init__(self, status: int, what: str = ""):
+        self.status = status
+        super().__init__(f"gqa_attn: {gqa_attn_strerror(status)} (status {status}){': ' + what if what else ''}")
+
+
+def load_library():
+    """Load libgqa_attn.so (once). Raises if it has not been built."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m grouped_query_exact_amd.build`")
+    lib = ctypes.CDLL(path)
+    c_int, c_float, vp = ctypes.c_int, ctypes.c_float, ctypes.c_void_p
+    lib.gqa_attn_fwd.argtypes = [vp, vp, vp, vp, vp] + [c_int] * 7 + [c_float, c_int, c_int, vp]
+    lib.gqa_attn_fwd.restype = c_int
+    lib.gqa_attn_choose.argtypes = [c_int] * 8 + [ctypes.POINTER(c_int), ctypes.POINTER(c_int)]
+    lib.gqa_attn_choose.restype = c_int
+    lib.gqa_attn_plan.argtypes = [c_int] * 10 + [ctypes.POINTER(_Plan)]
+    lib.gqa_attn_plan.restype = c_int
+    lib.gqa_attn_strerror.argtypes = [c_int]
+    lib.gqa_attn_strerror.restype = ctypes.c_char_p
+    _LIB = lib
+    return lib
+
+
+def gqa_attn_strerror(status: int) -> str:
+    return load_library().gqa_attn_strerror(int(status)).decode()
+
+
+def gqa_attn_choose(B: int, Sq: int, Sk: int, Hq: int, Hk: int, d: int, causal: bool,
+                    num_cus: int = 0) -> Tuple[int, int]:
+    """The library's heuristic: (pack_gqa, num_splits)."""
+    pk, ns = ctypes.c_int(), ctypes.c_int()
+    st = load_library().gqa_attn_choose(B, Sq, Sk, Hq, Hk, d, int(bool(causal)), num_cus,
+                                        ctypes.byref(pk), ctypes.byref(ns))
+    if st != GQA_OK:
+        raise GqaAttnError(st)
+    return pk.value, ns.value
+
+
+def gqa_attn_plan(B: int, Sq: int, Sk: int, Hq: int, Hk: int, d: int, causal: bool,
+                  pack_gqa: int = -1, num_splits: int = 0, num_cus: int = 0) -> dict:
+    """The launch plan gqa_attn_fwd would use for these sizes."""
+    p = _Plan()
+    st = load_library().gqa_attn_plan(B, Sq, Sk, Hq, Hk, d, int(bool(causal)), pack_gqa, num_splits,
+                                      num_cus, ctypes.byref(p))
+    if st != GQA_OK:
+        raise GqaAttnError(st)
+    return {name: getattr(p, name) for name, _ in _Plan._fields_}
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def gqa_attn_fwd(q, k, v, out, lse, causal: bool, scale: float, pack_gqa: int = -1,
+                 num_splits: int = 0, stream=None) -> None:
+    """Run the forward pass into caller-provided ``out`` (and ``lse`` or None).
+
+    q/out: [B, Sq, Hq, d] bf16, k/v: [B, Sk, Hk, d] bf16, lse: [B, Hq, Sq] fp32,
+    all contiguous on the same GPU. ``stream`` defaults to torch's current stream.
+    """
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+        if t.dtype != torch.bfloat16 or not t.is_contiguous() or t.dim() != 4 or not t.is_cuda:
+            raise ValueError(f"{name} must be a contiguous 4-d bfloat16 GPU tensor")
+    B, Sq, Hq, d = q.shape
+    _, Sk, Hk, _ = k.shape
+    if tuple(k.shape) != (B, Sk, Hk, d) or tuple(v.shape) != tuple(k.shape) or tuple(out.shape) != tuple(q.shape):
+        raise ValueError("shape mismatch between q, k, v and out")
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()
+                            or tuple(lse.shape) != (B, Hq, Sq) or not lse.is_cuda):
+        raise ValueError("lse must be a contiguous [B, Hq, Sq] float32 GPU tensor")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    elif hasattr(stream, "cuda_stream"):
+        stream = stream.cuda_stream
+    with torch.cuda.device(q.device):
+        st = load_library().gqa_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                                         B, Sq, Sk, Hq, Hk, d, int(bool(causal)), float(scale),
+                                         int(pack_gqa), int(num_splits), stream)
+    if st != GQA_OK:
+        raise GqaAttnError(st)
+
+
+def gqa_attn_func(q, k, v, causal: bool = False, softmax_scale: Optional[float] = None,
+                  pack_gqa: int = -1, num_splits: int = 0, return_lse: bool = False):
+    """Allocate the outputs and run gqa_attn_fwd. softmax_scale defaults to 1/sqrt(d)."""
+    import torch
+    B, Sq, Hq, d = q.shape
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d)
+    out = torch.empty_like(q)
+    lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device) if return_lse else None
+    gqa_attn_fwd(q, k, v, out, lse, causal, softmax_scale, pack_gqa, num_splits)
+    return (out, lse) if return_lse else out

@@ -1,0 +1,194 @@
+// C-ABI entry points of the GQA forward library (declared in include/gqa_attn.h).
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <mutex>
+
+#include "../../include/gqa_attn.h"
+#include "host_logic.h"
+#include "kernels.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_count[kMaxDevices];
+std::once_flag g_pool_once[kMaxDevices];
+
+int current_device() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return -1;
+    return dev;
+}
+
+// Compute units of the current device, cached per device. 0 on failure.
+int device_cus(int dev) {
+    if (dev < 0 || dev >= kMaxDevices) return 0;
+    int n = g_cu_count[dev].load(std::memory_order_relaxed);
+    if (n > 0) return n;
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    g_cu_count[dev].store(v, std::memory_order_relaxed);
+    return v;
+}
+
+// Keep freed workspace in the device's default pool so that steady-state
+// calls do not return memory to the driver and allocate it again.
+void keep_pool(int dev) {
+    if (dev < 0 || dev >= kMaxDevices) return;
+    std::call_once(g_pool_once[dev], [dev] {
+        hipMemPool_t pool;
+        if (hipDeviceGetDefaultMemPool(&pool, dev) == hipSuccess) {
+            uint64_t thr = UINT64_MAX;
+            (void)hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &thr);
+        }
+    });
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool log_enabled() {
+    static const bool on = [] {
+        const char* e = std::getenv("GQA_ATTN_LOG");
+        return e && e[0] == '1';
+    }();
+    return on;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gqa_attn_strerror(int status) {
+    switch (status) {
+        case GQA_OK: return "success";
+        case GQA_ERR_INVALID_ARG: return "invalid argument";
+        case GQA_ERR_UNSUPPORTED: return "unsupported head dimension or alignment";
+        case GQA_ERR_NOMEM: return "split-KV workspace allocation failed";
+        case GQA_ERR_HIP: return "HIP runtime or launch error";
+        default: return "unknown status";
+    }
+}
+
+int gqa_attn_choose(int B, int Sq, int Sk, int Hq, int Hk, int d, int causal, int num_cus,
+                    int* pack_gqa, int* num_splits) {
+    if (!pack_gqa || !num_splits) return GQA_ERR_INVALID_ARG;
+    const gqa::Shape s{B, Sq, Sk, Hq, Hk, d, causal ? 1 : 0};
+    const int st = gqa::check_sizes(s, 1.0f, -1, 0);
+    if (st != GQA_OK) return st;
+    if (num_cus <= 0) num_cus = device_cus(current_device());
+    gqa::choose(s, num_cus, pack_gqa, num_splits);
+    return GQA_OK;
+}
+
+int gqa_attn_plan(int B, int Sq, int Sk, int Hq, int Hk, int d, int causal, int pack_gqa,
+                  int num_splits, int num_cus, gqa_attn_plan_t* plan) {
+    if (!plan) return GQA_ERR_INVALID_ARG;
+    const gqa::Shape s{B, Sq, Sk, Hq, Hk, d, causal ? 1 : 0};
+    int st = gqa::check_sizes(s, 1.0f, pack_gqa, num_splits);
+    if (st != GQA_OK) return st;
+    if (num_cus <= 0 && (pack_gqa < 0 || num_splits == 0)) num_cus = device_cus(current_device());
+    gqa::Plan p;
+    st = gqa::make_plan(s, pack_gqa, num_splits, num_cus, &p);
+    if (st != GQA_OK) return st;
+    plan->pack_gqa = p.pack;
+    plan->num_splits = p.ns;
+    plan->block_m = gqa::kBlockM;
+    plan->block_n = gqa::kBlockN;
+    plan->row_tiles = p.row_tiles;
+    plan->key_tiles = p.key_tiles;
+    plan->grid = p.grid;
+    plan->combine_grid = p.combine_grid;
+    plan->workspace_bytes = p.workspace_bytes;
+    return GQA_OK;
+}
+
+int gqa_attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Sq,
+                 int Sk, int Hq, int Hk, int d, int causal, float scale, int pack_gqa, int num_splits,
+                 hipStream_t stream) {
+    try {
+        const gqa::Shape s{B, Sq, Sk, Hq, Hk, d, causal ? 1 : 0};
+        int st = gqa::check_sizes(s, scale, pack_gqa, num_splits);
+        if (st != GQA_OK) return st;
+        if ((long long)B * Sq == 0) return GQA_OK;
+        if (!q || !k || !v || !out) return GQA_ERR_INVALID_ARG;
+        if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return GQA_ERR_UNSUPPORTED;
+
+        const int dev = current_device();
+        if (dev < 0) return GQA_ERR_HIP;
+        int cus = 0;
+        if (pack_gqa < 0 || num_splits == 0) cus = device_cus(dev);
+        gqa::Plan plan;
+        st = gqa::make_plan(s, pack_gqa, num_splits, cus, &plan);
+        if (st != GQA_OK) return st;
+
+        gqa::FwdParams p{};
+        p.q = (const uint16_t*)q;
+        p.k = (const uint16_t*)k;
+        p.v = (const uint16_t*)v;
+        p.o = (uint16_t*)out;
+        p.lse = lse;
+        p.B = B;
+        p.Sq = Sq;
+        p.Sk = Sk;
+        p.Hq = Hq;
+        p.Hk = Hk;
+        p.G = plan.G;
+        p.Gp = plan.Gp;
+        const gqa::FastDiv fd = gqa::make_fastdiv((uint32_t)plan.Gp);
+        p.gmul = fd.mul;
+        p.gshift = fd.shift;
+        p.R = (int)plan.R;
+        p.row_tiles = plan.row_tiles;
+        p.units_per_b = plan.units_per_b;
+        p.ns = plan.ns;
+        p.grid = (int)plan.grid;
+        p.c = (float)(std::fabs((double)scale) * 1.4426950408889634);
+        p.qsign = scale < 0.f ? 0x80008000u : 0u;
+
+        if (log_enabled())
+            std::fprintf(stderr,
+                         "[gqa_attn] B=%d Sq=%d Sk=%d Hq=%d Hk=%d d=%d causal=%d -> pack=%d ns=%d "
+                         "row_tiles=%d key_tiles=%d grid=%lld combine_grid=%lld ws=%lld\n",
+                         B, Sq, Sk, Hq, Hk, d, s.causal, plan.pack, plan.ns, plan.row_tiles, plan.key_tiles,
+                         plan.grid, plan.combine_grid, plan.workspace_bytes);
+
+        if (plan.ns == 1) {
+            hipError_t e = gqa::launch_attention(p, d, s.causal != 0, false, stream);
+            return e == hipSuccess ? GQA_OK : GQA_ERR_HIP;
+        }
+
+        keep_pool(dev);
+        void* ws = nullptr;
+        if (hipMallocAsync(&ws, (size_t)plan.workspace_bytes, stream) != hipSuccess || !ws) {
+            (void)hipGetLastError();
+            return GQA_ERR_NOMEM;
+        }
+        const int64_t rows = (int64_t)B * Sq * Hq;
+        p.opart = (float*)ws;
+        p.lpart = (float*)ws + (int64_t)plan.ns * rows * d;
+        hipError_t e = gqa::launch_attention(p, d, s.causal != 0, true, stream);
+        if (e == hipSuccess) {
+            gqa::CombineParams cp{};
+            cp.opart = p.opart;
+            cp.lpart = p.lpart;
+            cp.o = (uint16_t*)out;
+            cp.lse = lse;
+            cp.rows = rows;
+            cp.ns = plan.ns;
+            cp.Sq = Sq;
+            cp.Hq = Hq;
+            e = gqa::launch_combine(cp, d, plan.combine_grid, stream);
+        }
+        const hipError_t ef = hipFreeAsync(ws, stream);
+        if (e != hipSuccess || ef != hipSuccess) return GQA_ERR_HIP;
+        return GQA_OK;
+    } catch (...) {
+        return GQA_ERR_HIP;
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,395 @@
+// Grouped-query attention forward kernels for gfx950 (MI355X).
+//
+// The attention kernel computes, for one tile of 128 query rows against the
+// keys of one KV head, the exact result of softmax(scale * Q K^T) V with a
+// tiled online softmax (running row maximum and sum) and emits the natural
+// log-sum-exp of every row. Query head h reads KV head h / (Hq/Hk)
+// (batch-sensitivity article, "core design of grouped-query attention").
+// With PackGQA (batch-sensitivity article, "Flash-Attention's PackGQA
+// optimisation"; rise-and-fall tuning article, "root cause") the rows of a
+// tile are the G query heads of one KV group, token-major: packed row r is
+// token r / G, head g*G + r % G. With split-KV ("split + combine",
+// rise-and-fall tuning article, "fix" table) a workgroup handles one part of
+// the tile's keys and writes a normalised fp32 partial and its log-sum-exp;
+// the combine kernel merges the parts with weights exp(LSE_s - LSE).
+//
+// Mapping onto CDNA4:
+//  * 256 threads = 4 wavefronts; wave w owns rows [32w, 32w+32) of the tile.
+//    Lane l owns row (l % 32); lanes l and l+32 share a row and split its
+//    keys (for scores) and its head-dimension columns (for the output).
+//  * Scores are computed transposed, S^T = K Q^T, with
+//    v_mfma_f32_32x32x16_bf16: the A operand is 32 keys read from LDS, the
+//    B operand is the wave's 32 query rows held in registers for the whole
+//    key loop. Each lane then holds 32 scores of its own row, so the row
+//    maximum is 31 in-lane max operations plus one exchange with lane l^32.
+//  * The output is accumulated transposed, O^T += V^T P^T, with the same
+//    MFMA: P^T (bf16) comes straight from the score registers, V^T is read
+//    from a natural-layout V tile in LDS with ds_read_b64_tr_b16.
+//  * K and V tiles travel HBM -> LDS with 16-byte global_load_lds (no VGPR
+//    staging), double-buffered so the next tile streams in during compute.
+//    LDS rows are stored with an XOR swizzle of their 16-byte chunks so the
+//    MFMA operand reads are free of bank conflicts.
+//  * Rows of 32 keys are stored in LDS in the order pi (below) so the score
+//    registers of a lane hold runs of 8 consecutive keys and the output
+//    registers hold runs of 8 consecutive head-dimension columns.
+//  * Online softmax in base 2 with scale*log2(e) folded into one FMA, and a
+//    lazily updated row maximum: the running maximum is only raised (and the
+//    accumulator rescaled) when a row's new maximum exceeds it by more than
+//    2^8. Every row's final O = acc / l uses the same maximum for numerator
+//    and denominator, so the result is the same exact softmax.
+//  * Causal tiles above the diagonal are never loaded; waves whose rows see
+//    none of a tile's keys skip its arithmetic; only boundary tiles evaluate
+//    the mask.
+//  * Workgroup ids are remapped so that consecutive work items (all row tiles
+//    of one batch element and KV group, heaviest causal tiles first) land on
+//    the same XCD and share its L2.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kernels.h"
+
+namespace gqa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+#define LDS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kRescaleThreshold = 8.0f;  // log2 units: rescale when the max grows by > 2^8
+
+__device__ __forceinline__ uint32_t fdiv(uint32_t n, uint32_t mul, uint32_t shift) {
+    return (__umulhi(n, mul) + n) >> shift;
+}
+
+// Position (within a block of 32) of the key stored in LDS row m, chosen so
+// that MFMA result slot i of lane half h holds key 16*(i/8) + 8*h + (i%8).
+__device__ __forceinline__ int pi32(int m) {
+    const int b = m >> 3, h = (m >> 2) & 1, r = m & 3;
+    return ((b >> 1) << 4) | (h << 3) | ((b & 1) << 2) | r;
+}
+
+// 16-byte chunk swizzle of LDS row `row`.
+__device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 3) & 1); }
+
+// Remap a hardware workgroup id (dealt round-robin over the 8 XCDs) to a
+// logical work item so that each XCD receives a contiguous logical range.
+__device__ __forceinline__ int xcd_remap(int bid, int total) {
+    const int per = total >> 3, rem = total & 7;
+    const int x = bid & 7, slot = bid >> 3;
+    return x * per + min(x, rem) + slot;
+}
+
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+template <int D>
+__device__ __forceinline__ void issue_tile(const uint16_t* __restrict__ kbase,
+                                           const uint16_t* __restrict__ vbase, int64_t kv_stride,
+                                           int kv0, int Sk, LDS uint16_t* kt, LDS uint16_t* vt,
+                                           int wave, int lane) {
+    constexpr int NCH = D / 8;                       // 16-byte chunks per row
+    constexpr int NLOAD = kBlockN * NCH / kThreads;  // loads per thread per tensor
+#pragma unroll
+    for (int u = 0; u < NLOAD; ++u) {
+        const int base = (u * 4 + wave) * 64;        // first chunk written by this wave
+        const int ci = base + lane;
+        const int row = ci / NCH;
+        const int phys = ci % NCH;
+        const int logical = phys ^ swz(row);
+        const int key = min(kv0 + row, Sk - 1);
+        const int64_t off = (int64_t)key * kv_stride + logical * 8;
+        __builtin_amdgcn_global_load_lds((const void*)(kbase + off), (LDS void*)(kt + base * 8), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(vbase + off), (LDS void*)(vt + base * 8), 16, 0, 0);
+    }
+}
+
+template <int D, bool CAUSAL, bool SPLIT>
+__global__ __launch_bounds__(256) void attn_fwd_kernel(const FwdParams p) {
+    constexpr int TILE = kBlockN * D;  // elements of one K or V tile
+    __shared__ __attribute__((aligned(16))) uint16_t smem[4 * TILE];
+    LDS uint16_t* lds = (LDS uint16_t*)smem;
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int col = lane & 31, half = lane >> 5;
+
+    // ---- work item
+    const int logical = xcd_remap(blockIdx.x, p.grid);
+    const int s = logical % p.ns;
+    int tmp = logical / p.ns;
+    const int rt = p.row_tiles - 1 - (tmp % p.row_tiles);  // heaviest causal tiles first
+    tmp /= p.row_tiles;
+    const int unit = tmp % p.units_per_b;
+    const int b = tmp / p.units_per_b;
+    const int g = p.Gp > 1 ? unit : unit / p.G;   // KV head
+    const int h0 = p.Gp > 1 ? unit * p.G : unit;  // first query head of the tile
+    const int r0 = rt * kBlockM;
+
+    // ---- this lane's row: token ti, head hh
+    const int r = r0 + wave * 32 + col;
+    const bool row_valid = r < p.R;
+    const int rc = min(r, p.R - 1);
+    const int ti = (int)fdiv((uint32_t)rc, p.gmul, p.gshift);
+    const int hh = h0 + (rc - ti * p.Gp);
+    const int koff = p.Sk - p.Sq;  // bottom-right causal offset
+
+    // ---- Q rows -> registers (B operand of S^T = K Q^T)
+    bf16x8 qreg[D / 16];
+    {
+        const uint16_t* qrow = p.q + (((int64_t)b * p.Sq + ti) * p.Hq + hh) * D;
+#pragma unroll
+        for (int dc = 0; dc < D / 16; ++dc) {
+            u32x4 w = *(const u32x4*)(qrow + dc * 16 + half * 8);
+            w ^= p.qsign;
+            qreg[dc] = __builtin_bit_cast(bf16x8, w);
+        }
+    }
+
+    // ---- key tile range of this work item
+    const int r_last = min(r0 + kBlockM, p.R) - 1;
+    const int i_max = (int)fdiv((uint32_t)r_last, p.gmul, p.gshift);
+    int kv_end = p.Sk;
+    if (CAUSAL) kv_end = min(p.Sk, i_max + koff + 1);
+    const int T = kv_end > 0 ? (kv_end + kBlockN - 1) / kBlockN : 0;
+    int t_begin = 0, t_end = T;
+    if (SPLIT) {
+        t_begin = (int)(((int64_t)s * T) / p.ns);
+        t_end = (int)(((int64_t)(s + 1) * T) / p.ns);
+    }
+
+    // rows of this wave: tokens [iw_min, iw_max]
+    const int rw0 = r0 + wave * 32;
+    const bool wave_active = rw0 < p.R;
+    const int iw_min = (int)fdiv((uint32_t)min(rw0, p.R - 1), p.gmul, p.gshift);
+    const int iw_max = (int)fdiv((uint32_t)(min(rw0 + 32, p.R) - 1), p.gmul, p.gshift);
+
+    const int64_t kv_stride = (int64_t)p.Hk * D;
+    const uint16_t* kbase = p.k + ((int64_t)b * p.Sk * p.Hk + g) * D;
+    const uint16_t* vbase = p.v + ((int64_t)b * p.Sk * p.Hk + g) * D;
+
+    f32x16 oacc[D / 32];
+#pragma unroll
+    for (int cb = 0; cb < D / 32; ++cb) oacc[cb] = f32x16{};
+    float m_run = -__builtin_inff();  // running max, scaled log2 units
+    float l_run = 0.f;                // this lane's partial row sum
+    const float c = p.c;
+
+    if (t_begin < t_end)
+        issue_tile<D>(kbase, vbase, kv_stride, t_begin * kBlockN, p.Sk, lds, lds + TILE, wave, lane);
+
+    for (int t = t_begin; t < t_end; ++t) {
+        const int buf = (t - t_begin) & 1;
+        LDS uint16_t* kt = lds + buf * 2 * TILE;
+        LDS uint16_t* vt = kt + TILE;
+        wait_vmem();
+        __syncthreads();
+        if (t + 1 < t_end) {
+            LDS uint16_t* kn = lds + (buf ^ 1) * 2 * TILE;
+            issue_tile<D>(kbase, vbase, kv_stride, (t + 1) * kBlockN, p.Sk, kn, kn + TILE, wave, lane);
+        }
+        const int kv0 = t * kBlockN;
+        if (!wave_active) continue;
+        if (CAUSAL && kv0 > iw_max + koff) continue;  // no row of this wave sees these keys
+
+        // ---- S^T = K Q^T: two blocks of 32 keys
+        f32x16 sacc[2];
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+            sacc[mb] = f32x16{};
+            const int krow = mb * 32 + pi32(col);
+            const LDS uint16_t* kr = kt + krow * D;
+            const int sw = swz(krow);
+#pragma unroll
+            for (int dc = 0; dc < D / 16; ++dc) {
+                const int ch = (2 * dc + half) ^ sw;
+                const bf16x8 a = *(const LDS bf16x8*)(kr + ch * 8);
+                sacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[dc], sacc[mb], 0, 0, 0);
+            }
+        }
+
+        // ---- mask (boundary tiles only)
+        const bool need_mask = (kv0 + kBlockN > p.Sk) || (CAUSAL && kv0 + kBlockN - 1 > iw_min + koff);
+        const int jlim = CAUSAL ? min(p.Sk - 1, ti + koff) : p.Sk - 1;  // last visible key of this row
+        float mx = -__builtin_inff();
+        if (need_mask) {
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int key = kv0 + mb * 32 + ((i >> 3) << 4) + half * 8 + (i & 7);
+                    if (key > jlim) sacc[mb][i] = -__builtin_inff();
+                }
+        }
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[mb][i]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+
+        // ---- lazy running-max update
+        const float mxs = (mx == -__builtin_inff()) ? -__builtin_inff() : mx * c;
+        float alpha = 1.f;
+        if (mxs > m_run + kRescaleThreshold) {
+            alpha = __builtin_amdgcn_exp2f(m_run - mxs);  // exp2(-inf) = 0 on the first update
+            m_run = mxs;
+        }
+        if (__builtin_amdgcn_read_exec() & __ballot(alpha != 1.f)) {
+            l_run *= alpha;
+#pragma unroll
+            for (int cb = 0; cb < D / 32; ++cb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) oacc[cb][i] *= alpha;
+        }
+        const float moff = (m_run == -__builtin_inff()) ? 0.f : m_run;
+
+        // ---- P = exp2(s*c - m), row sum, bf16 pack (B operand of O^T += V^T P^T)
+        bf16x8 pk[4];
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mb][i], c, -moff));
+                if (need_mask) {
+                    const int key = kv0 + mb * 32 + ((i >> 3) << 4) + half * 8 + (i & 7);
+                    if (key > jlim) e = 0.f;
+                }
+                l_run += e;
+                pk[mb * 2 + (i >> 3)][i & 7] = (__bf16)e;
+            }
+
+        // ---- O^T += V^T P^T
+        {
+            const int u = lane & 15, qq = (lane >> 4) & 1;
+            const int rho = ((u & 1) << 1) | ((u >> 1) & 1);  // 0,2,1,3
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+                for (int cb = 0; cb < D / 32; ++cb) {
+                    s16x4 part[2];
+#pragma unroll
+                    for (int rr = 0; rr < 2; ++rr) {
+                        const int vrow = kk * 16 + half * 8 + rr * 4 + (u >> 2);
+                        const int vcol = cb * 32 + qq * 16 + rho * 4;
+                        const int ch = (vcol >> 3) ^ swz(vrow);
+                        const LDS s16x4* a = (const LDS s16x4*)(vt + vrow * D + ch * 8 + (vcol & 7));
+                        part[rr] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS s16x4*)a);
+                    }
+                    const s16x8 av = __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7);
+                    oacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), pk[kk],
+                                                                         oacc[cb], 0, 0, 0);
+                }
+            }
+        }
+    }
+
+    // ---- epilogue
+    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    const bool live = l_tot > 0.f;
+    const float inv = live ? 1.f / l_tot : 0.f;
+    const float lse_val = live ? (m_run + __log2f(l_tot)) * kLn2 : -__builtin_inff();
+    const int64_t grow = ((int64_t)b * p.Sq + ti) * p.Hq + hh;  // row of [B, Sq, Hq]
+    if (!SPLIT) {
+        if (row_valid) {
+            uint16_t* orow = p.o + grow * D;
+#pragma unroll
+            for (int cb = 0; cb < D / 32; ++cb)
+#pragma unroll
+                for (int run = 0; run < 2; ++run) {
+                    bf16x8 ov;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) ov[i] = (__bf16)(oacc[cb][run * 8 + i] * inv);
+                    *(bf16x8*)(orow + cb * 32 + run * 16 + half * 8) = ov;
+                }
+            if (half == 0 && p.lse) p.lse[((int64_t)b * p.Hq + hh) * p.Sq + ti] = lse_val;
+        }
+    } else {
+        if (row_valid) {
+            const int64_t rows = (int64_t)p.B * p.Sq * p.Hq;
+            float* orow = p.opart + ((int64_t)s * rows + grow) * D;
+#pragma unroll
+            for (int cb = 0; cb < D / 32; ++cb)
+#pragma unroll
+                for (int run = 0; run < 2; ++run) {
+                    f32x4 v0, v1;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        v0[i] = oacc[cb][run * 8 + i] * inv;
+                        v1[i] = oacc[cb][run * 8 + 4 + i] * inv;
+                    }
+                    float* dst = orow + cb * 32 + run * 16 + half * 8;
+                    *(f32x4*)dst = v0;
+                    *(f32x4*)(dst + 4) = v1;
+                }
+            if (half == 0) p.lpart[(int64_t)s * rows + grow] = lse_val;
+        }
+    }
+}
+
+// Merge of split partials: LSE = M + ln sum_s exp(LSE_s - M) with
+// M = max_s LSE_s, O = sum_s exp(LSE_s - LSE) O_s. A row whose splits are all
+// empty gets O = 0 and LSE = -inf. One row per D/4 lanes, 4 columns a lane.
+template <int D>
+__global__ __launch_bounds__(256) void combine_kernel(const CombineParams p) {
+    constexpr int LPR = D / 4;
+    constexpr int RPB = 256 / LPR;
+    const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
+    const int c4 = threadIdx.x % LPR;
+    if (row >= p.rows) return;
+    float M = -__builtin_inff();
+    for (int s = 0; s < p.ns; ++s) M = fmaxf(M, p.lpart[(int64_t)s * p.rows + row]);
+    f32x4 acc = f32x4{};
+    float lse = -__builtin_inff();
+    if (M != -__builtin_inff()) {
+        float tot = 0.f;
+        for (int s = 0; s < p.ns; ++s) tot += __expf(p.lpart[(int64_t)s * p.rows + row] - M);
+        lse = M + __logf(tot);
+        for (int s = 0; s < p.ns; ++s) {
+            const float ls = p.lpart[(int64_t)s * p.rows + row];
+            const float w = __expf(ls - lse);  // exp(-inf) = 0 for empty splits
+            const f32x4 v = *(const f32x4*)(p.opart + ((int64_t)s * p.rows + row) * D + c4 * 4);
+            acc += w * v;
+        }
+    }
+    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+    bf16x4 ov;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ov[i] = (__bf16)acc[i];
+    *(bf16x4*)(p.o + row * D + c4 * 4) = ov;
+    if (c4 == 0 && p.lse) {
+        const int64_t hq = row % p.Hq;
+        const int64_t bt = row / p.Hq;
+        const int64_t i = bt % p.Sq, bb = bt / p.Sq;
+        p.lse[(bb * p.Hq + hq) * p.Sq + i] = lse;
+    }
+}
+
+// ---------------------------------------------------------------- launchers
+template <int D, bool CAUSAL, bool SPLIT>
+static hipError_t launch_attn(const FwdParams& p, hipStream_t stream) {
+    hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, SPLIT>), dim3(p.grid), dim3(kThreads), 0, stream, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_attention(const FwdParams& p, int d, bool causal, bool split, hipStream_t stream) {
+    if (d == 128) {
+        if (causal) return split ? launch_attn<128, true, true>(p, stream) : launch_attn<128, true, false>(p, stream);
+        return split ? launch_attn<128, false, true>(p, stream) : launch_attn<128, false, false>(p, stream);
+    }
+    if (causal) return split ? launch_attn<64, true, true>(p, stream) : launch_attn<64, true, false>(p, stream);
+    return split ? launch_attn<64, false, true>(p, stream) : launch_attn<64, false, false>(p, stream);
+}
+
+hipError_t launch_combine(const CombineParams& p, int d, long long grid, hipStream_t stream) {
+    if (d == 128)
+        hipLaunchKernelGGL((combine_kernel<128>), dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
+    else
+        hipLaunchKernelGGL((combine_kernel<64>), dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
+    return hipGetLastError();
+}
+
+}  // namespace gqa

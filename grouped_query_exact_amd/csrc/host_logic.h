@@ -1,0 +1,62 @@
+// Host-side logic of the GQA forward library: argument checks, the
+// pack/split heuristic, launch planning and the magic-number divisor.
+// Plain C++ with no HIP calls, so it can be built and tested on a CPU.
+#pragma once
+
+#include <cstdint>
+
+namespace gqa {
+
+// Tile shape of the attention kernel: 4 wavefronts of 64 lanes, each owning
+// 32 query rows, stream 64 keys per step.
+constexpr int kBlockM = 128;
+constexpr int kBlockN = 64;
+constexpr int kThreads = 256;
+
+// Division by a runtime constant through a precomputed multiplier (the
+// batch-sensitivity article, "PackGQA" mechanism 3, precomputes the
+// query-head -> KV-head map with a fast divide-and-modulo). Round-up method:
+// with l = ceil(log2 d) and m = floor(2^32 * (2^l - d) / d) + 1,
+// n / d == (umulhi(n, m) + n) >> l for every 0 <= n < 2^31.
+struct FastDiv {
+    uint32_t div;
+    uint32_t mul;
+    uint32_t shift;
+};
+FastDiv make_fastdiv(uint32_t d);
+inline uint32_t fastdiv_host(uint32_t n, const FastDiv& f) {
+    uint32_t hi = (uint32_t)(((uint64_t)n * f.mul) >> 32);
+    return (hi + n) >> f.shift;
+}
+
+struct Shape {
+    int B, Sq, Sk, Hq, Hk, d, causal;
+};
+
+// Returns 0 or a gqa_status_t error for the sizes alone (no pointers).
+int check_sizes(const Shape& s, float scale, int pack_gqa, int num_splits);
+
+// The heuristic: resolves pack_gqa (0/1) and num_splits (>= 1).
+void choose(const Shape& s, int num_cus, int* pack_gqa, int* num_splits);
+
+struct Plan {
+    int pack;           // resolved pack flag
+    int G;              // query heads per KV head
+    int Gp;             // rows per token in a tile: G if packed, else 1
+    int units_per_b;    // head units per batch element: Hk if packed, else Hq
+    long long R;        // query rows per head unit: Sq * Gp
+    int row_tiles;      // ceil(R / kBlockM)
+    int key_tiles;      // key tiles of the longest row tile
+    int ns;             // resolved, clamped split count
+    long long grid;     // attention workgroups
+    long long combine_grid;
+    long long workspace_bytes;
+};
+
+// Resolves the plan; returns 0 or a status (sizes too large for the grid).
+int make_plan(const Shape& s, int pack_gqa, int num_splits, int num_cus, Plan* p);
+
+// Rows of the combine kernel handled by one 256-thread workgroup.
+inline int combine_rows_per_block(int d) { return kThreads / (d / 4); }
+
+}  // namespace gqa

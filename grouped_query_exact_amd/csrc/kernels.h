@@ -1,0 +1,44 @@
+// Kernel parameter blocks and launchers of the GQA forward library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "host_logic.h"
+
+namespace gqa {
+
+struct FwdParams {
+    const uint16_t* q;  // [B, Sq, Hq, D] bf16
+    const uint16_t* k;  // [B, Sk, Hk, D] bf16
+    const uint16_t* v;  // [B, Sk, Hk, D] bf16
+    uint16_t* o;        // [B, Sq, Hq, D] bf16 (unsplit launches)
+    float* lse;         // [B, Hq, Sq] fp32 or null (unsplit launches)
+    float* opart;       // [ns, B*Sq*Hq, D] fp32 (split launches)
+    float* lpart;       // [ns, B*Sq*Hq] fp32 (split launches)
+    int B, Sq, Sk, Hq, Hk;
+    int G;              // Hq / Hk
+    int Gp;             // rows per token in a tile: G when packed, 1 otherwise
+    uint32_t gmul, gshift;  // magic divisor of Gp
+    int R;              // query rows per head unit: Sq * Gp
+    int row_tiles;      // ceil(R / kBlockM)
+    int units_per_b;    // Hk when packed, Hq otherwise
+    int ns;             // key splits
+    int grid;           // workgroups
+    float c;            // |scale| * log2(e)
+    uint32_t qsign;     // 0x80008000 to negate Q (negative scale), else 0
+};
+
+struct CombineParams {
+    const float* opart;
+    const float* lpart;
+    uint16_t* o;
+    float* lse;
+    int64_t rows;       // B * Sq * Hq
+    int ns, Sq, Hq;
+};
+
+hipError_t launch_attention(const FwdParams& p, int d, bool causal, bool split, hipStream_t stream);
+hipError_t launch_combine(const CombineParams& p, int d, long long grid, hipStream_t stream);
+
+}  // namespace gqa

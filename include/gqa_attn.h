@@ -1,0 +1,124 @@
+/*
+ * gqa_attn.h - exact grouped-query attention forward pass on AMD MI355X (gfx950).
+ *
+ * Operation (PyTorch profiling guide part 3, "the computational challenge of
+ * attention" formula; Llama-2 GQA article, section 1.2):
+ *
+ *     O[b,i,h,:] = sum_j softmax_j(scale * Q[b,i,h,:] . K[b,j,g,:]) * V[b,j,g,:]
+ *     LSE[b,h,i] = ln sum_j exp(scale * Q[b,i,h,:] . K[b,j,g,:])
+ *
+ * over the keys j visible to query i, where the query head h reads key/value
+ * head g = h / (Hq/Hk): with Hq=6, Hk=2, query heads 0-2 read KV head 0 and
+ * heads 3-5 read KV head 1, and Hq must be a multiple of Hk (batch-sensitivity
+ * article, "core design of grouped-query attention"; rise-and-fall tuning
+ * article, "root cause"). With causal != 0, key j is visible to query i iff
+ * j <= i + Sk - Sq (bottom-right alignment; the usual j <= i when Sq == Sk).
+ * A query that sees no key gets O = 0 and LSE = -inf. The result is exact up
+ * to floating-point rounding: tiles, the online softmax, PackGQA and split-KV
+ * only reorder the arithmetic.
+ *
+ * pack_gqa and num_splits are the two knobs of the pages' flash_attn_func
+ * (Stable-Diffusion GQA guide, "dynamic batch scheduling"; batch-sensitivity
+ * article, strategy 2 "PackGQA and num_splits"; rise-and-fall tuning article,
+ * "fix" table): pack_gqa puts the query heads of one KV group into one tile
+ * so each K/V tile is read once per group, and num_splits cuts the key axis
+ * into parts whose partial results are merged with log-sum-exp weights
+ * ("split + combine").
+ *
+ * Layouts (all row-major, last dimension contiguous, no padding):
+ *   q, out : [B, Sq, Hq, d] bf16 (stored as 16-bit words)
+ *   k, v   : [B, Sk, Hk, d] bf16
+ *   lse    : [B, Hq, Sq] fp32, natural logarithm, or NULL to skip it
+ * All tensor pointers are device pointers on the current HIP device and must
+ * be 16-byte aligned. d must be 64 or 128.
+ *
+ * Ownership: the caller owns every tensor. The library allocates only the
+ * split-KV workspace (fp32 partial outputs and log-sum-exps), stream-ordered
+ * with hipMallocAsync/hipFreeAsync on the caller's stream, so calls on
+ * different streams never share it. The library keeps no other state than a
+ * per-device cache of the compute-unit count.
+ *
+ * Calls are asynchronous with respect to the host and never synchronize the
+ * stream. They are thread-safe. No C++ exception crosses this boundary.
+ */
+#ifndef GQA_ATTN_H
+#define GQA_ATTN_H
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. Every error is reported before anything is launched, and
+ * leaves out and lse untouched, except GQA_ERR_HIP, which reports a failed
+ * HIP call (allocation of the workspace aside) or launch. */
+typedef enum {
+    GQA_OK = 0,
+    GQA_ERR_INVALID_ARG = -1, /* null tensor pointer, negative size, Hq % Hk != 0,
+                                 Sk == 0 while B*Sq > 0, pack_gqa not in {-1,0,1},
+                                 num_splits < 0, non-finite scale, size overflow */
+    GQA_ERR_UNSUPPORTED = -2, /* d not in {64,128}, pointer not 16-byte aligned */
+    GQA_ERR_NOMEM = -3,       /* the split-KV workspace could not be allocated */
+    GQA_ERR_HIP = -4          /* a HIP call or kernel launch failed */
+} gqa_status_t;
+
+/* Forward pass.
+ *   q, k, v, out, lse : see Layouts above. lse may be NULL.
+ *   B, Sq, Sk         : batch size, query length, key length (B*Sq == 0: no-op).
+ *   Hq, Hk, d         : query heads, key/value heads, head dimension.
+ *   causal            : 0 or non-zero (bottom-right aligned mask, see above).
+ *   scale             : softmax scale applied to Q.K (callers usually pass
+ *                       1/sqrt(d)); any finite value, including 0 and negatives.
+ *   pack_gqa          : 1 pack the G = Hq/Hk heads of a group into one tile,
+ *                       0 one head per tile, -1 let gqa_attn_choose decide.
+ *   num_splits        : >= 1 split the keys of every tile into that many parts
+ *                       (clamped to the number of key tiles), 0 automatic.
+ *   stream            : HIP stream the kernels are enqueued on (0 = null stream).
+ * Returns a gqa_status_t. */
+int gqa_attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+                 int B, int Sq, int Sk, int Hq, int Hk, int d,
+                 int causal, float scale, int pack_gqa, int num_splits,
+                 hipStream_t stream);
+
+/* The host heuristic behind pack_gqa = -1 / num_splits = 0. It follows the
+ * pages' rationale (rise-and-fall tuning article, "root cause" and "fix"
+ * table; batch-sensitivity article, "performance analysis"): pack when the
+ * query rows of one head fill a tile poorly (short or ragged Sq, decode),
+ * split the keys when there are too few tiles to fill the compute units.
+ * The thresholds are chosen for MI355X, not copied from the pages' H100
+ * tables. num_cus <= 0 means "ask the current device" (a host-only call
+ * otherwise: no HIP call is made). Writes *pack_gqa in {0,1} and
+ * *num_splits >= 1. Returns GQA_OK, or GQA_ERR_INVALID_ARG for invalid sizes
+ * or null outputs. */
+int gqa_attn_choose(int B, int Sq, int Sk, int Hq, int Hk, int d, int causal, int num_cus,
+                    int* pack_gqa, int* num_splits);
+
+/* Launch plan of one call, for tests and benchmarks. Host only: no HIP call
+ * is made when num_cus > 0. */
+typedef struct {
+    int pack_gqa;          /* resolved pack flag */
+    int num_splits;        /* resolved and clamped split count */
+    int block_m;           /* query rows per tile */
+    int block_n;           /* keys per tile */
+    int row_tiles;         /* row tiles per (batch, head unit) */
+    int key_tiles;         /* key tiles of the longest row tile */
+    long long grid;        /* workgroups of the attention kernel */
+    long long combine_grid;/* workgroups of the combine kernel (0 if none) */
+    long long workspace_bytes; /* split-KV workspace (0 if num_splits == 1) */
+} gqa_attn_plan_t;
+
+/* Resolve pack_gqa / num_splits exactly as gqa_attn_fwd would and describe
+ * the launches. Returns GQA_OK or the status gqa_attn_fwd would return for
+ * these sizes (pointer checks aside). */
+int gqa_attn_plan(int B, int Sq, int Sk, int Hq, int Hk, int d, int causal,
+                  int pack_gqa, int num_splits, int num_cus, gqa_attn_plan_t* plan);
+
+/* Static, human-readable text of a status code. */
+const char* gqa_attn_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GQA_ATTN_H */

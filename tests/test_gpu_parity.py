@@ -1,0 +1,84 @@
+"""Parity of the HIP path against the fp64 oracle on the five workloads (GPU).
+
+Small workloads are compared element by element in full. At the full sizes
+the oracle is run on sampled (batch, head, row) slices of the same seeded
+inputs, in the launch configuration the benchmark times.
+"""
+
+import random
+
+import numpy as np
+import pytest
+import torch
+
+import gqa_inputs as gi
+from _parity import assert_variants_agree, compare_to_oracle, gpu_run
+
+pytestmark = pytest.mark.gpu
+
+
+def _sample_rows(Sq, n, seed):
+    rs = random.Random(seed)
+    fixed = {0, 1, Sq - 1, Sq // 2}
+    for edge in (63, 64, 65, 127, 128, 129):
+        if edge < Sq:
+            fixed.add(edge)
+    extra = rs.sample(range(Sq), min(n, Sq))
+    return sorted(fixed | set(extra))
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("variant", gi.TINY.variants)
+def test_tiny(causal, variant):
+    w = gi.TINY.with_(causal=causal)
+    q, k, v = gi.make_qkv(w)
+    O, L = gpu_run(q, k, v, causal, w.scale, *variant)
+    compare_to_oracle(O, L, q, k, v, causal, w.scale, tag=f"{w.name} {variant}")
+
+
+@pytest.mark.parametrize("variant", gi.RAGGED.variants)
+def test_ragged_b212_s77(variant):
+    w = gi.RAGGED
+    q, k, v = gi.make_qkv(w)
+    O, L = gpu_run(q, k, v, w.causal, w.scale, *variant)
+    compare_to_oracle(O, L, q, k, v, w.causal, w.scale, tag=f"{w.name} {variant}")
+
+
+@pytest.mark.parametrize("variant", [(1, 1), (1, 4), (1, 8), (0, 4), (0, 1)])
+def test_decode_b64_sk8192(variant):
+    w = gi.DECODE
+    q, k, v = gi.make_qkv(w)
+    O, L = gpu_run(q, k, v, w.causal, w.scale, *variant)
+    compare_to_oracle(O, L, q, k, v, w.causal, w.scale, tag=f"{w.name} {variant}")
+
+
+def test_llama_prefill_b4():
+    w = gi.LLAMA_PREFILL
+    q, k, v = gi.make_qkv(w)
+    res = {}
+    for variant in w.variants:
+        O, L = gpu_run(q, k, v, w.causal, w.scale, *variant)
+        # batch 3 in full (all heads, all rows), sampled rows of the other batches
+        compare_to_oracle(O, L, q, k, v, w.causal, w.scale, batches=[3], tag=f"{w.name} {variant} b3")
+        compare_to_oracle(O, L, q, k, v, w.causal, w.scale, batches=[0, 1, 2], heads=[0, 5, 31],
+                          rows=_sample_rows(w.Sq, 40, 7), tag=f"{w.name} {variant} sampled")
+        res[variant] = (O, L)
+    (Oa, La), (Ob, Lb) = res[(1, 1)], res[(0, 1)]
+    assert torch.equal(Oa, Ob), "pack on/off must be bitwise identical"
+    assert torch.equal(La, Lb)
+
+
+@pytest.mark.parametrize("B", gi.SWEEP_BATCHES)
+def test_sweep_full_size(B):
+    w = gi.sweep(B)
+    q, k, v = gi.make_qkv_device(w, "cuda:0")
+    res = {}
+    bsel = sorted({0, B - 1, random.Random(B).randrange(B)})
+    for variant in w.variants:
+        O, L = gpu_run(q, k, v, w.causal, w.scale, *variant)
+        qs, ks, vs = (t[bsel].cpu() for t in (q, k, v))
+        compare_to_oracle(O[bsel], L[bsel], qs, ks, vs, w.causal, w.scale, heads=[0, 3, 4, 17, 31],
+                          rows=_sample_rows(w.Sq, 48, B), tag=f"{w.name} {variant}")
+        res[variant] = (O, L)
+    (Oa, La), (Ob, Lb) = res[(1, 1)], res[(0, 4)]
+    assert_variants_agree(Oa, La, Ob, Lb, float(v.abs().max()), tag=w.name)
