@@ -146,7 +146,15 @@ int gqa_attn_fwd(const void* q, const void* k, const void* v, void* out, float* 
         p.units_per_b = plan.units_per_b;
         p.ns = plan.ns;
         p.grid = (int)plan.grid;
-        p.c = (float)(std::fabs((double)scale) * 1.4426950408889634);
+        // softmax(scale * s) = softmax(|scale| * (sign(scale) * s)): a negative
+        // scale negates Q (exact in bf16). scale == 0 gives every visible key
+        // the score 0, which the kernel reproduces exactly by reading Q as 0.
+        // A scale so small that |scale|*log2(e) is not a normal fp32 number
+        // also gives every visible key exactly the same weight in fp32.
+        const double cd = std::fabs((double)scale) * 1.4426950408889634;
+        const bool zero_scale = cd < 1.1754943508222875e-38;
+        p.c = zero_scale ? 1.0f : (float)cd;
+        p.qand = zero_scale ? 0u : 0xFFFFFFFFu;
         p.qsign = scale < 0.f ? 0x80008000u : 0u;
 
         if (log_enabled())

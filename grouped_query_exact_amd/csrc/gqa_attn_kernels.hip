@@ -46,6 +46,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "kernels.h"
 
 namespace gqa {
@@ -74,8 +76,19 @@ __device__ __forceinline__ int pi32(int m) {
     return ((b >> 1) << 4) | (h << 3) | ((b & 1) << 2) | r;
 }
 
-// 16-byte chunk swizzle of LDS row `row`.
-__device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 3) & 1); }
+// 16-byte chunk swizzle of LDS row `row` (XORed into the chunk index).
+// gfx950's LDS serves a ds_read_b128 16 lanes at a time and a
+// ds_read_b64_tr_b16 32 lanes at a time, over 64 four-byte banks (256 B).
+// d=128 (256-byte rows, 16 chunks): the 16 rows read together by the K
+// operand get 16 distinct chunks, and the 4 rows x 4 chunks read together
+// by the V^T operand land in 4 distinct aligned groups of 4 chunks.
+// d=64 (128-byte rows, two rows per bank line): the same two properties
+// hold within each half of the bank line.
+template <int D>
+__device__ __forceinline__ int swz(int row) {
+    if (D == 128) return ((row & 3) << 2) | ((row >> 2) & 3);
+    return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+}
 
 // Remap a hardware workgroup id (dealt round-robin over the 8 XCDs) to a
 // logical work item so that each XCD receives a contiguous logical range.
@@ -87,35 +100,29 @@ __device__ __forceinline__ int xcd_remap(int bid, int total) {
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-template <int D>
-__device__ __forceinline__ void issue_tile(const uint16_t* __restrict__ kbase,
-                                           const uint16_t* __restrict__ vbase, int64_t kv_stride,
-                                           int kv0, int Sk, LDS uint16_t* kt, LDS uint16_t* vt,
-                                           int wave, int lane) {
-    constexpr int NCH = D / 8;                       // 16-byte chunks per row
-    constexpr int NLOAD = kBlockN * NCH / kThreads;  // loads per thread per tensor
-#pragma unroll
-    for (int u = 0; u < NLOAD; ++u) {
-        const int base = (u * 4 + wave) * 64;        // first chunk written by this wave
-        const int ci = base + lane;
-        const int row = ci / NCH;
-        const int phys = ci % NCH;
-        const int logical = phys ^ swz(row);
-        const int key = min(kv0 + row, Sk - 1);
-        const int64_t off = (int64_t)key * kv_stride + logical * 8;
-        __builtin_amdgcn_global_load_lds((const void*)(kbase + off), (LDS void*)(kt + base * 8), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((const void*)(vbase + off), (LDS void*)(vt + base * 8), 16, 0, 0);
-    }
+// Exchange with the lane 32 positions away: returns {v_self_or_partner...}
+// such that max/sum of the two components is the reduction over lanes l and l^32.
+__device__ __forceinline__ float xhalf_max(float v) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xhalf_sum(float v) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 template <int D, bool CAUSAL, bool SPLIT>
-__global__ __launch_bounds__(256) void attn_fwd_kernel(const FwdParams p) {
-    constexpr int TILE = kBlockN * D;  // elements of one K or V tile
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_kernel(const FwdParams p) {
+    constexpr int TILE = kBlockN * D;                 // elements of one K or V tile
+    constexpr int TILE_B = TILE * 2;                  // bytes
+    constexpr int NCH = D / 8;                        // 16-byte chunks per row
+    constexpr int NLOAD = kBlockN * NCH / kThreads;   // 16-byte loads per thread per tensor
     __shared__ __attribute__((aligned(16))) uint16_t smem[4 * TILE];
-    LDS uint16_t* lds = (LDS uint16_t*)smem;
+    LDS char* lds = (LDS char*)smem;                  // [buf][K|V] tiles
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
     const int col = lane & 31, half = lane >> 5;
 
     // ---- work item
@@ -145,7 +152,7 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const FwdParams p) {
 #pragma unroll
         for (int dc = 0; dc < D / 16; ++dc) {
             u32x4 w = *(const u32x4*)(qrow + dc * 16 + half * 8);
-            w ^= p.qsign;
+            w = (w & p.qand) ^ p.qsign;
             qreg[dc] = __builtin_bit_cast(bf16x8, w);
         }
     }
@@ -168,78 +175,124 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const FwdParams p) {
     const int iw_min = (int)fdiv((uint32_t)min(rw0, p.R - 1), p.gmul, p.gshift);
     const int iw_max = (int)fdiv((uint32_t)(min(rw0 + 32, p.R) - 1), p.gmul, p.gshift);
 
-    const int64_t kv_stride = (int64_t)p.Hk * D;
-    const uint16_t* kbase = p.k + ((int64_t)b * p.Sk * p.Hk + g) * D;
-    const uint16_t* vbase = p.v + ((int64_t)b * p.Sk * p.Hk + g) * D;
+    // ---- K/V tile loads: per-lane byte offsets inside a tile, scalar tile base
+    const int64_t kv_stride_b = (int64_t)p.Hk * D * 2;
+    const char* kbase = (const char*)(p.k + ((int64_t)b * p.Sk * p.Hk + g) * D);
+    const char* vbase = (const char*)(p.v + ((int64_t)b * p.Sk * p.Hk + g) * D);
+    uint32_t goff[NLOAD];
+#pragma unroll
+    for (int u = 0; u < NLOAD; ++u) {
+        const int ci = (u * 4 + wave) * 64 + lane;
+        const int row = ci / NCH;
+        const int logical_ch = (ci % NCH) ^ swz<D>(row);
+        goff[u] = (uint32_t)(row * kv_stride_b + logical_ch * 16);
+    }
+    auto issue = [&](int kv0, int buf) {
+        LDS char* kt = lds + buf * 2 * TILE_B;
+        LDS char* vt = kt + TILE_B;
+        const char* kg = kbase + kv0 * kv_stride_b;
+        const char* vg = vbase + kv0 * kv_stride_b;
+        if (kv0 + kBlockN <= p.Sk) {
+#pragma unroll
+            for (int u = 0; u < NLOAD; ++u) {
+                const int dst = (u * 4 + wave) * 1024;
+                __builtin_amdgcn_global_load_lds((const void*)(kg + goff[u]), (LDS void*)(kt + dst), 16, 0, 0);
+                __builtin_amdgcn_global_load_lds((const void*)(vg + goff[u]), (LDS void*)(vt + dst), 16, 0, 0);
+            }
+        } else {  // ragged last tile: rows past the end re-read the last key (masked later)
+#pragma unroll
+            for (int u = 0; u < NLOAD; ++u) {
+                const int dst = (u * 4 + wave) * 1024;
+                const int ci = (u * 4 + wave) * 64 + lane;
+                const int row = ci / NCH;
+                const int logical_ch = (ci % NCH) ^ swz<D>(row);
+                const int key = min(kv0 + row, p.Sk - 1) - kv0;
+                const uint32_t o = (uint32_t)(key * kv_stride_b + logical_ch * 16);
+                __builtin_amdgcn_global_load_lds((const void*)(kg + o), (LDS void*)(kt + dst), 16, 0, 0);
+                __builtin_amdgcn_global_load_lds((const void*)(vg + o), (LDS void*)(vt + dst), 16, 0, 0);
+            }
+        }
+    };
+
+    // ---- per-lane LDS operand offsets (bytes, relative to the tile start)
+    const int krow0 = pi32(col);
+    uint32_t kofs[D / 16];
+#pragma unroll
+    for (int dc = 0; dc < D / 16; ++dc) kofs[dc] = krow0 * (D * 2) + (((2 * dc + half) ^ swz<D>(krow0)) * 16);
+    const int u16 = lane & 15, qq = (lane >> 4) & 1;
+    const int rho = ((u16 & 1) << 1) | ((u16 >> 1) & 1);  // 0,2,1,3
+    uint32_t vofs[D / 32][2];
+#pragma unroll
+    for (int cb = 0; cb < D / 32; ++cb)
+#pragma unroll
+        for (int rr = 0; rr < 2; ++rr) {
+            const int vrow = half * 8 + rr * 4 + (u16 >> 2);   // + 16*kk, which keeps the swizzle
+            const int vcol = cb * 32 + qq * 16 + rho * 4;
+            vofs[cb][rr] = vrow * (D * 2) + (((vcol >> 3) ^ swz<D>(vrow)) * 16) + (vcol & 7) * 2;
+        }
 
     f32x16 oacc[D / 32];
 #pragma unroll
     for (int cb = 0; cb < D / 32; ++cb) oacc[cb] = f32x16{};
     float m_run = -__builtin_inff();  // running max, scaled log2 units
-    float l_run = 0.f;                // this lane's partial row sum
+    float l_part[4] = {0.f, 0.f, 0.f, 0.f};  // this lane's partial row sums
     const float c = p.c;
+    const int jlim = CAUSAL ? min(p.Sk - 1, ti + koff) : p.Sk - 1;  // last key visible to this row
 
-    if (t_begin < t_end)
-        issue_tile<D>(kbase, vbase, kv_stride, t_begin * kBlockN, p.Sk, lds, lds + TILE, wave, lane);
+    // One key tile: scores, online softmax, output update. `buf` selects the
+    // LDS stage; `need_mask` is uniform across the wave.
+    auto compute = [&](int buf, int kv0, bool need_mask) {
+        const LDS char* kt = lds + buf * 2 * TILE_B;
+        const LDS char* vt = kt + TILE_B;
 
-    for (int t = t_begin; t < t_end; ++t) {
-        const int buf = (t - t_begin) & 1;
-        LDS uint16_t* kt = lds + buf * 2 * TILE;
-        LDS uint16_t* vt = kt + TILE;
-        wait_vmem();
-        __syncthreads();
-        if (t + 1 < t_end) {
-            LDS uint16_t* kn = lds + (buf ^ 1) * 2 * TILE;
-            issue_tile<D>(kbase, vbase, kv_stride, (t + 1) * kBlockN, p.Sk, kn, kn + TILE, wave, lane);
-        }
-        const int kv0 = t * kBlockN;
-        if (!wave_active) continue;
-        if (CAUSAL && kv0 > iw_max + koff) continue;  // no row of this wave sees these keys
-
-        // ---- S^T = K Q^T: two blocks of 32 keys
+        // S^T = K Q^T: two blocks of 32 keys
         f32x16 sacc[2];
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
             sacc[mb] = f32x16{};
-            const int krow = mb * 32 + pi32(col);
-            const LDS uint16_t* kr = kt + krow * D;
-            const int sw = swz(krow);
 #pragma unroll
             for (int dc = 0; dc < D / 16; ++dc) {
-                const int ch = (2 * dc + half) ^ sw;
-                const bf16x8 a = *(const LDS bf16x8*)(kr + ch * 8);
+                const bf16x8 a = *(const LDS bf16x8*)(kt + kofs[dc] + mb * 32 * D * 2);
                 sacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[dc], sacc[mb], 0, 0, 0);
             }
         }
-
-        // ---- mask (boundary tiles only)
-        const bool need_mask = (kv0 + kBlockN > p.Sk) || (CAUSAL && kv0 + kBlockN - 1 > iw_min + koff);
-        const int jlim = CAUSAL ? min(p.Sk - 1, ti + koff) : p.Sk - 1;  // last visible key of this row
-        float mx = -__builtin_inff();
+        // keys of this lane's slots: kv0 + 32*mb + 16*(i/8) + 8*half + (i%8)
         if (need_mask) {
+            const int lim = jlim - kv0 - half * 8;
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int key = kv0 + mb * 32 + ((i >> 3) << 4) + half * 8 + (i & 7);
-                    if (key > jlim) sacc[mb][i] = -__builtin_inff();
-                }
+                for (int i = 0; i < 16; ++i)
+                    if (mb * 32 + ((i >> 3) << 4) + (i & 7) > lim) sacc[mb][i] = -__builtin_inff();
         }
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[mb][i]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-
-        // ---- lazy running-max update
+        float mx;
+        {
+            float t0 = fmaxf(fmaxf(sacc[0][0], sacc[0][1]), sacc[0][2]);
+            float t1 = fmaxf(fmaxf(sacc[0][3], sacc[0][4]), sacc[0][5]);
+            float t2 = fmaxf(fmaxf(sacc[0][6], sacc[0][7]), sacc[0][8]);
+            float t3 = fmaxf(fmaxf(sacc[0][9], sacc[0][10]), sacc[0][11]);
+            t0 = fmaxf(fmaxf(t0, sacc[0][12]), sacc[0][13]);
+            t1 = fmaxf(fmaxf(t1, sacc[0][14]), sacc[0][15]);
+            t2 = fmaxf(fmaxf(t2, sacc[1][0]), sacc[1][1]);
+            t3 = fmaxf(fmaxf(t3, sacc[1][2]), sacc[1][3]);
+            t0 = fmaxf(fmaxf(t0, sacc[1][4]), sacc[1][5]);
+            t1 = fmaxf(fmaxf(t1, sacc[1][6]), sacc[1][7]);
+            t2 = fmaxf(fmaxf(t2, sacc[1][8]), sacc[1][9]);
+            t3 = fmaxf(fmaxf(t3, sacc[1][10]), sacc[1][11]);
+            t0 = fmaxf(fmaxf(t0, sacc[1][12]), sacc[1][13]);
+            t1 = fmaxf(fmaxf(t1, sacc[1][14]), sacc[1][15]);
+            mx = xhalf_max(fmaxf(fmaxf(t0, t1), fmaxf(t2, t3)));
+        }
+        // lazy running-max update (per row; both lanes of a row agree)
         const float mxs = (mx == -__builtin_inff()) ? -__builtin_inff() : mx * c;
         float alpha = 1.f;
         if (mxs > m_run + kRescaleThreshold) {
             alpha = __builtin_amdgcn_exp2f(m_run - mxs);  // exp2(-inf) = 0 on the first update
             m_run = mxs;
         }
-        if (__builtin_amdgcn_read_exec() & __ballot(alpha != 1.f)) {
-            l_run *= alpha;
+        if (__ballot(alpha != 1.f)) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) l_part[i] *= alpha;
 #pragma unroll
             for (int cb = 0; cb < D / 32; ++cb)
 #pragma unroll
@@ -247,48 +300,48 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const FwdParams p) {
         }
         const float moff = (m_run == -__builtin_inff()) ? 0.f : m_run;
 
-        // ---- P = exp2(s*c - m), row sum, bf16 pack (B operand of O^T += V^T P^T)
+        // P = exp2(s*c - m) -> bf16 (B operand of O^T += V^T P^T). Masked scores
+        // are -inf and c > 0, so their P is exactly 0.
         bf16x8 pk[4];
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mb][i], c, -moff));
-                if (need_mask) {
-                    const int key = kv0 + mb * 32 + ((i >> 3) << 4) + half * 8 + (i & 7);
-                    if (key > jlim) e = 0.f;
-                }
-                l_run += e;
-                pk[mb * 2 + (i >> 3)][i & 7] = (__bf16)e;
+                const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mb][i], c, -moff));
+                l_part[i & 3] += x;
+                pk[mb * 2 + (i >> 3)][i & 7] = (__bf16)x;
             }
 
-        // ---- O^T += V^T P^T
-        {
-            const int u = lane & 15, qq = (lane >> 4) & 1;
-            const int rho = ((u & 1) << 1) | ((u >> 1) & 1);  // 0,2,1,3
+        // O^T += V^T P^T
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
+        for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
-                for (int cb = 0; cb < D / 32; ++cb) {
-                    s16x4 part[2];
-#pragma unroll
-                    for (int rr = 0; rr < 2; ++rr) {
-                        const int vrow = kk * 16 + half * 8 + rr * 4 + (u >> 2);
-                        const int vcol = cb * 32 + qq * 16 + rho * 4;
-                        const int ch = (vcol >> 3) ^ swz(vrow);
-                        const LDS s16x4* a = (const LDS s16x4*)(vt + vrow * D + ch * 8 + (vcol & 7));
-                        part[rr] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS s16x4*)a);
-                    }
-                    const s16x8 av = __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7);
-                    oacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), pk[kk],
-                                                                         oacc[cb], 0, 0, 0);
-                }
+            for (int cb = 0; cb < D / 32; ++cb) {
+                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS s16x4*)(vt + vofs[cb][0] + kk * 16 * D * 2));
+                const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS s16x4*)(vt + vofs[cb][1] + kk * 16 * D * 2));
+                const s16x8 av = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                oacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), pk[kk],
+                                                                     oacc[cb], 0, 0, 0);
             }
+        }
+    };
+
+    if (t_begin < t_end) issue(t_begin * kBlockN, 0);
+    for (int t = t_begin; t < t_end; ++t) {
+        const int buf = (t - t_begin) & 1;
+        wait_vmem();
+        __syncthreads();
+        if (t + 1 < t_end) issue((t + 1) * kBlockN, buf ^ 1);
+        const int kv0 = t * kBlockN;
+        // waves whose rows see none of these keys skip the arithmetic
+        if (wave_active && !(CAUSAL && kv0 > iw_max + koff)) {
+            const bool need_mask = (kv0 + kBlockN > p.Sk) || (CAUSAL && kv0 + kBlockN - 1 > iw_min + koff);
+            compute(buf, kv0, need_mask);
         }
     }
 
     // ---- epilogue
-    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    const float l_tot = xhalf_sum((l_part[0] + l_part[1]) + (l_part[2] + l_part[3]));
     const bool live = l_tot > 0.f;
     const float inv = live ? 1.f / l_tot : 0.f;
     const float lse_val = live ? (m_run + __log2f(l_tot)) * kLn2 : -__builtin_inff();

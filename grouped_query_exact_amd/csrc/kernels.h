@@ -25,7 +25,8 @@ struct FwdParams {
     int units_per_b;    // Hk when packed, Hq otherwise
     int ns;             // key splits
     int grid;           // workgroups
-    float c;            // |scale| * log2(e)
+    float c;            // |scale| * log2(e), or 1 when scale == 0
+    uint32_t qand;      // 0 when scale == 0 (Q read as zeros: every visible score is 0), else all ones
     uint32_t qsign;     // 0x80008000 to negate Q (negative scale), else 0
 };
 
