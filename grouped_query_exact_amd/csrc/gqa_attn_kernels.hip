@@ -98,6 +98,22 @@ __device__ __forceinline__ int xcd_remap(int bid, int total) {
     return x * per + min(x, rem) + slot;
 }
 
+// 16-byte global -> LDS copy of every lane: lane l writes LDS bytes
+// [lds + 16*l, lds + 16*l + 16) with the 16 bytes at base + voff. Written as
+// inline assembly so that the compiler's wait-count tracking does not order
+// the LDS reads of the tile being computed behind these in-flight copies (it
+// would otherwise drain every LDS read to zero). The kernel waits for the
+// copies itself (vmcnt) before the barrier that publishes a tile. The
+// instruction has no VGPR destination; M0 is set inside the same block and
+// nothing else in the kernel uses it.
+__device__ __forceinline__ void lds_dma16(const void* base, uint32_t voff, LDS void* lds) {
+    const uint32_t m0 = (uint32_t)(size_t)lds;
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :
+                 : "s"(m0), "v"(voff), "s"(base)
+                 : "memory", "m0");
+}
+
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Exchange with the lane 32 positions away: returns {v_self_or_partner...}
@@ -196,8 +212,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
             for (int u = 0; u < NLOAD; ++u) {
                 const int dst = (u * 4 + wave) * 1024;
-                __builtin_amdgcn_global_load_lds((const void*)(kg + goff[u]), (LDS void*)(kt + dst), 16, 0, 0);
-                __builtin_amdgcn_global_load_lds((const void*)(vg + goff[u]), (LDS void*)(vt + dst), 16, 0, 0);
+                lds_dma16(kg, goff[u], kt + dst);
+                lds_dma16(vg, goff[u], vt + dst);
             }
         } else {  // ragged last tile: rows past the end re-read the last key (masked later)
 #pragma unroll
@@ -208,8 +224,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 const int logical_ch = (ci % NCH) ^ swz<D>(row);
                 const int key = min(kv0 + row, p.Sk - 1) - kv0;
                 const uint32_t o = (uint32_t)(key * kv_stride_b + logical_ch * 16);
-                __builtin_amdgcn_global_load_lds((const void*)(kg + o), (LDS void*)(kt + dst), 16, 0, 0);
-                __builtin_amdgcn_global_load_lds((const void*)(vg + o), (LDS void*)(vt + dst), 16, 0, 0);
+                lds_dma16(kg, o, kt + dst);
+                lds_dma16(vg, o, vt + dst);
             }
         }
     };
