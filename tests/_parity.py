@@ -9,8 +9,8 @@ Variants (pack_gqa on/off, num_splits) against each other:
     P.V product, each relative to its own running maximum, so an unsplit and a split
     result can differ by up to 2 * 2^-9 * max|V| in fp32 plus one bf16 step of the
     output rounding. Every element must stay within max(1e-3, that bound); in addition
-    the mean difference must stay below 1e-4 and at most 0.1% of the elements may
-    differ by more than 1e-3 (a dropped or doubled key would break both).
+    the mean difference must stay below max(1e-4, 2^-9 * mean|O|), the size
+    of one probability rounding relative to the outputs' own magnitude.
   pack_gqa on/off does the same arithmetic per row and is required to be bitwise equal.
 """
 
@@ -45,8 +45,34 @@ def f64(t) -> np.ndarray:
     return t.detach().to("cpu").to(torch.float64).numpy()
 
 
-def compare_to_oracle(O_gpu, L_gpu, q, k, v, causal, scale, batches=None, heads=None, rows=None, tag=""):
-    """Compare GPU outputs (full tensors) with the oracle on the selected slice."""
+def rounding_bound(Or: np.ndarray, q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float) -> np.ndarray:
+    """Per-element error bound of the GPU arithmetic against the exact result.
+
+    Each probability P = 2^(s*c - m) carries a relative error of at most
+    2^-9 from its bf16 rounding plus |scale| * gamma_d * sum_i |q_i k_i| from
+    the fp32 accumulation of the score (gamma_d = d * 2^-24, the classical
+    dot-product bound), so the fp32 output is within eps * max|V| of the
+    exact one. Rounding the output to bf16 adds half a bf16 step at the
+    largest magnitude the fp32 value can have; 1e-4 covers exp2 and the
+    final normalisation. Used for stress inputs whose outputs reach
+    magnitudes where the flat 2e-2 tolerance is below the output rounding.
+    """
+    d = q.shape[-1]
+    qabs = np.abs(q).sum(axis=-1).max()
+    kmax = np.abs(k).max()
+    eps = 2.0 ** -9 + abs(scale) * d * 2.0 ** -24 * qabs * kmax
+    vmax = float(np.abs(v).max())
+    top = np.abs(Or) + eps * vmax + 1e-4
+    half_ulp = np.exp2(np.floor(np.log2(np.maximum(top, 2.0 ** -126))) - 8)
+    return eps * vmax + half_ulp + 1e-4
+
+
+def compare_to_oracle(O_gpu, L_gpu, q, k, v, causal, scale, batches=None, heads=None, rows=None, tag="",
+                      derived_bound=False):
+    """Compare GPU outputs (full tensors) with the oracle on the selected slice.
+
+    derived_bound=True replaces the flat max tolerance by rounding_bound (stress inputs only).
+    """
     Or, Lr = oracle.attention_fp64(f64(q), f64(k), f64(v), causal, scale, batches=batches, heads=heads, rows=rows)
     bs = list(range(q.shape[0])) if batches is None else list(batches)
     hs = list(range(q.shape[2])) if heads is None else list(heads)
@@ -55,7 +81,11 @@ def compare_to_oracle(O_gpu, L_gpu, q, k, v, causal, scale, batches=None, heads=
     dO = np.abs(Og - Or)
     assert np.isfinite(Og).all(), f"{tag}: non-finite output"
     mx, mean = float(dO.max()) if dO.size else 0.0, float(dO.mean()) if dO.size else 0.0
-    assert mx <= TOL_O_MAX, f"{tag}: max|dO| = {mx}"
+    if derived_bound:
+        excess = float((dO - rounding_bound(Or, f64(q), f64(k), f64(v), scale)).max()) if dO.size else 0.0
+        assert excess <= 0, f"{tag}: max|dO| = {mx} exceeds the rounding bound by {excess}"
+    else:
+        assert mx <= TOL_O_MAX, f"{tag}: max|dO| = {mx}"
     assert mean <= TOL_O_MEAN, f"{tag}: mean|dO| = {mean}"
     if L_gpu is not None:
         Lg = f64(L_gpu[bs][:, hs][:, :, rs])
@@ -85,7 +115,7 @@ def bf16_ulp(x: torch.Tensor) -> torch.Tensor:
 
 
 def assert_variants_agree(Oa, La, Ob, Lb, vmax: float, tag=""):
-    dmax, dsum, nbig, n = 0.0, 0.0, 0, 0
+    dmax, dsum, asum, nbig, n = 0.0, 0.0, 0.0, 0, 0
     for i in range(Oa.shape[0]):  # one batch element at a time bounds the temporaries
         a, b = Oa[i].float(), Ob[i].float()
         d = (a - b).abs()
@@ -94,11 +124,11 @@ def assert_variants_agree(Oa, La, Ob, Lb, vmax: float, tag=""):
         assert worst <= 0, f"{tag}: variants differ by {float(d.max())} at batch {i}, beyond the rounding bound"
         dmax = max(dmax, float(d.max()))
         dsum += float(d.double().sum())
+        asum += float(a.abs().double().sum())
         nbig += int((d > TOL_VARIANT).sum())
         n += d.numel()
     mean, frac = dsum / n, nbig / n
-    assert mean <= 1e-4, f"{tag}: mean variant difference {mean}"
-    assert frac <= 1e-3, f"{tag}: {frac:.2e} of the elements differ by more than 1e-3"
+    assert mean <= max(1e-4, 2.0 ** -9 * asum / n), f"{tag}: mean variant difference {mean} (mean|O| {asum / n})"
     if La is not None and Lb is not None:
         fa, fb = torch.isfinite(La), torch.isfinite(Lb)
         assert torch.equal(fa, fb), f"{tag}: LSE -inf pattern differs"

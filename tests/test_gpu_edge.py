@@ -1,0 +1,240 @@
+"""Edge cases of the HIP path against the fp64 oracle (GPU).
+
+Ragged lengths around the 64-key / 128-row tile boundaries, every group size
+the packing has to divide by, masks that empty whole rows, structured inputs
+whose answers are known exactly, scale corner cases, determinism, guard bands
+around the outputs and the error paths.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import gqa_inputs as gi
+import oracle
+from _parity import assert_variants_agree, compare_to_oracle, f64, gpu_run
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+LENGTHS_Q = [1, 2, 63, 64, 65, 77, 129, 257]
+LENGTHS_K = [1, 63, 64, 65, 127, 128, 129, 257]
+GROUPS = [1, 2, 3, 4, 8]
+
+
+def _qkv(seed, B, Sq, Sk, Hq, Hk, d, std=1.0):
+    q = gi.random_bf16(seed, (B, Sq, Hq, d), std)
+    k = gi.random_bf16(seed + 1, (B, Sk, Hk, d), std)
+    v = gi.random_bf16(seed + 2, (B, Sk, Hk, d))
+    return q, k, v
+
+
+def test_ragged_length_sweep():
+    """Every (Sq, Sk) pair of the boundary lists, cycling G, d, pack and splits; causal and not."""
+    n = 0
+    for iq, Sq in enumerate(LENGTHS_Q):
+        for ik, Sk in enumerate(LENGTHS_K):
+            G = GROUPS[(iq + ik) % len(GROUPS)]
+            Hk = 1 + (iq % 2)
+            Hq = G * Hk
+            d = 64 if (iq + ik) % 2 == 0 else 128
+            q, k, v = _qkv(100 + 10 * iq + ik, 2, Sq, Sk, Hq, Hk, d)
+            scale = gi.fp32(1 / math.sqrt(d))
+            for causal in (False, True):
+                pack = (iq + ik + int(causal)) % 2
+                ns = 1 + ((iq * 3 + ik) % 3)
+                O, L = gpu_run(q, k, v, causal, scale, pack, ns)
+                compare_to_oracle(O, L, q, k, v, causal, scale,
+                                  tag=f"Sq={Sq} Sk={Sk} G={G} Hk={Hk} d={d} causal={causal} pack={pack} ns={ns}")
+                n += 1
+    assert n == 2 * len(LENGTHS_Q) * len(LENGTHS_K)
+
+
+@pytest.mark.parametrize("G", GROUPS)
+@pytest.mark.parametrize("d", [64, 128])
+def test_group_sizes_pack_is_bitwise_equal(G, d):
+    """For every group size: both packings match the oracle and each other bit for bit."""
+    Hk = 2
+    q, k, v = _qkv(7 * G + d, 2, 131, 150, G * Hk, Hk, d)
+    scale = gi.fp32(1 / math.sqrt(d))
+    for causal in (False, True):
+        Oa, La = gpu_run(q, k, v, causal, scale, 1, 1)
+        Ob, Lb = gpu_run(q, k, v, causal, scale, 0, 1)
+        compare_to_oracle(Oa, La, q, k, v, causal, scale, tag=f"G={G} d={d} pack=1")
+        assert torch.equal(Oa, Ob) and torch.equal(La, Lb), f"G={G} d={d} causal={causal}"
+
+
+def test_head_map_structured_exact():
+    """V[b, j, g, :] = g + 1: every output of query head h is exactly h // G + 1 (the Hq=6, Hk=2 map)."""
+    pairs = [(0, 0), (1, 0), (2, 0), (3, 1), (4, 1), (5, 1)]
+    B, Sq, Sk, Hq, Hk, d = 2, 77, 100, 6, 2, 64
+    q, k, _ = _qkv(11, B, Sq, Sk, Hq, Hk, d)
+    v = torch.empty((B, Sk, Hk, d), dtype=torch.bfloat16)
+    for g in range(Hk):
+        v[:, :, g, :] = g + 1
+    for causal in (False, True):
+        for pack, ns in ((1, 1), (0, 1), (1, 2)):
+            O, _ = gpu_run(q, k, v, causal, 0.125, pack, ns)
+            Oc = O.float().cpu()
+            for h, g in pairs:
+                assert torch.all(Oc[:, :, h, :] == g + 1), (h, g, causal, pack, ns)
+            # the tiling mistake h % Hk would give head 1 the value 2
+            assert not torch.all(Oc[:, :, 1, :] == 2)
+
+
+def test_zero_queries_give_mean_of_values():
+    B, Sq, Sk, Hq, Hk, d = 1, 70, 70, 4, 2, 128
+    _, k, v = _qkv(21, B, Sq, Sk, Hq, Hk, d)
+    q = torch.zeros((B, Sq, Hq, d), dtype=torch.bfloat16)
+    for causal in (False, True):
+        O, L = gpu_run(q, k, v, causal, 0.3, 1, 1)
+        compare_to_oracle(O, L, q, k, v, causal, 0.3, tag=f"Q=0 causal={causal}")
+        cnt = (np.arange(Sq) + 1) if causal else np.full(Sq, Sk)
+        assert np.allclose(f64(L[0, 0]), np.log(cnt), atol=2e-6)
+
+
+def test_causal_first_row_is_first_value():
+    B, Sq, Sk, Hq, Hk, d = 2, 96, 96, 8, 2, 128
+    q, k, v = _qkv(31, B, Sq, Sk, Hq, Hk, d)
+    scale = gi.fp32(1 / math.sqrt(d))
+    for pack, ns in ((1, 1), (0, 2)):
+        O, L = gpu_run(q, k, v, True, scale, pack, ns)
+        G = Hq // Hk
+        for h in range(Hq):
+            assert torch.equal(O[:, 0, h, :].cpu(), v[:, 0, h // G, :]), h
+            s0 = scale * (f64(q[:, 0, h, :]) * f64(k[:, 0, h // G, :])).sum(-1)
+            assert np.allclose(f64(L[:, h, 0]), s0, atol=2e-5)
+
+
+def test_large_scores_exercise_rescaling():
+    """Q, K ~ N(0, 3^2): scores up to ~50, so the running maximum moves by many powers of two."""
+    B, Sq, Sk, Hq, Hk, d = 2, 200, 333, 8, 2, 128
+    q, k, v = _qkv(41, B, Sq, Sk, Hq, Hk, d, std=3.0)
+    scale = gi.fp32(1 / math.sqrt(d))
+    for causal in (False, True):
+        for pack, ns in ((1, 1), (0, 3)):
+            O, L = gpu_run(q, k, v, causal, scale, pack, ns)
+            compare_to_oracle(O, L, q, k, v, causal, scale, tag=f"std3 causal={causal} {pack},{ns}",
+                              derived_bound=True)
+
+
+def test_one_hot_keys():
+    """K[j*] = 10 q_i (all other keys random): the output of row i is V[j*] to bf16 rounding."""
+    B, Sq, Sk, Hq, Hk, d = 1, 8, 300, 1, 1, 64
+    q, k, v = _qkv(51, B, Sq, Sk, Hq, Hk, d)
+    for i in range(Sq):
+        k[0, 37 * i + 5, 0, :] = (10 * q[0, i, 0, :].float()).to(torch.bfloat16)
+    O, L = gpu_run(q, k, v, False, gi.fp32(1 / 8), 1, 1)
+    compare_to_oracle(O, L, q, k, v, False, gi.fp32(1 / 8), tag="one-hot", derived_bound=True)
+    for i in range(Sq):
+        assert torch.allclose(O[0, i, 0].float().cpu(), v[0, 37 * i + 5, 0].float(), atol=2e-2)
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.125, 1.0, 1e-30, -1e-41])
+def test_scale_corner_cases(scale):
+    B, Sq, Sk, Hq, Hk, d = 2, 65, 130, 4, 1, 64
+    q, k, v = _qkv(61, B, Sq, Sk, Hq, Hk, d)
+    s = gi.fp32(scale)
+    for causal in (False, True):
+        O, L = gpu_run(q, k, v, causal, s, 1, 1)
+        compare_to_oracle(O, L, q, k, v, causal, s, tag=f"scale={scale} causal={causal}")
+
+
+def test_fully_masked_rows():
+    """Causal with Sq > Sk: the first Sq - Sk rows see no key and get O = 0, LSE = -inf."""
+    B, Sq, Sk, Hq, Hk, d = 2, 300, 70, 6, 2, 64
+    q, k, v = _qkv(71, B, Sq, Sk, Hq, Hk, d)
+    for pack, ns in ((1, 1), (0, 1), (1, 2), (0, 4)):
+        O, L = gpu_run(q, k, v, True, 0.125, pack, ns)
+        compare_to_oracle(O, L, q, k, v, True, 0.125, tag=f"masked rows {pack},{ns}")
+        assert torch.all(O[:, :Sq - Sk] == 0)
+        assert torch.all(torch.isneginf(L[:, :, :Sq - Sk]))
+
+
+def test_mqa_and_mha():
+    for Hq, Hk in ((8, 1), (4, 4)):
+        q, k, v = _qkv(81 + Hq, 2, 150, 150, Hq, Hk, 128)
+        for causal in (False, True):
+            O, L = gpu_run(q, k, v, causal, gi.fp32(128 ** -0.5), -1, 0)
+            compare_to_oracle(O, L, q, k, v, causal, gi.fp32(128 ** -0.5), tag=f"Hq={Hq} Hk={Hk}")
+
+
+def test_split_counts_and_empty_splits():
+    """Many splits on few key tiles (clamped), and causal row tiles whose early splits are empty."""
+    B, Sq, Sk, Hq, Hk, d = 1, 400, 400, 4, 2, 64
+    q, k, v = _qkv(91, B, Sq, Sk, Hq, Hk, d)
+    Or, Lr = gpu_run(q, k, v, True, 0.125, 1, 1)
+    vmax = float(v.abs().max())
+    for ns in (2, 3, 5, 7, 16, 64):
+        O, L = gpu_run(q, k, v, True, 0.125, 1, ns)
+        compare_to_oracle(O, L, q, k, v, True, 0.125, tag=f"ns={ns}")
+        assert_variants_agree(Or, Lr, O, L, vmax, tag=f"ns={ns}")
+
+
+def test_deterministic():
+    w = gi.TINY.with_(B=3, Sq=200, Sk=300)
+    q, k, v = gi.make_qkv(w)
+    for variant in ((1, 1), (0, 3)):
+        a = gpu_run(q, k, v, True, w.scale, *variant)
+        b = gpu_run(q, k, v, True, w.scale, *variant)
+        assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_guard_bands_and_coverage():
+    """Outputs sit inside poisoned buffers: every element is written, nothing outside is."""
+    import grouped_query_exact_amd as g
+    B, Sq, Sk, Hq, Hk, d = 2, 131, 97, 6, 2, 64
+    q, k, v = (t.to(DEV) for t in _qkv(101, B, Sq, Sk, Hq, Hk, d))
+    n_o, n_l, guard = B * Sq * Hq * d, B * Hq * Sq, 64
+    for causal, pack, ns in ((True, 1, 1), (False, 0, 3)):
+        obuf = torch.full((n_o + 2 * guard,), -1, dtype=torch.int16, device=DEV)   # 0xFFFF: a NaN
+        lbuf = torch.full((n_l + 2 * guard,), float("nan"), dtype=torch.float32, device=DEV)
+        out = obuf[guard:guard + n_o].view(torch.bfloat16).view(B, Sq, Hq, d)
+        lse = lbuf[guard:guard + n_l].view(B, Hq, Sq)
+        g.gqa_attn_fwd(q, k, v, out, lse, causal, 0.125, pack, ns)
+        torch.cuda.synchronize()
+        assert torch.all(obuf[:guard] == -1) and torch.all(obuf[guard + n_o:] == -1)
+        assert torch.all(torch.isnan(lbuf[:guard])) and torch.all(torch.isnan(lbuf[guard + n_l:]))
+        assert not torch.isnan(out.float()).any()
+        assert not torch.isnan(lse).any()
+        compare_to_oracle(out, lse, q.cpu(), k.cpu(), v.cpu(), causal, 0.125, tag="guard")
+
+
+def test_errors_leave_outputs_untouched():
+    import grouped_query_exact_amd as g
+    q, k, v = (t.to(DEV) for t in _qkv(111, 1, 16, 16, 6, 2, 64))
+    out = torch.full_like(q, 3.0)
+    lse = torch.full((1, 6, 16), 5.0, device=DEV)
+    for kwargs, status in ((dict(pack_gqa=3), g.GQA_ERR_INVALID_ARG), (dict(num_splits=-2), g.GQA_ERR_INVALID_ARG),
+                           (dict(scale=float("inf")), g.GQA_ERR_INVALID_ARG)):
+        args = dict(pack_gqa=1, num_splits=1, scale=0.125)
+        args.update(kwargs)
+        with pytest.raises(g.GqaAttnError) as e:
+            g.gqa_attn_fwd(q, k, v, out, lse, True, args["scale"], args["pack_gqa"], args["num_splits"])
+        assert e.value.status == status
+    # Hq not a multiple of Hk, through the C-ABI directly
+    k4 = torch.zeros((1, 16, 4, 64), dtype=torch.bfloat16, device=DEV)
+    st = g.load_library().gqa_attn_fwd(q.data_ptr(), k4.data_ptr(), k4.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                       1, 16, 16, 6, 4, 64, 1, 0.125, 1, 1, None)
+    assert st == g.GQA_ERR_INVALID_ARG
+    torch.cuda.synchronize()
+    assert torch.all(out.float() == 3.0) and torch.all(lse == 5.0)
+
+
+def test_without_lse_and_on_a_side_stream():
+    import grouped_query_exact_amd as g
+    w = gi.TINY.with_(B=2)
+    q, k, v = gi.make_qkv(w)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    ref, ref_l = gpu_run(q, k, v, True, w.scale, 1, 2)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        out = torch.empty_like(qd)
+        g.gqa_attn_fwd(qd, kd, vd, out, None, True, w.scale, 1, 2)
+    s.synchronize()
+    assert torch.equal(out, ref)
+    out2 = g.gqa_attn_func(qd, kd, vd, causal=True, pack_gqa=1, num_splits=2)
+    torch.cuda.synchronize()
+    assert torch.equal(out2, ref)

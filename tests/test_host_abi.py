@@ -1,0 +1,201 @@
+"""CPU tests of the C-ABI library: exported symbols, status strings, the
+heuristic and launch plan, and argument checks that return before any HIP call.
+
+No compute is launched here (there is no GPU in this environment): every
+gqa_attn_fwd call below carries an invalid argument and must be rejected by
+the host-side checks.
+"""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gqa_attn.h")
+LIB = os.path.join(ROOT, "grouped_query_exact_amd", "libgqa_attn.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libgqa_attn.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(gqa_attn_\w+)\s*\(", text, flags=re.M)))
+
+
+def lib():
+    import grouped_query_exact_amd as g
+    return g.load_library()
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    assert names == ["gqa_attn_choose", "gqa_attn_fwd", "gqa_attn_plan", "gqa_attn_strerror"]
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\sT\s(\w+)$", out, flags=re.M))
+    for name in declared_functions():
+        assert name in exported, name
+    for name in declared_functions():
+        assert hasattr(lib(), name)
+
+
+def test_strerror():
+    import grouped_query_exact_amd as g
+    assert g.gqa_attn_strerror(0) == "success"
+    for st in (g.GQA_ERR_INVALID_ARG, g.GQA_ERR_UNSUPPORTED, g.GQA_ERR_NOMEM, g.GQA_ERR_HIP):
+        assert g.gqa_attn_strerror(st) not in ("success", "unknown status")
+    assert g.gqa_attn_strerror(12345) == "unknown status"
+
+
+def _fwd(q=1, k=1, v=1, out=1, lse=None, B=1, Sq=4, Sk=4, Hq=2, Hk=1, d=64, causal=0, scale=0.125,
+         pack=-1, ns=0):
+    """Call gqa_attn_fwd with fake (never dereferenced) pointers; only invalid calls are allowed."""
+    L = lib()
+    P = lambda x: None if x is None else ctypes.c_void_p(x * 4096)
+    return L.gqa_attn_fwd(P(q), P(k), P(v), P(out), P(lse), B, Sq, Sk, Hq, Hk, d, causal, scale, pack, ns, None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(Hq=6, Hk=4),           # Hq not a multiple of Hk (the pages' divisibility rule)
+    dict(Hk=0),
+    dict(Hq=-2),
+    dict(B=-1),
+    dict(Sq=-1),
+    dict(Sk=-3),
+    dict(Sk=0),                 # queries but no keys
+    dict(pack=2),
+    dict(pack=-2),
+    dict(ns=-1),
+    dict(scale=float("inf")),
+    dict(scale=float("nan")),
+    dict(q=None),
+    dict(k=None),
+    dict(v=None),
+    dict(out=None),
+])
+def test_invalid_arguments_are_rejected(kw):
+    import grouped_query_exact_amd as g
+    assert _fwd(**kw) == g.GQA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("d", [0, 32, 96, 256])
+def test_unsupported_head_dim(d):
+    import grouped_query_exact_amd as g
+    assert _fwd(d=d) == g.GQA_ERR_UNSUPPORTED
+
+
+def test_misaligned_pointer_is_unsupported():
+    import grouped_query_exact_amd as g
+    L = lib()
+    st = L.gqa_attn_fwd(ctypes.c_void_p(4096 + 8), ctypes.c_void_p(4096), ctypes.c_void_p(4096),
+                        ctypes.c_void_p(8192), None, 1, 4, 4, 2, 1, 64, 0, 0.125, 1, 1, None)
+    assert st == g.GQA_ERR_UNSUPPORTED
+
+
+def test_empty_problem_is_a_no_op():
+    import grouped_query_exact_amd as g
+    # B*Sq == 0: nothing to do, no pointer is touched (null pointers allowed)
+    assert _fwd(q=None, k=None, v=None, out=None, B=0) == g.GQA_OK
+    assert _fwd(q=None, k=None, v=None, out=None, Sq=0) == g.GQA_OK
+
+
+def test_choose_heuristic_shapes():
+    import grouped_query_exact_amd as g
+    # prefill: long sequences, plenty of tiles -> pack, no split
+    assert g.gqa_attn_choose(128, 2048, 2048, 32, 8, 128, True, 256) == (1, 1)
+    assert g.gqa_attn_choose(4, 2048, 2048, 32, 8, 128, True, 256) == (1, 1)
+    # short ragged sequences (Sq=77 fills 60% of a 128-row tile, 3 heads packed fill 90%)
+    assert g.gqa_attn_choose(212, 77, 77, 6, 2, 64, False, 256)[0] == 1
+    # decode: one query row per head -> pack, and split the 8192 keys
+    pk, ns = g.gqa_attn_choose(64, 1, 8192, 32, 8, 128, False, 256)
+    assert pk == 1 and ns > 1
+    # MHA: nothing to pack
+    assert g.gqa_attn_choose(8, 512, 512, 8, 8, 64, True, 256)[0] == 0
+    # invalid sizes are reported
+    with pytest.raises(g.GqaAttnError):
+        g.gqa_attn_choose(1, 4, 4, 6, 4, 64, False, 256)
+
+
+def test_plan_grid_and_workspace():
+    import grouped_query_exact_amd as g
+    p = g.gqa_attn_plan(128, 2048, 2048, 32, 8, 128, True, 1, 1, 256)
+    assert p["pack_gqa"] == 1 and p["num_splits"] == 1 and p["workspace_bytes"] == 0
+    assert p["block_n"] == 64
+    assert p["row_tiles"] * p["block_m"] >= 2048 * 4
+    assert p["grid"] == 128 * 8 * p["row_tiles"]
+    p = g.gqa_attn_plan(16, 2048, 2048, 32, 8, 128, True, 0, 4, 256)
+    assert p["pack_gqa"] == 0 and p["num_splits"] == 4
+    assert p["grid"] == 16 * 32 * p["row_tiles"] * 4
+    assert p["workspace_bytes"] == 4 * 16 * 2048 * 32 * (128 * 4 + 4)
+    # the split count is clamped to the number of key tiles
+    p = g.gqa_attn_plan(1, 1, 100, 4, 4, 64, False, 0, 16, 256)
+    assert p["num_splits"] == 2 and p["key_tiles"] == 2
+    # a single-head group never packs
+    assert g.gqa_attn_plan(2, 300, 300, 4, 4, 64, False, 1, 1, 256)["pack_gqa"] == 0
+
+
+CPP_TEST = r"""
+#include "host_logic.h"
+#include "../../include/gqa_attn.h"
+#include <cstdio>
+#include <cstdlib>
+#include <random>
+using namespace gqa;
+int main() {
+    long long checked = 0;
+    for (uint32_t d = 1; d <= 64; ++d) {
+        FastDiv f = make_fastdiv(d);
+        for (uint32_t n = 0; n < (1u << 20); ++n) {
+            if (fastdiv_host(n, f) != n / d) { std::printf("FAIL d=%u n=%u\n", d, n); return 1; }
+            ++checked;
+        }
+    }
+    std::mt19937 rng(7);
+    for (int i = 0; i < 2000000; ++i) {
+        uint32_t d = 1 + rng() % 100000, n = rng() & 0x7FFFFFFFu;
+        FastDiv f = make_fastdiv(d);
+        if (fastdiv_host(n, f) != n / d) { std::printf("FAIL d=%u n=%u\n", d, n); return 1; }
+        ++checked;
+    }
+    for (uint32_t d : {1u, 2u, 3u, 7u, 1000u}) {
+        FastDiv f = make_fastdiv(d);
+        uint32_t n = 0x7FFFFFFFu;
+        if (fastdiv_host(n, f) != n / d) { std::printf("FAIL edge d=%u\n", d); return 1; }
+    }
+    // plans for a sweep of shapes must stay internally consistent
+    for (int B : {1, 3, 64, 256}) for (int Sq : {1, 2, 77, 128, 129, 2048}) for (int Sk : {1, 63, 64, 65, 2048, 8192})
+    for (int G : {1, 2, 3, 4, 8}) for (int causal : {0, 1}) for (int pk : {-1, 0, 1}) for (int ns : {0, 1, 3, 16}) {
+        Shape s{B, Sq, Sk, 2 * G, 2, 128, causal};
+        Plan p;
+        if (make_plan(s, pk, ns, 256, &p) != GQA_OK) { std::printf("plan failed\n"); return 1; }
+        if (p.ns < 1 || p.ns > (p.key_tiles > 0 ? p.key_tiles : 1)) { std::printf("bad ns\n"); return 1; }
+        if ((long long)p.row_tiles * kBlockM < p.R || (long long)(p.row_tiles - 1) * kBlockM >= p.R) { std::printf("bad row tiles\n"); return 1; }
+        if (p.grid != (long long)B * p.units_per_b * p.row_tiles * p.ns) { std::printf("bad grid\n"); return 1; }
+    }
+    std::printf("ok %lld\n", checked);
+    return 0;
+}
+"""
+
+
+def test_fastdiv_and_plan_under_sanitizers(tmp_path):
+    """The magic-number divide equals n / d (exhaustive for d <= 64, n < 2^20; random up to 2^31),
+    and launch plans stay consistent, in a g++ build with AddressSanitizer and UBSan."""
+    csrc = os.path.join(ROOT, "grouped_query_exact_amd", "csrc")
+    src = tmp_path / "t.cpp"
+    src.write_text(CPP_TEST.replace('"host_logic.h"', f'"{csrc}/host_logic.h"')
+                   .replace('"../../include/gqa_attn.h"', f'"{ROOT}/include/gqa_attn.h"'))
+    exe = tmp_path / "t"
+    cmd = ["g++", "-std=c++17", "-O1", "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+           "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include",
+           str(src), os.path.join(csrc, "host_logic.cpp"), "-o", str(exe)]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0 and r.stdout.startswith("ok"), r.stdout + r.stderr
