@@ -1,0 +1,221 @@
+#!/usr/bin/env python3
+"""HBM traffic and kernel-trace summaries of the GQA forward kernels (rocprofv3).
+
+    python bench_traffic.py [--out-dir gpurun_out/traffic]
+
+runs, for each benchmark workload, three profiled child processes of this
+script (``--run NAME``): one ``--kernel-trace --stats`` pass, one
+``--pmc FETCH_SIZE`` pass and one ``--pmc WRITE_SIZE`` pass. It calibrates the
+two counters on a plain 1 GiB device copy (``--copy-ref``), then writes
+
+into <out-dir>/profiles/ (to be copied into profiles/):
+
+  * traffic.json: per workload, measured HBM bytes per launch of the
+    attention kernel (FETCH + WRITE, each scaled by the copy's bytes/counter
+    ratio), keyed by a hash of the kernel source so bench.py drops the figure
+    once the kernel changes;
+  * attn_fwd_<workload>.md: the trace and counter summary with the
+    commands that produced it.
+
+It never touches the GPU itself; the profiled children do.
+"""
+
+from __future__ import annotations
+
+import argparse
+import collections
+import csv
+import glob
+import hashlib
+import json
+import os
+import subprocess
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+KERNEL_SRC = os.path.join(ROOT, "grouped_query_exact_amd", "csrc", "gqa_attn_kernels.hip")
+PROFILES = os.path.join(ROOT, "profiles")
+COPY_BYTES = 1 << 30
+RUN_LAUNCHES = 4
+
+# name -> (workload factory, pack_gqa, num_splits); -1 / 0 = the library's choice
+WORKLOADS = {
+    "sweep_b128_s2048": ("sweep128", -1, 0),
+    "llama2_prefill_b4_s2048": ("llama", -1, 0),
+    "decode_b64_sk8192": ("decode", -1, 0),
+    "ragged_b212_s77": ("ragged", -1, 0),
+}
+
+
+def kernel_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def workload(name):
+    import gqa_inputs as gi
+    kind = WORKLOADS[name][0]
+    return {"sweep128": gi.sweep(128), "llama": gi.LLAMA_PREFILL, "decode": gi.DECODE,
+            "ragged": gi.RAGGED}[kind]
+
+
+# ------------------------------------------------------------- child programs
+def run_workload(name):
+    import torch
+    import grouped_query_exact_amd as g
+    import gqa_inputs as gi
+    w = workload(name)
+    _, pack, ns = WORKLOADS[name]
+    dev = torch.device("cuda:0")
+    q, k, v = gi.make_qkv_device(w, dev)
+    out = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.Sq), dtype=torch.float32, device=dev)
+    for _ in range(RUN_LAUNCHES):
+        g.gqa_attn_fwd(q, k, v, out, lse, w.causal, w.scale, pack, ns)
+    torch.cuda.synchronize()
+    plan = g.gqa_attn_plan(w.B, w.Sq, w.Sk, w.Hq, w.Hk, w.d, w.causal, pack, ns)
+    print(json.dumps({"workload": name, "launches": RUN_LAUNCHES, "plan": plan}), flush=True)
+
+
+def run_copy():
+    import torch
+    a = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda:0")
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print("copied", COPY_BYTES, "bytes x3", flush=True)
+
+
+# --------------------------------------------------------------- orchestrator
+def rocprof(args, out_dir, tag, child):
+    cmd = ["rocprofv3"] + args + ["--output-format", "csv", "-d", os.path.join(out_dir, tag), "-o", tag,
+                                  "--", sys.executable, os.path.abspath(__file__)] + child
+    env = dict(os.environ, TMPDIR="/tmp")
+    t0 = time.time()
+    r = subprocess.run(["timeout", "-s", "KILL", "300"] + cmd, cwd="/tmp", env=env, capture_output=True, text=True)
+    print(f"[traffic] {tag}: rc={r.returncode} {time.time() - t0:.1f}s", flush=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout[-3000:] + r.stderr[-3000:])
+        raise SystemExit(f"rocprofv3 pass {tag} failed")
+    return " ".join(cmd)
+
+
+def read_counter(out_dir, tag, counter):
+    """Per-dispatch sums of one counter, grouped by kernel name."""
+    files = glob.glob(os.path.join(out_dir, tag, "**", "*counter_collection.csv"), recursive=True)
+    per = collections.defaultdict(lambda: collections.defaultdict(float))
+    for path in files:
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                if row["Counter_Name"] == counter:
+                    per[row["Kernel_Name"]][row["Dispatch_Id"]] += float(row["Counter_Value"])
+    return {k: list(v.values()) for k, v in per.items()}
+
+
+def read_trace(out_dir, tag):
+    files = glob.glob(os.path.join(out_dir, tag, "**", "*kernel_stats.csv"), recursive=True)
+    rows = []
+    for path in files:
+        with open(path) as f:
+            rows.extend(csv.DictReader(f))
+    return rows
+
+
+def attention_only(d):
+    return {k: v for k, v in d.items() if "attn_fwd_kernel" in k or "combine_kernel" in k}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--run", help=argparse.SUPPRESS)
+    ap.add_argument("--copy-ref", action="store_true", help=argparse.SUPPRESS)
+    ap.add_argument("--out-dir", default=os.path.join(ROOT, "gpurun_out", "traffic"))
+    ap.add_argument("--workloads", nargs="*", default=list(WORKLOADS))
+    a = ap.parse_args()
+    if a.run:
+        return run_workload(a.run)
+    if a.copy_ref:
+        return run_copy()
+
+    out = os.path.abspath(a.out_dir)
+    os.makedirs(out, exist_ok=True)
+    cmd_cf = rocprof(["--pmc", "FETCH_SIZE"], out, "copy_fetch", ["--copy-ref"])
+    cmd_cw = rocprof(["--pmc", "WRITE_SIZE"], out, "copy_write", ["--copy-ref"])
+    copy_f = [x for k, v in read_counter(out, "copy_fetch", "FETCH_SIZE").items() if "copyBuffer" in k for x in v]
+    copy_w = [x for k, v in read_counter(out, "copy_write", "WRITE_SIZE").items() if "copyBuffer" in k for x in v]
+    fetch_scale = COPY_BYTES / (sum(copy_f) / len(copy_f) * 1024)
+    write_scale = COPY_BYTES / (sum(copy_w) / len(copy_w) * 1024)
+    print(f"[traffic] copy calibration: FETCH x{fetch_scale:.3f}, WRITE x{write_scale:.3f}", flush=True)
+
+    prof_out = os.path.join(out, "profiles")  # copied into profiles/ once reviewed
+    os.makedirs(prof_out, exist_ok=True)
+    tr_path = os.path.join(PROFILES, "traffic.json")
+    try:
+        with open(tr_path) as f:
+            traffic = json.load(f)
+    except (OSError, ValueError):
+        traffic = {}
+    if traffic.get("kernel_hash") != kernel_hash():
+        traffic = {"kernel_hash": kernel_hash(), "entries": {}}
+    traffic["calibration"] = {"copy_bytes": COPY_BYTES, "fetch_scale": fetch_scale, "write_scale": write_scale}
+
+    for name in a.workloads:
+        w = workload(name)
+        cmd_t = rocprof(["--kernel-trace", "--stats"], out, f"{name}_trace", ["--run", name])
+        cmd_f = rocprof(["--pmc", "FETCH_SIZE"], out, f"{name}_fetch", ["--run", name])
+        cmd_w = rocprof(["--pmc", "WRITE_SIZE"], out, f"{name}_write", ["--run", name])
+        fetch = attention_only(read_counter(out, f"{name}_fetch", "FETCH_SIZE"))
+        write = attention_only(read_counter(out, f"{name}_write", "WRITE_SIZE"))
+        stats = [r for r in read_trace(out, f"{name}_trace") if "attn_fwd_kernel" in r["Name"] or "combine_kernel" in r["Name"]]
+        import grouped_query_exact_amd as g  # host-only calls
+        _, pack, ns = WORKLOADS[name]
+        plan = g.gqa_attn_plan(w.B, w.Sq, w.Sk, w.Hq, w.Hk, w.d, w.causal, pack, ns, 256)
+        lines = []
+        total_bytes = 0.0
+        kernels = {}
+        for kname in sorted(set(fetch) | set(write)):
+            f_kib = sum(fetch.get(kname, [0])) / max(1, len(fetch.get(kname, [1])))
+            w_kib = sum(write.get(kname, [0])) / max(1, len(write.get(kname, [1])))
+            bytes_ = f_kib * 1024 * fetch_scale + w_kib * 1024 * write_scale
+            total_bytes += bytes_
+            kernels[kname] = {"fetch_kib": f_kib, "write_kib": w_kib, "hbm_bytes": bytes_}
+        key = f"{name}|pack{plan['pack_gqa']}|ns{plan['num_splits']}"
+        main_kernel = max(kernels, key=lambda k: kernels[k]["hbm_bytes"]) if kernels else None
+        traffic["entries"][key] = {
+            "hbm_bytes_per_launch": kernels[main_kernel]["hbm_bytes"] if main_kernel else None,
+            "hbm_bytes_per_call": total_bytes, "algorithmic_bytes": w.io_bytes, "kernels": kernels,
+            "measured": time.strftime("%Y-%m-%d %H:%M:%S"),
+        }
+        md = [f"# {name}: attention kernels, pack_gqa={plan['pack_gqa']}, num_splits={plan['num_splits']}", "",
+              f"Workload: B={w.B}, Sq={w.Sq}, Sk={w.Sk}, Hq={w.Hq}, Hk={w.Hk}, d={w.d}, causal={w.causal}, "
+              f"seeded bf16 N(0,1) inputs; {RUN_LAUNCHES} launches per profiled run. Kernel source hash {kernel_hash()}.", "",
+              "Commands (REPO = repository root on the GPU box, run from /tmp with TMPDIR=/tmp):", "",
+              "    " + cmd_t.replace(ROOT, "$REPO"), "    " + cmd_f.replace(ROOT, "$REPO"),
+              "    " + cmd_w.replace(ROOT, "$REPO"), "    " + cmd_cf.replace(ROOT, "$REPO"),
+              "    " + cmd_cw.replace(ROOT, "$REPO"), "",
+              "Kernel trace (rocprofv3 --stats):", "", "| kernel | calls | average (us) | min (us) | max (us) |", "|---|---|---|---|---|"]
+        for r in stats:
+            md.append(f"| `{r['Name'][:90]}` | {r.get('Calls')} | {float(r.get('AverageNs', 0)) / 1e3:.2f} | "
+                      f"{float(r.get('MinNs', 0)) / 1e3:.2f} | {float(r.get('MaxNs', 0)) / 1e3:.2f} |")
+        md += ["", f"HBM counters per dispatch (FETCH x{fetch_scale:.3f}, WRITE x{write_scale:.3f} from a 1 GiB copy):", "",
+               "| kernel | FETCH_SIZE (KiB) | WRITE_SIZE (KiB) | HBM bytes (scaled) |", "|---|---|---|---|"]
+        for kname, kv in kernels.items():
+            md.append(f"| `{kname[:90]}` | {kv['fetch_kib']:.0f} | {kv['write_kib']:.0f} | {kv['hbm_bytes'] / 1e9:.4f} GB |")
+        md += ["", f"Algorithmic bytes (Q + K + V + O + LSE once): {w.io_bytes / 1e9:.4f} GB; "
+                   f"measured / algorithmic = {total_bytes / w.io_bytes:.3f}.", ""]
+        fname = f"attn_fwd_{name}.md"
+        with open(os.path.join(prof_out, fname), "w") as f:
+            f.write("\n".join(md))
+        print(f"[traffic] {name}: {total_bytes / 1e9:.4f} GB per call (algorithmic {w.io_bytes / 1e9:.4f})", flush=True)
+
+    with open(os.path.join(prof_out, "traffic.json"), "w") as f:
+        json.dump(traffic, f, indent=1, sort_keys=True)
+    print(f"[traffic] wrote {prof_out}", flush=True)
+
+
+if __name__ == "__main__":
+    main()
