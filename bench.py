@@ -239,7 +239,8 @@ def main():
             msd, pl = measure(g, wd, qd, kd, vd, pack, ns, args.steps, 5)
             dec[f"pack{pl['pack_gqa']}_ns{pl['num_splits']}" + ("_auto" if pack < 0 else "")] = {
                 "us": round(msd * 1e3, 2), "GB_per_s": round(wd.io_bytes / (msd * 1e-3) / 1e9, 1),
-                "frac_hbm_peak": round(wd.io_bytes / (msd * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+                "frac_hbm_peak": round(wd.io_bytes / (msd * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                "kernel": "attn_decode_kernel" if pl["block_m"] == 32 else "attn_fwd_kernel"}
             print(f"[bench] decode pack={pack} ns={ns}: {msd*1e3:.1f} us", file=sys.stderr, flush=True)
         extra["decode_b64_sk8192"] = dec
         del qd, kd, vd

@@ -38,6 +38,7 @@ sys.path.insert(0, ROOT)
 KERNEL_SRC = os.path.join(ROOT, "grouped_query_exact_amd", "csrc", "gqa_attn_kernels.hip")
 PROFILES = os.path.join(ROOT, "profiles")
 COPY_BYTES = 1 << 30
+KERNEL_NAMES = ("attn_fwd_kernel", "attn_decode_kernel", "combine_kernel")
 RUN_LAUNCHES = 4
 
 # name -> (workload factory, pack_gqa, num_splits); -1 / 0 = the library's choice
@@ -126,7 +127,7 @@ def read_trace(out_dir, tag):
 
 
 def attention_only(d):
-    return {k: v for k, v in d.items() if "attn_fwd_kernel" in k or "combine_kernel" in k}
+    return {k: v for k, v in d.items() if any(n in k for n in KERNEL_NAMES)}
 
 
 def main():
@@ -170,7 +171,7 @@ def main():
         cmd_w = rocprof(["--pmc", "WRITE_SIZE"], out, f"{name}_write", ["--run", name])
         fetch = attention_only(read_counter(out, f"{name}_fetch", "FETCH_SIZE"))
         write = attention_only(read_counter(out, f"{name}_write", "WRITE_SIZE"))
-        stats = [r for r in read_trace(out, f"{name}_trace") if "attn_fwd_kernel" in r["Name"] or "combine_kernel" in r["Name"]]
+        stats = [r for r in read_trace(out, f"{name}_trace") if any(n in r["Name"] for n in KERNEL_NAMES)]
         import grouped_query_exact_amd as g  # host-only calls
         _, pack, ns = WORKLOADS[name]
         plan = g.gqa_attn_plan(w.B, w.Sq, w.Sk, w.Hq, w.Hk, w.d, w.causal, pack, ns, 256)

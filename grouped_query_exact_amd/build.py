@@ -18,8 +18,11 @@ LIB = os.path.join(HERE, "libgqa_attn.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 
 ARCH = "gfx950"
-# Packed-fp32 VALU instructions are disabled for all device code.
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Packed-fp32 VALU instructions are disabled for all device code. MFMA results
+# stay in ordinary VGPRs (no accumulator-register copies around the online
+# softmax rescale of the output accumulators).
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                "-mllvm", "-amdgpu-mfma-vgpr-form=1"]
 COMMON = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-result"]
 
 SOURCES = [

@@ -96,8 +96,8 @@ int gqa_attn_plan(int B, int Sq, int Sk, int Hq, int Hk, int d, int causal, int 
     if (st != GQA_OK) return st;
     plan->pack_gqa = p.pack;
     plan->num_splits = p.ns;
-    plan->block_m = gqa::kBlockM;
-    plan->block_n = gqa::kBlockN;
+    plan->block_m = p.block_m;
+    plan->block_n = p.block_n;
     plan->row_tiles = p.row_tiles;
     plan->key_tiles = p.key_tiles;
     plan->grid = p.grid;
@@ -160,12 +160,17 @@ int gqa_attn_fwd(const void* q, const void* k, const void* v, void* out, float* 
         if (log_enabled())
             std::fprintf(stderr,
                          "[gqa_attn] B=%d Sq=%d Sk=%d Hq=%d Hk=%d d=%d causal=%d -> pack=%d ns=%d "
-                         "row_tiles=%d key_tiles=%d grid=%lld combine_grid=%lld ws=%lld\n",
-                         B, Sq, Sk, Hq, Hk, d, s.causal, plan.pack, plan.ns, plan.row_tiles, plan.key_tiles,
+                         "kernel=%s row_tiles=%d key_tiles=%d grid=%lld combine_grid=%lld ws=%lld\n",
+                         B, Sq, Sk, Hq, Hk, d, s.causal, plan.pack, plan.ns, plan.decode ? "decode" : "tiled",
+                         plan.row_tiles, plan.key_tiles,
                          plan.grid, plan.combine_grid, plan.workspace_bytes);
 
+        auto launch = [&](bool split) {
+            return plan.decode ? gqa::launch_decode(p, d, s.causal != 0, split, stream)
+                               : gqa::launch_attention(p, d, s.causal != 0, split, stream);
+        };
         if (plan.ns == 1) {
-            hipError_t e = gqa::launch_attention(p, d, s.causal != 0, false, stream);
+            hipError_t e = launch(false);
             return e == hipSuccess ? GQA_OK : GQA_ERR_HIP;
         }
 
@@ -178,7 +183,7 @@ int gqa_attn_fwd(const void* q, const void* k, const void* v, void* out, float* 
         const int64_t rows = (int64_t)B * Sq * Hq;
         p.opart = (float*)ws;
         p.lpart = (float*)ws + (int64_t)plan.ns * rows * d;
-        hipError_t e = gqa::launch_attention(p, d, s.causal != 0, true, stream);
+        hipError_t e = launch(true);
         if (e == hipSuccess) {
             gqa::CombineParams cp{};
             cp.opart = p.opart;

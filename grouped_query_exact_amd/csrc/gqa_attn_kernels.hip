@@ -115,6 +115,12 @@ __device__ __forceinline__ void lds_dma16(const void* base, uint32_t voff, LDS v
 }
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Wait until at most N vector-memory operations of this wave are in flight.
+template <int N>
+__device__ __forceinline__ void wait_vmem_n() {
+    static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit field");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
 // Exchange with the lane 32 positions away: returns {v_self_or_partner...}
 // such that max/sum of the two components is the reduction over lanes l and l^32.
@@ -399,6 +405,244 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
 }
 
+// Decode-shaped work (the pages' decode regime: one or a few new tokens per
+// sequence against a long KV cache, bound by reading K and V from HBM): a
+// head unit has at most 32 query rows (with PackGQA, the G query heads of a
+// KV group times the new tokens), so one wavefront holds them all. Each
+// workgroup is that single wavefront: it streams its split of the keys in
+// tiles of 32 through a ring of STAGES LDS stages, keeping STAGES-1 tiles in
+// flight and waiting only for the oldest (no workgroup barrier), so several
+// independent workgroups per compute unit keep HBM busy. The arithmetic per
+// tile is the same as in the tiled kernel (transposed MFMA products, lazy
+// online softmax in base 2), on one block of 32 keys.
+template <int D, bool CAUSAL, bool SPLIT, int STAGES>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void attn_decode_kernel(const FwdParams p) {
+    constexpr int BN = kDecBlockN;                 // keys per tile
+    constexpr int TILE_B = BN * D * 2;             // bytes of one K or V tile
+    constexpr int NCH = D / 8;                     // 16-byte chunks per row
+    constexpr int NLOAD = BN * NCH / 64;           // 16-byte copies per lane per tensor and tile
+    static_assert(BN == 32, "one 32-key MFMA block per tile");
+    __shared__ __attribute__((aligned(16))) uint16_t smem[STAGES * 2 * BN * D];
+    LDS char* lds = (LDS char*)smem;               // stage s: K tile, then V tile
+
+    const int lane = threadIdx.x;
+    const int col = lane & 31, half = lane >> 5;
+
+    // ---- work item: (batch, head unit, split), split fastest
+    const int item = blockIdx.x;
+    const int s = item % p.ns;
+    const int tmp = item / p.ns;
+    const int unit = tmp % p.units_per_b;
+    const int b = tmp / p.units_per_b;
+    const int g = p.Gp > 1 ? unit : unit / p.G;   // KV head
+    const int h0 = p.Gp > 1 ? unit * p.G : unit;  // first query head of the unit
+
+    // ---- this lane's row (all R <= 32 rows of the head unit): token ti, head hh
+    const int r = col;
+    const bool row_valid = r < p.R;
+    const int rc = min(r, p.R - 1);
+    const int ti = (int)fdiv((uint32_t)rc, p.gmul, p.gshift);
+    const int hh = h0 + (rc - ti * p.Gp);
+    const int koff = p.Sk - p.Sq;  // bottom-right causal offset
+
+    bf16x8 qreg[D / 16];
+    {
+        const uint16_t* qrow = p.q + (((int64_t)b * p.Sq + ti) * p.Hq + hh) * D;
+#pragma unroll
+        for (int dc = 0; dc < D / 16; ++dc) {
+            u32x4 w = *(const u32x4*)(qrow + dc * 16 + half * 8);
+            w = (w & p.qand) ^ p.qsign;
+            qreg[dc] = __builtin_bit_cast(bf16x8, w);
+        }
+    }
+
+    // ---- key tiles of this split. The unit's rows are tokens 0 .. Sq-1.
+    int kv_end = p.Sk;
+    if (CAUSAL) kv_end = min(p.Sk, p.Sq - 1 + koff + 1);
+    const int T = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
+    int t_begin = 0, t_end = T;
+    if (SPLIT) {
+        t_begin = (int)(((int64_t)s * T) / p.ns);
+        t_end = (int)(((int64_t)(s + 1) * T) / p.ns);
+    }
+    const int n = t_end - t_begin;
+
+    // ---- tile copies: per-lane byte offsets inside a tile
+    const int64_t kv_stride_b = (int64_t)p.Hk * D * 2;
+    const char* kbase = (const char*)(p.k + ((int64_t)b * p.Sk * p.Hk + g) * D);
+    const char* vbase = (const char*)(p.v + ((int64_t)b * p.Sk * p.Hk + g) * D);
+    uint32_t goff[NLOAD];
+#pragma unroll
+    for (int u = 0; u < NLOAD; ++u) {
+        const int ci = u * 64 + lane;
+        const int row = ci / NCH;
+        goff[u] = (uint32_t)(row * kv_stride_b + (((ci % NCH) ^ swz<D>(row)) * 16));
+    }
+    auto issue = [&](int t, int stage) {
+        const int kv0 = t * BN;
+        LDS char* kt = lds + stage * 2 * TILE_B;
+        LDS char* vt = kt + TILE_B;
+        const char* kg = kbase + kv0 * kv_stride_b;
+        const char* vg = vbase + kv0 * kv_stride_b;
+        if (kv0 + BN <= p.Sk) {
+#pragma unroll
+            for (int u = 0; u < NLOAD; ++u) {
+                lds_dma16(kg, goff[u], kt + u * 1024);
+                lds_dma16(vg, goff[u], vt + u * 1024);
+            }
+        } else {  // ragged last tile: rows past the end re-read the last key (masked later)
+#pragma unroll
+            for (int u = 0; u < NLOAD; ++u) {
+                const int ci = u * 64 + lane;
+                const int row = ci / NCH;
+                const int key = min(kv0 + row, p.Sk - 1) - kv0;
+                const uint32_t o = (uint32_t)(key * kv_stride_b + (((ci % NCH) ^ swz<D>(row)) * 16));
+                lds_dma16(kg, o, kt + u * 1024);
+                lds_dma16(vg, o, vt + u * 1024);
+            }
+        }
+    };
+
+    // ---- per-lane LDS operand offsets (as in the tiled kernel, one key block)
+    const int krow0 = pi32(col);
+    uint32_t kofs[D / 16];
+#pragma unroll
+    for (int dc = 0; dc < D / 16; ++dc) kofs[dc] = krow0 * (D * 2) + (((2 * dc + half) ^ swz<D>(krow0)) * 16);
+    const int u16 = lane & 15, qq = (lane >> 4) & 1;
+    const int rho = ((u16 & 1) << 1) | ((u16 >> 1) & 1);
+    uint32_t vofs[D / 32][2];
+#pragma unroll
+    for (int cb = 0; cb < D / 32; ++cb)
+#pragma unroll
+        for (int rr = 0; rr < 2; ++rr) {
+            const int vrow = half * 8 + rr * 4 + (u16 >> 2);
+            const int vcol = cb * 32 + qq * 16 + rho * 4;
+            vofs[cb][rr] = vrow * (D * 2) + (((vcol >> 3) ^ swz<D>(vrow)) * 16) + (vcol & 7) * 2;
+        }
+
+    f32x16 oacc[D / 32];
+#pragma unroll
+    for (int cb = 0; cb < D / 32; ++cb) oacc[cb] = f32x16{};
+    float m_run = -__builtin_inff();
+    float l_part[4] = {0.f, 0.f, 0.f, 0.f};
+    const float c = p.c;
+    const int jlim = CAUSAL ? min(p.Sk - 1, ti + koff) : p.Sk - 1;
+
+    auto compute = [&](int stage, int kv0) {
+        const LDS char* kt = lds + stage * 2 * TILE_B;
+        const LDS char* vt = kt + TILE_B;
+        f32x16 sacc = f32x16{};
+#pragma unroll
+        for (int dc = 0; dc < D / 16; ++dc) {
+            const bf16x8 a = *(const LDS bf16x8*)(kt + kofs[dc]);
+            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[dc], sacc, 0, 0, 0);
+        }
+        // slot i of this lane holds key kv0 + 16*(i/8) + 8*half + (i%8)
+        if ((kv0 + BN > p.Sk) || (CAUSAL && kv0 + BN - 1 > koff)) {
+            const int lim = jlim - kv0 - half * 8;
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                if (((i >> 3) << 4) + (i & 7) > lim) sacc[i] = -__builtin_inff();
+        }
+        float t0 = fmaxf(fmaxf(sacc[0], sacc[1]), sacc[2]);
+        float t1 = fmaxf(fmaxf(sacc[3], sacc[4]), sacc[5]);
+        float t2 = fmaxf(fmaxf(sacc[6], sacc[7]), sacc[8]);
+        float t3 = fmaxf(fmaxf(sacc[9], sacc[10]), sacc[11]);
+        t0 = fmaxf(fmaxf(t0, sacc[12]), sacc[13]);
+        t1 = fmaxf(fmaxf(t1, sacc[14]), sacc[15]);
+        const float mx = xhalf_max(fmaxf(fmaxf(t0, t1), fmaxf(t2, t3)));
+        const float mxs = (mx == -__builtin_inff()) ? -__builtin_inff() : mx * c;
+        float alpha = 1.f;
+        if (mxs > m_run + kRescaleThreshold) {
+            alpha = __builtin_amdgcn_exp2f(m_run - mxs);
+            m_run = mxs;
+        }
+        if (__ballot(alpha != 1.f)) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) l_part[i] *= alpha;
+#pragma unroll
+            for (int cb = 0; cb < D / 32; ++cb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) oacc[cb][i] *= alpha;
+        }
+        const float moff = (m_run == -__builtin_inff()) ? 0.f : m_run;
+        bf16x8 pk[2];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[i], c, -moff));
+            l_part[i & 3] += x;
+            pk[i >> 3][i & 7] = (__bf16)x;
+        }
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+            for (int cb = 0; cb < D / 32; ++cb) {
+                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS s16x4*)(vt + vofs[cb][0] + kk * 16 * D * 2));
+                const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS s16x4*)(vt + vofs[cb][1] + kk * 16 * D * 2));
+                const s16x8 av = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                oacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), pk[kk],
+                                                                     oacc[cb], 0, 0, 0);
+            }
+        }
+    };
+
+    // ---- ring: tile j lives in stage j % STAGES. Before computing tile j the
+    // wave starts tile j+STAGES-1 (into the stage tile j-1 used, whose reads
+    // are complete) and waits until only the copies of the tiles after j are
+    // still in flight. Copies complete in issue order.
+#pragma unroll
+    for (int i = 0; i < STAGES - 1; ++i)
+        if (i < n) issue(t_begin + i, i);
+    for (int j = 0; j < n; ++j) {
+        if (j + STAGES - 1 < n) {
+            issue(t_begin + j + STAGES - 1, (j + STAGES - 1) % STAGES);
+            wait_vmem_n<2 * NLOAD * (STAGES - 1)>();
+        } else {
+            wait_vmem();
+        }
+        compute(j % STAGES, (t_begin + j) * BN);
+    }
+
+    // ---- epilogue
+    const float l_tot = xhalf_sum((l_part[0] + l_part[1]) + (l_part[2] + l_part[3]));
+    const bool live = l_tot > 0.f;
+    const float inv = live ? 1.f / l_tot : 0.f;
+    const float lse_val = live ? (m_run + __log2f(l_tot)) * kLn2 : -__builtin_inff();
+    const int64_t grow = ((int64_t)b * p.Sq + ti) * p.Hq + hh;
+    if (!row_valid) return;
+    if (!SPLIT) {
+        uint16_t* orow = p.o + grow * D;
+#pragma unroll
+        for (int cb = 0; cb < D / 32; ++cb)
+#pragma unroll
+            for (int run = 0; run < 2; ++run) {
+                bf16x8 ov;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) ov[i] = (__bf16)(oacc[cb][run * 8 + i] * inv);
+                *(bf16x8*)(orow + cb * 32 + run * 16 + half * 8) = ov;
+            }
+        if (half == 0 && p.lse) p.lse[((int64_t)b * p.Hq + hh) * p.Sq + ti] = lse_val;
+    } else {
+        const int64_t rows = (int64_t)p.B * p.Sq * p.Hq;
+        float* orow = p.opart + ((int64_t)s * rows + grow) * D;
+#pragma unroll
+        for (int cb = 0; cb < D / 32; ++cb)
+#pragma unroll
+            for (int run = 0; run < 2; ++run) {
+                f32x4 v0, v1;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    v0[i] = oacc[cb][run * 8 + i] * inv;
+                    v1[i] = oacc[cb][run * 8 + 4 + i] * inv;
+                }
+                float* dst = orow + cb * 32 + run * 16 + half * 8;
+                *(f32x4*)dst = v0;
+                *(f32x4*)(dst + 4) = v1;
+            }
+        if (half == 0) p.lpart[(int64_t)s * rows + grow] = lse_val;
+    }
+}
+
 // Merge of split partials: LSE = M + ln sum_s exp(LSE_s - M) with
 // M = max_s LSE_s, O = sum_s exp(LSE_s - LSE) O_s. A row whose splits are all
 // empty gets O = 0 and LSE = -inf. One row per D/4 lanes, 4 columns a lane.
@@ -451,6 +695,21 @@ hipError_t launch_attention(const FwdParams& p, int d, bool causal, bool split, 
     }
     if (causal) return split ? launch_attn<64, true, true>(p, stream) : launch_attn<64, true, false>(p, stream);
     return split ? launch_attn<64, false, true>(p, stream) : launch_attn<64, false, false>(p, stream);
+}
+
+template <int D, bool CAUSAL, bool SPLIT>
+static hipError_t launch_dec(const FwdParams& p, hipStream_t stream) {
+    hipLaunchKernelGGL((attn_decode_kernel<D, CAUSAL, SPLIT, kDecStages>), dim3(p.grid), dim3(kDecThreads), 0, stream, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode(const FwdParams& p, int d, bool causal, bool split, hipStream_t stream) {
+    if (d == 128) {
+        if (causal) return split ? launch_dec<128, true, true>(p, stream) : launch_dec<128, true, false>(p, stream);
+        return split ? launch_dec<128, false, true>(p, stream) : launch_dec<128, false, false>(p, stream);
+    }
+    if (causal) return split ? launch_dec<64, true, true>(p, stream) : launch_dec<64, true, false>(p, stream);
+    return split ? launch_dec<64, false, true>(p, stream) : launch_dec<64, false, false>(p, stream);
 }
 
 hipError_t launch_combine(const CombineParams& p, int d, long long grid, hipStream_t stream) {

@@ -31,16 +31,16 @@ int check_sizes(const Shape& s, float scale, int pack_gqa, int num_splits) {
 
 static long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
 
-// Key tiles needed by the row tile holding query rows [r0, r1) of a head unit.
-static int key_tiles_for(const Shape& s, int Gp, long long r0, long long r1) {
+// Key tiles (of bn keys) needed by the last row of a tile ending at row r1
+// of a head unit.
+static int key_tiles_for(const Shape& s, int Gp, long long r1, int bn) {
     long long kv_end = s.Sk;
     if (s.causal) {
         long long i_max = (r1 - 1) / Gp;
         kv_end = std::min<long long>(s.Sk, i_max + (s.Sk - s.Sq) + 1);
     }
     if (kv_end <= 0) return 0;
-    (void)r0;
-    return (int)ceil_div(kv_end, kBlockN);
+    return (int)ceil_div(kv_end, bn);
 }
 
 void choose(const Shape& s, int num_cus, int* pack_gqa, int* num_splits) {
@@ -57,15 +57,18 @@ void choose(const Shape& s, int num_cus, int* pack_gqa, int* num_splits) {
     const int pack = (G > 1 && util_p >= util_np) ? 1 : 0;
     *pack_gqa = pack;
 
-    // Split the keys when the grid is too small to fill the GPU. A workgroup
-    // that owns only a few query rows is memory-bound (decode): it then needs
-    // many more workgroups in flight to cover HBM latency.
+    // Split the keys when the grid is too small to fill the GPU. The tiled
+    // kernel wants two workgroups per compute unit. The decode kernel (at
+    // most 32 rows, memory-bound) also wants two per compute unit, each with
+    // kDecStages-1 tiles in flight: measured on MI355X, more and shorter
+    // workgroups only add tail and merge costs.
     const int Gp = pack ? G : 1;
     const long long R = (long long)s.Sq * Gp;
-    const long long units = (long long)s.B * (pack ? s.Hk : s.Hq) * ceil_div(R, kBlockM);
-    const int T = key_tiles_for(s, Gp, std::max<long long>(0, R - kBlockM), R);
-    const bool memory_bound = R <= kBlockM / 4;
-    const long long target = (memory_bound ? 8LL : 2LL) * num_cus;
+    const bool decode = R <= kDecBlockM;
+    const int bm = decode ? kDecBlockM : kBlockM, bn = decode ? kDecBlockN : kBlockN;
+    const long long units = (long long)s.B * (pack ? s.Hk : s.Hq) * ceil_div(R, bm);
+    const int T = R > 0 ? key_tiles_for(s, Gp, R, bn) : 0;
+    const long long target = 2LL * num_cus;
     int ns = 1;
     if (units > 0 && units < target && T > 1) {
         ns = (int)std::min<long long>(ceil_div(target, units), 16);
@@ -90,8 +93,11 @@ int make_plan(const Shape& s, int pack_gqa, int num_splits, int num_cus, Plan* p
     p->units_per_b = pack ? s.Hk : s.Hq;
     p->R = (long long)s.Sq * p->Gp;
     if (p->R > INT_MAX / 2) return GQA_ERR_INVALID_ARG;
-    p->row_tiles = (int)ceil_div(p->R, kBlockM);
-    p->key_tiles = p->R > 0 ? key_tiles_for(s, p->Gp, std::max<long long>(0, p->R - kBlockM), p->R) : 0;
+    p->decode = p->R <= kDecBlockM ? 1 : 0;
+    p->block_m = p->decode ? kDecBlockM : kBlockM;
+    p->block_n = p->decode ? kDecBlockN : kBlockN;
+    p->row_tiles = (int)ceil_div(p->R, p->block_m);
+    p->key_tiles = p->R > 0 ? key_tiles_for(s, p->Gp, p->R, p->block_n) : 0;
     ns = std::max(1, std::min(ns, std::max(1, p->key_tiles)));
     p->ns = ns;
     p->grid = (long long)s.B * p->units_per_b * p->row_tiles * ns;

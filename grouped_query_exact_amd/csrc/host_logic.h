@@ -13,6 +13,14 @@ constexpr int kBlockM = 128;
 constexpr int kBlockN = 64;
 constexpr int kThreads = 256;
 
+// Decode-shaped launches (at most kDecBlockM query rows per head unit, e.g.
+// one new token of a KV group): one wavefront per workgroup streaming tiles
+// of kDecBlockN keys through a ring of kDecStages LDS stages.
+constexpr int kDecBlockM = 32;
+constexpr int kDecBlockN = 32;
+constexpr int kDecThreads = 64;
+constexpr int kDecStages = 4;
+
 // Division by a runtime constant through a precomputed multiplier (the
 // batch-sensitivity article, "PackGQA" mechanism 3, precomputes the
 // query-head -> KV-head map with a fast divide-and-modulo). Round-up method:
@@ -40,12 +48,15 @@ int check_sizes(const Shape& s, float scale, int pack_gqa, int num_splits);
 void choose(const Shape& s, int num_cus, int* pack_gqa, int* num_splits);
 
 struct Plan {
+    int decode;         // 1: decode kernel (R <= kDecBlockM), 0: tiled kernel
+    int block_m;        // query rows per tile
+    int block_n;        // keys per tile
     int pack;           // resolved pack flag
     int G;              // query heads per KV head
     int Gp;             // rows per token in a tile: G if packed, else 1
     int units_per_b;    // head units per batch element: Hk if packed, else Hq
     long long R;        // query rows per head unit: Sq * Gp
-    int row_tiles;      // ceil(R / kBlockM)
+    int row_tiles;      // ceil(R / block_m)
     int key_tiles;      // key tiles of the longest row tile
     int ns;             // resolved, clamped split count
     long long grid;     // attention workgroups

@@ -21,7 +21,7 @@ struct FwdParams {
     int Gp;             // rows per token in a tile: G when packed, 1 otherwise
     uint32_t gmul, gshift;  // magic divisor of Gp
     int R;              // query rows per head unit: Sq * Gp
-    int row_tiles;      // ceil(R / kBlockM)
+    int row_tiles;      // ceil(R / rows per tile)
     int units_per_b;    // Hk when packed, Hq otherwise
     int ns;             // key splits
     int grid;           // workgroups
@@ -40,6 +40,7 @@ struct CombineParams {
 };
 
 hipError_t launch_attention(const FwdParams& p, int d, bool causal, bool split, hipStream_t stream);
+hipError_t launch_decode(const FwdParams& p, int d, bool causal, bool split, hipStream_t stream);
 hipError_t launch_combine(const CombineParams& p, int d, long long grid, hipStream_t stream);
 
 }  // namespace gqa

@@ -1,0 +1,104 @@
+"""The decode kernel (at most 32 query rows per head unit) against the fp64 oracle (GPU).
+
+Decode-shaped work -- one or a few new tokens per sequence against a long KV
+cache, the pages' memory-bound regime -- runs on its own kernel: one
+wavefront per workgroup, 32-key tiles, a ring of LDS stages. These cases
+cover what is particular to it: the ring's head and tail (splits of 1 to 5
+tiles), ragged key lengths around the 32-key tile, the 32-row capacity on
+both sides of the boundary with the tiled kernel, causal rows that see no key
+at all, both head dimensions and every split count up to one tile per split.
+"""
+
+import math
+
+import pytest
+import torch
+
+import gqa_inputs as gi
+from _parity import assert_variants_agree, compare_to_oracle, gpu_run
+
+pytestmark = pytest.mark.gpu
+
+
+def _qkv(seed, B, Sq, Sk, Hq, Hk, d):
+    return (gi.random_bf16(seed, (B, Sq, Hq, d)), gi.random_bf16(seed + 1, (B, Sk, Hk, d)),
+            gi.random_bf16(seed + 2, (B, Sk, Hk, d)))
+
+
+def _plan(q, k, causal, pack, ns):
+    import grouped_query_exact_amd as g
+    B, Sq, Hq, d = q.shape
+    Sk, Hk = k.shape[1], k.shape[2]
+    return g.gqa_attn_plan(B, Sq, Sk, Hq, Hk, d, causal, pack, ns, 256)
+
+
+# Sk around the 32-key tile: 1 .. 5 tiles, full and ragged last tiles
+SK_RING = [1, 31, 32, 33, 64, 95, 96, 97, 160, 161]
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("Sk", SK_RING)
+def test_one_token_ring_head_and_tail(d, Sk):
+    """One new token of 3 groups of 4 heads: every tile count of the ring, causal and not, ns 1 and 2."""
+    q, k, v = _qkv(9000 + Sk + d, 2, 1, Sk, 12, 3, d)
+    scale = gi.fp32(1 / math.sqrt(d))
+    for causal in (False, True):
+        for ns in (1, 2):
+            plan = _plan(q, k, causal, 1, ns)
+            assert plan["block_m"] == 32 and plan["block_n"] == 32
+            O, L = gpu_run(q, k, v, causal, scale, 1, ns)
+            compare_to_oracle(O, L, q, k, v, causal, scale, tag=f"d={d} Sk={Sk} causal={causal} ns={ns}")
+
+
+@pytest.mark.parametrize("Sq,G,pack", [(8, 4, 1), (4, 8, 1), (32, 4, 0), (3, 3, 1), (2, 1, 0)])
+def test_rows_up_to_capacity(Sq, G, pack):
+    """Up to 32 rows per head unit (packed and not), causal with Sq > 1, ragged Sk, several splits."""
+    Hk = 2
+    for Sk in (40, 129, 1000):
+        q, k, v = _qkv(9100 + Sq * 10 + G + Sk, 2, Sq, Sk, G * Hk, Hk, 64 if Sq % 2 else 128)
+        d = q.shape[-1]
+        scale = gi.fp32(1 / math.sqrt(d))
+        for causal in (False, True):
+            for ns in (1, 3, 7):
+                plan = _plan(q, k, causal, pack, ns)
+                assert plan["block_m"] == 32, plan
+                O, L = gpu_run(q, k, v, causal, scale, pack, ns)
+                compare_to_oracle(O, L, q, k, v, causal, scale,
+                                  tag=f"Sq={Sq} G={G} pack={pack} Sk={Sk} causal={causal} ns={ns}")
+
+
+def test_capacity_boundary_between_kernels():
+    """Sq=9, G=4: packed rows (36) go to the tiled kernel, unpacked rows (9) to the decode
+    kernel; both match the oracle and agree with each other within the variant bound."""
+    q, k, v = _qkv(9200, 3, 9, 700, 16, 4, 128)
+    scale = gi.fp32(1 / math.sqrt(128))
+    for causal in (False, True):
+        assert _plan(q, k, causal, 1, 1)["block_m"] == 128
+        assert _plan(q, k, causal, 0, 1)["block_m"] == 32
+        Ot, Lt = gpu_run(q, k, v, causal, scale, 1, 1)
+        Od, Ld = gpu_run(q, k, v, causal, scale, 0, 1)
+        compare_to_oracle(Ot, Lt, q, k, v, causal, scale, tag=f"tiled causal={causal}")
+        compare_to_oracle(Od, Ld, q, k, v, causal, scale, tag=f"decode causal={causal}")
+        assert_variants_agree(Ot, Lt, Od, Ld, float(v.float().abs().max()), tag=f"tiled vs decode causal={causal}")
+
+
+def test_causal_rows_that_see_no_key():
+    """Bottom-right causal with Sq > Sk: the first Sq - Sk tokens see no key (O = 0, LSE = -inf)."""
+    q, k, v = _qkv(9300, 2, 8, 3, 8, 2, 64)
+    for pack, ns in ((1, 1), (0, 1), (1, 2)):
+        O, L = gpu_run(q, k, v, True, 0.125, pack, ns)
+        compare_to_oracle(O, L, q, k, v, True, 0.125, tag=f"pack={pack} ns={ns}")
+        assert torch.all(O[:, :5].float() == 0)
+        assert torch.all(torch.isneginf(L[:, :, :5]))
+        assert torch.all(torch.isfinite(L[:, :, 5:]))
+
+
+def test_one_tile_per_split():
+    """As many splits as tiles (every split holds exactly one tile), and more splits than tiles."""
+    q, k, v = _qkv(9400, 1, 1, 32 * 16, 8, 2, 128)
+    scale = gi.fp32(1 / math.sqrt(128))
+    for ns in (16, 40):
+        plan = _plan(q, k, False, 1, ns)
+        assert plan["num_splits"] == 16
+        O, L = gpu_run(q, k, v, False, scale, 1, ns)
+        compare_to_oracle(O, L, q, k, v, False, scale, tag=f"ns={ns}")

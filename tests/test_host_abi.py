@@ -112,9 +112,11 @@ def test_choose_heuristic_shapes():
     assert g.gqa_attn_choose(4, 2048, 2048, 32, 8, 128, True, 256) == (1, 1)
     # short ragged sequences (Sq=77 fills 60% of a 128-row tile, 3 heads packed fill 90%)
     assert g.gqa_attn_choose(212, 77, 77, 6, 2, 64, False, 256)[0] == 1
-    # decode: one query row per head -> pack, and split the 8192 keys
-    pk, ns = g.gqa_attn_choose(64, 1, 8192, 32, 8, 128, False, 256)
-    assert pk == 1 and ns > 1
+    # decode: one query row per head -> pack; 64 x 8 groups already give two
+    # workgroups per compute unit, 8 x 8 groups need the keys split
+    assert g.gqa_attn_choose(64, 1, 8192, 32, 8, 128, False, 256) == (1, 1)
+    pk, ns = g.gqa_attn_choose(8, 1, 8192, 32, 8, 128, False, 256)
+    assert pk == 1 and ns == 8
     # MHA: nothing to pack
     assert g.gqa_attn_choose(8, 512, 512, 8, 8, 64, True, 256)[0] == 0
     # invalid sizes are reported
@@ -133,9 +135,17 @@ def test_plan_grid_and_workspace():
     assert p["pack_gqa"] == 0 and p["num_splits"] == 4
     assert p["grid"] == 16 * 32 * p["row_tiles"] * 4
     assert p["workspace_bytes"] == 4 * 16 * 2048 * 32 * (128 * 4 + 4)
-    # the split count is clamped to the number of key tiles
+    # the split count is clamped to the number of key tiles (decode tiles: 32 keys)
     p = g.gqa_attn_plan(1, 1, 100, 4, 4, 64, False, 0, 16, 256)
-    assert p["num_splits"] == 2 and p["key_tiles"] == 2
+    assert p["num_splits"] == 4 and p["key_tiles"] == 4
+    assert p["block_m"] == 32 and p["block_n"] == 32 and p["grid"] == 4 * 4
+    p = g.gqa_attn_plan(1, 40, 100, 4, 4, 64, False, 0, 16, 256)
+    assert p["num_splits"] == 2 and p["key_tiles"] == 2 and p["block_m"] == 128
+    # decode-shaped work (at most 32 query rows per head unit) uses 32 x 32 tiles
+    p = g.gqa_attn_plan(64, 1, 8192, 32, 8, 128, False, -1, 0, 256)
+    assert (p["block_m"], p["block_n"], p["key_tiles"], p["grid"]) == (32, 32, 256, 512)
+    p = g.gqa_attn_plan(2, 9, 300, 32, 8, 128, True, 1, 1, 256)
+    assert p["block_m"] == 128 and p["row_tiles"] == 1  # 36 packed rows
     # a single-head group never packs
     assert g.gqa_attn_plan(2, 300, 300, 4, 4, 64, False, 1, 1, 256)["pack_gqa"] == 0
 
@@ -175,7 +185,8 @@ int main() {
         Plan p;
         if (make_plan(s, pk, ns, 256, &p) != GQA_OK) { std::printf("plan failed\n"); return 1; }
         if (p.ns < 1 || p.ns > (p.key_tiles > 0 ? p.key_tiles : 1)) { std::printf("bad ns\n"); return 1; }
-        if ((long long)p.row_tiles * kBlockM < p.R || (long long)(p.row_tiles - 1) * kBlockM >= p.R) { std::printf("bad row tiles\n"); return 1; }
+        if ((long long)p.row_tiles * p.block_m < p.R || (long long)(p.row_tiles - 1) * p.block_m >= p.R) { std::printf("bad row tiles\n"); return 1; }
+        if (p.decode != (p.R <= kDecBlockM) || p.block_m != (p.decode ? kDecBlockM : kBlockM)) { std::printf("bad kernel choice\n"); return 1; }
         if (p.grid != (long long)B * p.units_per_b * p.row_tiles * p.ns) { std::printf("bad grid\n"); return 1; }
     }
     std::printf("ok %lld\n", checked);
