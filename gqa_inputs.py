@@ -140,3 +140,51 @@ def make_qkv_device(w: Workload, device, std: float = 1.0):
 def random_bf16(seed: int, shape: Sequence[int], std: float = 1.0) -> torch.Tensor:
     """One seeded bf16 tensor of any shape (edge-case tests)."""
     return _gen(seed, 0, 0, shape, std)
+
+
+@dataclass
+class PagedKV:
+    """A paged K/V cache: ``k_cache``/``v_cache`` [num_pages, page_size, Hk, d] bf16,
+    ``block_table`` [B, max_pages] int32, ``seqlens_k`` [B] int32 (CPU tensors)."""
+    k_cache: torch.Tensor
+    v_cache: torch.Tensor
+    block_table: torch.Tensor
+    seqlens_k: torch.Tensor
+
+    def to(self, device) -> "PagedKV":
+        return PagedKV(self.k_cache.to(device), self.v_cache.to(device), self.block_table.to(device),
+                       self.seqlens_k.to(device))
+
+
+def paged_kv(seed: int, seqlens: Sequence[int], page_size: int, Hk: int, d: int, spare_pages: int = 2,
+             max_pages: Optional[int] = None, fill: float = float("nan")) -> PagedKV:
+    """A seeded paged K/V cache holding sequences of the given key lengths.
+
+    Sequence b owns ceil(seqlens[b] / page_size) pages of the pool, handed out
+    in a seeded random order; key j of sequence b is row j % page_size of page
+    block_table[b, j // page_size]. Its keys and values are the draws of
+    batch_slice for batch element b (tensors 1 and 2, shape [seqlens[b], Hk, d]).
+    Page rows that hold no key (the tail of each last page and ``spare_pages``
+    unused pages) are set to ``fill`` and table entries past a sequence's last
+    page are -1, so a reader that touches anything else shows it.
+    """
+    lens = [int(n) for n in seqlens]
+    need = [-(-n // page_size) for n in lens]
+    mp = max(max(need) if need else 1, 1) if max_pages is None else int(max_pages)
+    num_pages = sum(need) + spare_pages
+    order = torch.randperm(max(num_pages, 1), generator=torch.Generator().manual_seed(seed * 7919 + 13))
+    k_cache = torch.full((max(num_pages, 1), page_size, Hk, d), fill, dtype=torch.bfloat16)
+    v_cache = torch.full_like(k_cache, fill)
+    table = torch.full((len(lens), mp), -1, dtype=torch.int32)
+    nxt = 0
+    for b, n in enumerate(lens):
+        kb = _gen(seed, TENSOR_K, b, (n, Hk, d))
+        vb = _gen(seed, TENSOR_V, b, (n, Hk, d))
+        for p in range(need[b]):
+            page = int(order[nxt])
+            nxt += 1
+            table[b, p] = page
+            rows = min(page_size, n - p * page_size)
+            k_cache[page, :rows] = kb[p * page_size:p * page_size + rows]
+            v_cache[page, :rows] = vb[p * page_size:p * page_size + rows]
+    return PagedKV(k_cache, v_cache, table, torch.tensor(lens, dtype=torch.int32))
