@@ -243,7 +243,26 @@ def main():
                 "kernel": "attn_decode_kernel" if pl["block_m"] == 32 else "attn_fwd_kernel"}
             print(f"[bench] decode pack={pack} ns={ns}: {msd*1e3:.1f} us", file=sys.stderr, flush=True)
         extra["decode_b64_sk8192"] = dec
-        del qd, kd, vd
+        del kd, vd
+        # the same decode over a paged cache: pages of 256 keys in random pool order
+        ps = 256
+        P = wd.Sk // ps
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(10)
+        kc = torch.randn((wd.B * P, ps, wd.Hk, wd.d), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        vc = torch.randn((wd.B * P, ps, wd.Hk, wd.d), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        table = torch.randperm(wd.B * P, generator=gen, device=dev).to(torch.int32).view(wd.B, P).contiguous()
+        lens = torch.full((wd.B,), wd.Sk, dtype=torch.int32, device=dev)
+        outp = torch.empty_like(qd)
+        lsep = torch.empty((wd.B, wd.Hq, wd.Sq), dtype=torch.float32, device=dev)
+        msp, _ = time_calls(lambda: g.gqa_attn_fwd_paged(qd, kc, vc, table, lens, outp, lsep, wd.causal, wd.scale),
+                            args.steps, 5)
+        extra["decode_paged_b64_sk8192_ps256"] = {
+            "us": round(msp * 1e3, 2), "GB_per_s": round(wd.io_bytes / (msp * 1e-3) / 1e9, 1),
+            "frac_hbm_peak": round(wd.io_bytes / (msp * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "kernel": "attn_decode_kernel (paged)"}
+        print(f"[bench] paged decode ps={ps}: {msp*1e3:.1f} us", file=sys.stderr, flush=True)
+        del qd, kc, vc, table, lens, outp, lsep
         torch.cuda.empty_cache()
         result["extra"] = extra
 

@@ -14,7 +14,8 @@ import math
 import os
 from typing import Optional, Tuple
 
-__all__ = ["GqaAttnError", "gqa_attn_fwd", "gqa_attn_func", "gqa_attn_choose", "gqa_attn_plan",
+__all__ = ["GqaAttnError", "gqa_attn_fwd", "gqa_attn_func", "gqa_attn_fwd_paged", "gqa_attn_func_paged",
+           "gqa_attn_choose", "gqa_attn_plan",
            "gqa_attn_strerror", "library_path", "load_library",
            "GQA_OK", "GQA_ERR_INVALID_ARG", "GQA_ERR_UNSUPPORTED", "GQA_ERR_NOMEM", "GQA_ERR_HIP"]
 
@@ -57,6 +58,8 @@ def load_library():
     c_int, c_float, vp = ctypes.c_int, ctypes.c_float, ctypes.c_void_p
     lib.gqa_attn_fwd.argtypes = [vp, vp, vp, vp, vp] + [c_int] * 7 + [c_float, c_int, c_int, vp]
     lib.gqa_attn_fwd.restype = c_int
+    lib.gqa_attn_fwd_paged.argtypes = [vp] * 7 + [c_int] * 8 + [c_int, c_float, c_int, c_int, vp]
+    lib.gqa_attn_fwd_paged.restype = c_int
     lib.gqa_attn_choose.argtypes = [c_int] * 8 + [ctypes.POINTER(c_int), ctypes.POINTER(c_int)]
     lib.gqa_attn_choose.restype = c_int
     lib.gqa_attn_plan.argtypes = [c_int] * 10 + [ctypes.POINTER(_Plan)]
@@ -137,4 +140,57 @@ def gqa_attn_func(q, k, v, causal: bool = False, softmax_scale: Optional[float] 
     out = torch.empty_like(q)
     lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device) if return_lse else None
     gqa_attn_fwd(q, k, v, out, lse, causal, softmax_scale, pack_gqa, num_splits)
+    return (out, lse) if return_lse else out
+
+
+def gqa_attn_fwd_paged(q, k_cache, v_cache, block_table, seqlens_k, out, lse, causal: bool, scale: float,
+                       pack_gqa: int = -1, num_splits: int = 0, stream=None) -> None:
+    """Run the forward pass over a paged KV cache into ``out`` (and ``lse`` or None).
+
+    q/out: [B, Sq, Hq, d] bf16; k_cache/v_cache: [num_pages, page_size, Hk, d] bf16;
+    block_table: [B, max_pages] int32; seqlens_k: [B] int32; lse: [B, Hq, Sq] fp32.
+    All contiguous on the same GPU.
+    """
+    import torch
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("out", out)):
+        if t.dtype != torch.bfloat16 or not t.is_contiguous() or t.dim() != 4 or not t.is_cuda:
+            raise ValueError(f"{name} must be a contiguous 4-d bfloat16 GPU tensor")
+    B, Sq, Hq, d = q.shape
+    num_pages, page_size, Hk, dk = k_cache.shape
+    if dk != d or tuple(v_cache.shape) != tuple(k_cache.shape) or tuple(out.shape) != tuple(q.shape):
+        raise ValueError("shape mismatch between q, k_cache, v_cache and out")
+    if (block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != B
+            or not block_table.is_contiguous() or not block_table.is_cuda):
+        raise ValueError("block_table must be a contiguous [B, max_pages] int32 GPU tensor")
+    if (seqlens_k.dtype != torch.int32 or tuple(seqlens_k.shape) != (B,) or not seqlens_k.is_contiguous()
+            or not seqlens_k.is_cuda):
+        raise ValueError("seqlens_k must be a contiguous [B] int32 GPU tensor")
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()
+                            or tuple(lse.shape) != (B, Hq, Sq) or not lse.is_cuda):
+        raise ValueError("lse must be a contiguous [B, Hq, Sq] float32 GPU tensor")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    elif hasattr(stream, "cuda_stream"):
+        stream = stream.cuda_stream
+    with torch.cuda.device(q.device):
+        st = load_library().gqa_attn_fwd_paged(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+                                               _ptr(seqlens_k), _ptr(out), _ptr(lse), B, Sq, Hq, Hk, d,
+                                               num_pages, page_size, block_table.shape[1], int(bool(causal)),
+                                               float(scale), int(pack_gqa), int(num_splits), stream)
+    if st != GQA_OK:
+        raise GqaAttnError(st)
+
+
+def gqa_attn_func_paged(q, k_cache, v_cache, block_table, seqlens_k, causal: bool = False,
+                        softmax_scale: Optional[float] = None, pack_gqa: int = -1, num_splits: int = 0,
+                        return_lse: bool = False):
+    """Allocate the outputs and run gqa_attn_fwd_paged. softmax_scale defaults to 1/sqrt(d)."""
+    import torch
+    B, Sq, Hq, d = q.shape
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d)
+    out = torch.empty_like(q)
+    lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device) if return_lse else None
+    gqa_attn_fwd_paged(q, k_cache, v_cache, block_table, seqlens_k, out, lse, causal, softmax_scale, pack_gqa,
+                       num_splits)
     return (out, lse) if return_lse else out

@@ -2,6 +2,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <climits>
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
@@ -106,6 +107,129 @@ int gqa_attn_plan(int B, int Sq, int Sk, int Hq, int Hk, int d, int causal, int 
     return GQA_OK;
 }
 
+}  // extern "C"
+
+namespace {
+
+// One forward call: contiguous K/V ([B, Sk, Hk, d]) or a paged pool.
+struct Call {
+    const void *q, *k, *v;
+    void* out;
+    float* lse;
+    gqa::Shape s;  // for paged calls, Sk = the table's capacity max_pages * page_size
+    float scale;
+    int pack_gqa, num_splits;
+    bool paged;
+    const int* block_table;
+    const int* seqlens_k;
+    int page_size, max_pages, num_pages;
+    hipStream_t stream;
+};
+
+int run(const Call& c) {
+    const gqa::Shape& s = c.s;
+    const int d = s.d;
+    const int dev = current_device();
+    if (dev < 0) return GQA_ERR_HIP;
+    int cus = 0;
+    if (c.pack_gqa < 0 || c.num_splits == 0) cus = device_cus(dev);
+    gqa::Plan plan;
+    int st = gqa::make_plan(s, c.pack_gqa, c.num_splits, cus, &plan);
+    if (st != GQA_OK) return st;
+    if (c.paged && !plan.decode) return GQA_ERR_UNSUPPORTED;
+
+    gqa::FwdParams p{};
+    p.q = (const uint16_t*)c.q;
+    p.k = (const uint16_t*)c.k;
+    p.v = (const uint16_t*)c.v;
+    p.o = (uint16_t*)c.out;
+    p.lse = c.lse;
+    p.B = s.B;
+    p.Sq = s.Sq;
+    p.Sk = s.Sk;
+    p.Hq = s.Hq;
+    p.Hk = s.Hk;
+    p.G = plan.G;
+    p.Gp = plan.Gp;
+    const gqa::FastDiv fd = gqa::make_fastdiv((uint32_t)plan.Gp);
+    p.gmul = fd.mul;
+    p.gshift = fd.shift;
+    p.R = (int)plan.R;
+    p.row_tiles = plan.row_tiles;
+    p.units_per_b = plan.units_per_b;
+    p.ns = plan.ns;
+    p.grid = (int)plan.grid;
+    // softmax(scale * s) = softmax(|scale| * (sign(scale) * s)): a negative
+    // scale negates Q (exact in bf16). scale == 0 gives every visible key
+    // the score 0, which the kernel reproduces exactly by reading Q as 0.
+    // A scale so small that |scale|*log2(e) is not a normal fp32 number
+    // also gives every visible key exactly the same weight in fp32.
+    const double cd = std::fabs((double)c.scale) * 1.4426950408889634;
+    const bool zero_scale = cd < 1.1754943508222875e-38;
+    p.c = zero_scale ? 1.0f : (float)cd;
+    p.qand = zero_scale ? 0u : 0xFFFFFFFFu;
+    p.qsign = c.scale < 0.f ? 0x80008000u : 0u;
+    if (c.paged) {
+        p.block_table = c.block_table;
+        p.seqlens_k = c.seqlens_k;
+        p.page_size = c.page_size;
+        p.max_pages = c.max_pages;
+        p.num_pages = c.num_pages;
+        const gqa::FastDiv pd = gqa::make_fastdiv((uint32_t)c.page_size);
+        p.pmul = pd.mul;
+        p.pshift = pd.shift;
+    }
+
+    if (log_enabled())
+        std::fprintf(stderr,
+                     "[gqa_attn] B=%d Sq=%d Sk=%d Hq=%d Hk=%d d=%d causal=%d paged=%d -> pack=%d ns=%d "
+                     "kernel=%s row_tiles=%d key_tiles=%d grid=%lld combine_grid=%lld ws=%lld\n",
+                     s.B, s.Sq, s.Sk, s.Hq, s.Hk, d, s.causal, c.paged ? 1 : 0, plan.pack, plan.ns,
+                     plan.decode ? "decode" : "tiled", plan.row_tiles, plan.key_tiles, plan.grid,
+                     plan.combine_grid, plan.workspace_bytes);
+
+    auto launch = [&](bool split) {
+        return plan.decode ? gqa::launch_decode(p, d, s.causal != 0, split, c.paged, c.stream)
+                           : gqa::launch_attention(p, d, s.causal != 0, split, c.stream);
+    };
+    if (plan.ns == 1) {
+        hipError_t e = launch(false);
+        return e == hipSuccess ? GQA_OK : GQA_ERR_HIP;
+    }
+
+    keep_pool(dev);
+    void* ws = nullptr;
+    if (hipMallocAsync(&ws, (size_t)plan.workspace_bytes, c.stream) != hipSuccess || !ws) {
+        (void)hipGetLastError();
+        return GQA_ERR_NOMEM;
+    }
+    const int64_t rows = (int64_t)s.B * s.Sq * s.Hq;
+    p.opart = (float*)ws;
+    p.lpart = (float*)ws + (int64_t)plan.ns * rows * d;
+    hipError_t e = launch(true);
+    if (e == hipSuccess) {
+        gqa::CombineParams cp{};
+        cp.opart = p.opart;
+        cp.lpart = p.lpart;
+        cp.o = (uint16_t*)c.out;
+        cp.lse = c.lse;
+        cp.rows = rows;
+        cp.ns = plan.ns;
+        cp.Sq = s.Sq;
+        cp.Hq = s.Hq;
+        e = gqa::launch_combine(cp, d, plan.combine_grid, c.stream);
+    }
+    const hipError_t ef = hipFreeAsync(ws, c.stream);
+    if (e != hipSuccess || ef != hipSuccess) return GQA_ERR_HIP;
+    return GQA_OK;
+}
+
+bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
+
+}  // namespace
+
+extern "C" {
+
 int gqa_attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Sq,
                  int Sk, int Hq, int Hk, int d, int causal, float scale, int pack_gqa, int num_splits,
                  hipStream_t stream) {
@@ -116,89 +240,39 @@ int gqa_attn_fwd(const void* q, const void* k, const void* v, void* out, float* 
         if ((long long)B * Sq == 0) return GQA_OK;
         if (!q || !k || !v || !out) return GQA_ERR_INVALID_ARG;
         if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return GQA_ERR_UNSUPPORTED;
+        Call c{q, k, v, out, lse, s, scale, pack_gqa, num_splits, false, nullptr, nullptr, 0, 0, 0, stream};
+        return run(c);
+    } catch (...) {
+        return GQA_ERR_HIP;
+    }
+}
 
-        const int dev = current_device();
-        if (dev < 0) return GQA_ERR_HIP;
-        int cus = 0;
-        if (pack_gqa < 0 || num_splits == 0) cus = device_cus(dev);
-        gqa::Plan plan;
-        st = gqa::make_plan(s, pack_gqa, num_splits, cus, &plan);
+int gqa_attn_fwd_paged(const void* q, const void* k_cache, const void* v_cache, const int* block_table,
+                       const int* seqlens_k, void* out, float* lse, int B, int Sq, int Hq, int Hk, int d,
+                       int num_pages, int page_size, int max_pages, int causal, float scale, int pack_gqa,
+                       int num_splits, hipStream_t stream) {
+    try {
+        if (page_size <= 0 || max_pages <= 0 || num_pages <= 0) return GQA_ERR_INVALID_ARG;
+        if ((long long)max_pages * page_size > INT_MAX / 2) return GQA_ERR_INVALID_ARG;
+        const gqa::Shape s{B, Sq, max_pages * page_size, Hq, Hk, d, causal ? 1 : 0};
+        int st = gqa::check_sizes(s, scale, pack_gqa, num_splits);
         if (st != GQA_OK) return st;
-
-        gqa::FwdParams p{};
-        p.q = (const uint16_t*)q;
-        p.k = (const uint16_t*)k;
-        p.v = (const uint16_t*)v;
-        p.o = (uint16_t*)out;
-        p.lse = lse;
-        p.B = B;
-        p.Sq = Sq;
-        p.Sk = Sk;
-        p.Hq = Hq;
-        p.Hk = Hk;
-        p.G = plan.G;
-        p.Gp = plan.Gp;
-        const gqa::FastDiv fd = gqa::make_fastdiv((uint32_t)plan.Gp);
-        p.gmul = fd.mul;
-        p.gshift = fd.shift;
-        p.R = (int)plan.R;
-        p.row_tiles = plan.row_tiles;
-        p.units_per_b = plan.units_per_b;
-        p.ns = plan.ns;
-        p.grid = (int)plan.grid;
-        // softmax(scale * s) = softmax(|scale| * (sign(scale) * s)): a negative
-        // scale negates Q (exact in bf16). scale == 0 gives every visible key
-        // the score 0, which the kernel reproduces exactly by reading Q as 0.
-        // A scale so small that |scale|*log2(e) is not a normal fp32 number
-        // also gives every visible key exactly the same weight in fp32.
-        const double cd = std::fabs((double)scale) * 1.4426950408889634;
-        const bool zero_scale = cd < 1.1754943508222875e-38;
-        p.c = zero_scale ? 1.0f : (float)cd;
-        p.qand = zero_scale ? 0u : 0xFFFFFFFFu;
-        p.qsign = scale < 0.f ? 0x80008000u : 0u;
-
-        if (log_enabled())
-            std::fprintf(stderr,
-                         "[gqa_attn] B=%d Sq=%d Sk=%d Hq=%d Hk=%d d=%d causal=%d -> pack=%d ns=%d "
-                         "kernel=%s row_tiles=%d key_tiles=%d grid=%lld combine_grid=%lld ws=%lld\n",
-                         B, Sq, Sk, Hq, Hk, d, s.causal, plan.pack, plan.ns, plan.decode ? "decode" : "tiled",
-                         plan.row_tiles, plan.key_tiles,
-                         plan.grid, plan.combine_grid, plan.workspace_bytes);
-
-        auto launch = [&](bool split) {
-            return plan.decode ? gqa::launch_decode(p, d, s.causal != 0, split, stream)
-                               : gqa::launch_attention(p, d, s.causal != 0, split, stream);
-        };
-        if (plan.ns == 1) {
-            hipError_t e = launch(false);
-            return e == hipSuccess ? GQA_OK : GQA_ERR_HIP;
+        if (page_size % 16 != 0) return GQA_ERR_UNSUPPORTED;
+        if ((long long)page_size * Hk * d * 2 > INT_MAX) return GQA_ERR_INVALID_ARG;  // 32-bit in-page offsets
+        {  // decode-shaped calls only (the pack decision does not depend on the CU count)
+            gqa::Plan probe;
+            st = gqa::make_plan(s, pack_gqa, num_splits, 256, &probe);
+            if (st != GQA_OK) return st;
+            if (!probe.decode) return GQA_ERR_UNSUPPORTED;
         }
-
-        keep_pool(dev);
-        void* ws = nullptr;
-        if (hipMallocAsync(&ws, (size_t)plan.workspace_bytes, stream) != hipSuccess || !ws) {
-            (void)hipGetLastError();
-            return GQA_ERR_NOMEM;
-        }
-        const int64_t rows = (int64_t)B * Sq * Hq;
-        p.opart = (float*)ws;
-        p.lpart = (float*)ws + (int64_t)plan.ns * rows * d;
-        hipError_t e = launch(true);
-        if (e == hipSuccess) {
-            gqa::CombineParams cp{};
-            cp.opart = p.opart;
-            cp.lpart = p.lpart;
-            cp.o = (uint16_t*)out;
-            cp.lse = lse;
-            cp.rows = rows;
-            cp.ns = plan.ns;
-            cp.Sq = Sq;
-            cp.Hq = Hq;
-            e = gqa::launch_combine(cp, d, plan.combine_grid, stream);
-        }
-        const hipError_t ef = hipFreeAsync(ws, stream);
-        if (e != hipSuccess || ef != hipSuccess) return GQA_ERR_HIP;
-        return GQA_OK;
+        if ((long long)B * Sq == 0) return GQA_OK;
+        if (!q || !k_cache || !v_cache || !block_table || !seqlens_k || !out) return GQA_ERR_INVALID_ARG;
+        if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
+            !aligned4(block_table) || !aligned4(seqlens_k))
+            return GQA_ERR_UNSUPPORTED;
+        Call c{q, k_cache, v_cache, out, lse, s, scale, pack_gqa, num_splits, true, block_table, seqlens_k,
+               page_size, max_pages, num_pages, stream};
+        return run(c);
     } catch (...) {
         return GQA_ERR_HIP;
     }

@@ -415,7 +415,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // independent workgroups per compute unit keep HBM busy. The arithmetic per
 // tile is the same as in the tiled kernel (transposed MFMA products, lazy
 // online softmax in base 2), on one block of 32 keys.
-template <int D, bool CAUSAL, bool SPLIT, int STAGES>
+//
+// PAGED: the keys of sequence b live in a pool of fixed-size pages (the
+// pages' paged KV cache for dynamic-length sequences, Stable-Diffusion GQA
+// guide, application scenario one): key j is row j % page_size of pool page
+// block_table[b][j / page_size], and sequence b has seqlens_k[b] keys
+// (causal alignment per sequence). page_size is a multiple of 16, so every
+// 16-key half of a tile lies in one page and each copy instruction (4 or 8
+// key rows) reads from one page. Lengths are clamped to the table's capacity
+// and page numbers to the pool, so no input makes a read leave the buffers.
+template <int D, bool CAUSAL, bool SPLIT, bool PAGED, int STAGES>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void attn_decode_kernel(const FwdParams p) {
     constexpr int BN = kDecBlockN;                 // keys per tile
     constexpr int TILE_B = BN * D * 2;             // bytes of one K or V tile
@@ -443,7 +452,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
     const int rc = min(r, p.R - 1);
     const int ti = (int)fdiv((uint32_t)rc, p.gmul, p.gshift);
     const int hh = h0 + (rc - ti * p.Gp);
-    const int koff = p.Sk - p.Sq;  // bottom-right causal offset
+    int Sk = p.Sk;  // keys of this sequence
+    if (PAGED) Sk = __builtin_amdgcn_readfirstlane(min(max(p.seqlens_k[b], 0), p.max_pages * p.page_size));
+    const int koff = Sk - p.Sq;  // bottom-right causal offset
 
     bf16x8 qreg[D / 16];
     {
@@ -457,8 +468,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
     }
 
     // ---- key tiles of this split. The unit's rows are tokens 0 .. Sq-1.
-    int kv_end = p.Sk;
-    if (CAUSAL) kv_end = min(p.Sk, p.Sq - 1 + koff + 1);
+    int kv_end = Sk;
+    if (CAUSAL) kv_end = min(Sk, p.Sq - 1 + koff + 1);
     const int T = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
     int t_begin = 0, t_end = T;
     if (SPLIT) {
@@ -469,8 +480,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
 
     // ---- tile copies: per-lane byte offsets inside a tile
     const int64_t kv_stride_b = (int64_t)p.Hk * D * 2;
-    const char* kbase = (const char*)(p.k + ((int64_t)b * p.Sk * p.Hk + g) * D);
-    const char* vbase = (const char*)(p.v + ((int64_t)b * p.Sk * p.Hk + g) * D);
+    // contiguous: this sequence's rows of head g; paged: head g of page 0
+    const int64_t seq_off = PAGED ? (int64_t)g * D : ((int64_t)b * p.Sk * p.Hk + g) * D;
+    const char* kbase = (const char*)(p.k + seq_off);
+    const char* vbase = (const char*)(p.v + seq_off);
     uint32_t goff[NLOAD];
 #pragma unroll
     for (int u = 0; u < NLOAD; ++u) {
@@ -482,9 +495,39 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
         const int kv0 = t * BN;
         LDS char* kt = lds + stage * 2 * TILE_B;
         LDS char* vt = kt + TILE_B;
+        if (PAGED) {
+            // each 16-key half: the page of its first key (or of the last key
+            // when the half lies past the end), rows clamped to the last key
+            constexpr int RPI = 64 / NCH;  // key rows per copy instruction
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                const int key_first = min(kv0 + 16 * hf, Sk - 1);
+                const int pidx = (int)fdiv((uint32_t)key_first, p.pmul, p.pshift);
+                // scalar load (constant address space): a vector load would make
+                // the compiler wait for every tile copy in flight before using it
+                const __attribute__((address_space(4))) int* table =
+                    (const __attribute__((address_space(4))) int*)p.block_table;
+                const int page = __builtin_amdgcn_readfirstlane(
+                    min(max(table[(int64_t)b * p.max_pages + pidx], 0), p.num_pages - 1));
+                const int pstart = pidx * p.page_size;
+                const int64_t page_off = (int64_t)page * p.page_size * kv_stride_b;
+                const char* kg = kbase + page_off;
+                const char* vg = vbase + page_off;
+#pragma unroll
+                for (int u = hf * (16 / RPI); u < (hf + 1) * (16 / RPI); ++u) {
+                    const int ci = u * 64 + lane;
+                    const int row = ci / NCH;
+                    const int key = min(kv0 + row, Sk - 1) - pstart;
+                    const uint32_t o = (uint32_t)(key * kv_stride_b + (((ci % NCH) ^ swz<D>(row)) * 16));
+                    lds_dma16(kg, o, kt + u * 1024);
+                    lds_dma16(vg, o, vt + u * 1024);
+                }
+            }
+            return;
+        }
         const char* kg = kbase + kv0 * kv_stride_b;
         const char* vg = vbase + kv0 * kv_stride_b;
-        if (kv0 + BN <= p.Sk) {
+        if (kv0 + BN <= Sk) {
 #pragma unroll
             for (int u = 0; u < NLOAD; ++u) {
                 lds_dma16(kg, goff[u], kt + u * 1024);
@@ -495,7 +538,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
             for (int u = 0; u < NLOAD; ++u) {
                 const int ci = u * 64 + lane;
                 const int row = ci / NCH;
-                const int key = min(kv0 + row, p.Sk - 1) - kv0;
+                const int key = min(kv0 + row, Sk - 1) - kv0;
                 const uint32_t o = (uint32_t)(key * kv_stride_b + (((ci % NCH) ^ swz<D>(row)) * 16));
                 lds_dma16(kg, o, kt + u * 1024);
                 lds_dma16(vg, o, vt + u * 1024);
@@ -526,7 +569,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
     float m_run = -__builtin_inff();
     float l_part[4] = {0.f, 0.f, 0.f, 0.f};
     const float c = p.c;
-    const int jlim = CAUSAL ? min(p.Sk - 1, ti + koff) : p.Sk - 1;
+    const int jlim = CAUSAL ? min(Sk - 1, ti + koff) : Sk - 1;
 
     auto compute = [&](int stage, int kv0) {
         const LDS char* kt = lds + stage * 2 * TILE_B;
@@ -538,7 +581,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
             sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[dc], sacc, 0, 0, 0);
         }
         // slot i of this lane holds key kv0 + 16*(i/8) + 8*half + (i%8)
-        if ((kv0 + BN > p.Sk) || (CAUSAL && kv0 + BN - 1 > koff)) {
+        if ((kv0 + BN > Sk) || (CAUSAL && kv0 + BN - 1 > koff)) {
             const int lim = jlim - kv0 - half * 8;
 #pragma unroll
             for (int i = 0; i < 16; ++i)
@@ -697,19 +740,23 @@ hipError_t launch_attention(const FwdParams& p, int d, bool causal, bool split, 
     return split ? launch_attn<64, false, true>(p, stream) : launch_attn<64, false, false>(p, stream);
 }
 
-template <int D, bool CAUSAL, bool SPLIT>
+template <int D, bool CAUSAL, bool SPLIT, bool PAGED>
 static hipError_t launch_dec(const FwdParams& p, hipStream_t stream) {
-    hipLaunchKernelGGL((attn_decode_kernel<D, CAUSAL, SPLIT, kDecStages>), dim3(p.grid), dim3(kDecThreads), 0, stream, p);
+    hipLaunchKernelGGL((attn_decode_kernel<D, CAUSAL, SPLIT, PAGED, kDecStages>), dim3(p.grid), dim3(kDecThreads), 0,
+                       stream, p);
     return hipGetLastError();
 }
 
-hipError_t launch_decode(const FwdParams& p, int d, bool causal, bool split, hipStream_t stream) {
-    if (d == 128) {
-        if (causal) return split ? launch_dec<128, true, true>(p, stream) : launch_dec<128, true, false>(p, stream);
-        return split ? launch_dec<128, false, true>(p, stream) : launch_dec<128, false, false>(p, stream);
-    }
-    if (causal) return split ? launch_dec<64, true, true>(p, stream) : launch_dec<64, true, false>(p, stream);
-    return split ? launch_dec<64, false, true>(p, stream) : launch_dec<64, false, false>(p, stream);
+template <int D, bool PAGED>
+static hipError_t launch_dec_d(const FwdParams& p, bool causal, bool split, hipStream_t stream) {
+    if (causal) return split ? launch_dec<D, true, true, PAGED>(p, stream) : launch_dec<D, true, false, PAGED>(p, stream);
+    return split ? launch_dec<D, false, true, PAGED>(p, stream) : launch_dec<D, false, false, PAGED>(p, stream);
+}
+
+hipError_t launch_decode(const FwdParams& p, int d, bool causal, bool split, bool paged, hipStream_t stream) {
+    if (d == 128)
+        return paged ? launch_dec_d<128, true>(p, causal, split, stream) : launch_dec_d<128, false>(p, causal, split, stream);
+    return paged ? launch_dec_d<64, true>(p, causal, split, stream) : launch_dec_d<64, false>(p, causal, split, stream);
 }
 
 hipError_t launch_combine(const CombineParams& p, int d, long long grid, hipStream_t stream) {

@@ -28,6 +28,12 @@ struct FwdParams {
     float c;            // |scale| * log2(e), or 1 when scale == 0
     uint32_t qand;      // 0 when scale == 0 (Q read as zeros: every visible score is 0), else all ones
     uint32_t qsign;     // 0x80008000 to negate Q (negative scale), else 0
+    // paged K/V (decode kernel only): k and v point at page pools
+    // [num_pages, page_size, Hk, D]; Sk is unused.
+    const int* block_table;  // [B, max_pages] pool page of each logical page
+    const int* seqlens_k;    // [B] keys of each sequence
+    int page_size, max_pages, num_pages;
+    uint32_t pmul, pshift;   // magic divisor of page_size
 };
 
 struct CombineParams {
@@ -40,7 +46,7 @@ struct CombineParams {
 };
 
 hipError_t launch_attention(const FwdParams& p, int d, bool causal, bool split, hipStream_t stream);
-hipError_t launch_decode(const FwdParams& p, int d, bool causal, bool split, hipStream_t stream);
+hipError_t launch_decode(const FwdParams& p, int d, bool causal, bool split, bool paged, hipStream_t stream);
 hipError_t launch_combine(const CombineParams& p, int d, long long grid, hipStream_t stream);
 
 }  // namespace gqa

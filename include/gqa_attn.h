@@ -57,8 +57,12 @@ typedef enum {
     GQA_OK = 0,
     GQA_ERR_INVALID_ARG = -1, /* null tensor pointer, negative size, Hq % Hk != 0,
                                  Sk == 0 while B*Sq > 0, pack_gqa not in {-1,0,1},
-                                 num_splits < 0, non-finite scale, size overflow */
-    GQA_ERR_UNSUPPORTED = -2, /* d not in {64,128}, pointer not 16-byte aligned */
+                                 num_splits < 0, non-finite scale, size overflow;
+                                 paged: page_size, max_pages or num_pages <= 0 */
+    GQA_ERR_UNSUPPORTED = -2, /* d not in {64,128}, pointer not 16-byte aligned;
+                                 paged: page_size % 16 != 0, more than 32 query
+                                 rows per head unit, table pointers not 4-byte
+                                 aligned */
     GQA_ERR_NOMEM = -3,       /* the split-KV workspace could not be allocated */
     GQA_ERR_HIP = -4          /* a HIP call or kernel launch failed */
 } gqa_status_t;
@@ -80,6 +84,43 @@ int gqa_attn_fwd(const void* q, const void* k, const void* v, void* out, float* 
                  int B, int Sq, int Sk, int Hq, int Hk, int d,
                  int causal, float scale, int pack_gqa, int num_splits,
                  hipStream_t stream);
+
+/* Forward pass over a paged KV cache, for decode-shaped calls.
+ *
+ * The pages serve dynamic-length sequences (and caches of sequences longer
+ * than 8192 tokens) with FlashAttention's paged KV cache (Stable-Diffusion
+ * GQA guide, application scenario one and the troubleshooting checklist);
+ * they fix no layout, so this one is the plainest reading:
+ *   k_cache, v_cache : [num_pages, page_size, Hk, d] bf16, a pool of pages
+ *   block_table      : [B, max_pages] int32, device memory. Entry (b, p) is
+ *                      the pool page holding keys p*page_size ..
+ *                      (p+1)*page_size - 1 of sequence b, so key j of
+ *                      sequence b is row j % page_size of page
+ *                      block_table[b][j / page_size].
+ *   seqlens_k        : [B] int32, device memory: the number of keys of
+ *                      sequence b (0 allowed: its rows get O = 0, LSE = -inf).
+ *   q, out, lse      : as for gqa_attn_fwd ([B, Sq, Hq, d], [B, Hq, Sq]).
+ * The result for sequence b is gqa_attn_fwd's over its seqlens_k[b] keys,
+ * with the causal alignment of that length (key j visible to query i iff
+ * j <= i + seqlens_k[b] - Sq). Table entries past a sequence's last page
+ * and page rows past its last key are never read.
+ *
+ * Limits: page_size a positive multiple of 16; a head unit may hold at most
+ * 32 query rows (G * Sq with PackGQA, Sq without: decode and a few
+ * speculative tokens), else GQA_ERR_UNSUPPORTED. num_splits and pack_gqa
+ * are resolved as for a contiguous call with Sk = max_pages * page_size.
+ * seqlens_k and block_table live on the device and are not validated on the
+ * host: the kernel clamps a length to [0, max_pages * page_size] and a page
+ * number to [0, num_pages - 1], so bad values give wrong results, never an
+ * out-of-bounds read. Pointers to the caches, q and out 16-byte aligned,
+ * block_table and seqlens_k 4-byte aligned. Ownership, errors, streams and
+ * the split workspace are as for gqa_attn_fwd. */
+int gqa_attn_fwd_paged(const void* q, const void* k_cache, const void* v_cache,
+                       const int* block_table, const int* seqlens_k, void* out, float* lse,
+                       int B, int Sq, int Hq, int Hk, int d,
+                       int num_pages, int page_size, int max_pages,
+                       int causal, float scale, int pack_gqa, int num_splits,
+                       hipStream_t stream);
 
 /* The host heuristic behind pack_gqa = -1 / num_splits = 0. It follows the
  * pages' rationale (rise-and-fall tuning article, "root cause" and "fix"

@@ -1,0 +1,114 @@
+"""Decode over a paged KV cache (gqa_attn_fwd_paged) against the paged fp64 oracle (GPU).
+
+The cache is a pool of pages handed out in a seeded random order; sequences
+have their own key lengths (empty ones included) and the unused page rows,
+unused pages and unused table entries hold NaN / -1, so any read outside the
+sequences shows up as a non-finite output. Cases: page sizes 16 to 256 around
+the 32-key tile, lengths around page and tile boundaries, causal and not, one
+and four new tokens, both head dimensions and several split counts; the
+paged path against the contiguous path (bitwise, same tile order); and the
+full-size decode workload on sampled sequences.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import gqa_inputs as gi
+import oracle
+from _parity import TOL_LSE, TOL_O_MAX, TOL_O_MEAN, f64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def run_paged(q, kv, causal, scale, pack=-1, ns=0):
+    import grouped_query_exact_amd as g
+    q = q.to(DEV)
+    kvd = kv.to(DEV)
+    B, Sq, Hq, d = q.shape
+    out = torch.empty_like(q)
+    lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=DEV)
+    g.gqa_attn_fwd_paged(q, kvd.k_cache, kvd.v_cache, kvd.block_table, kvd.seqlens_k, out, lse, causal, scale,
+                         pack, ns)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def compare_paged(O, L, q, kv, causal, scale, batches=None, tag=""):
+    bs = list(range(q.shape[0])) if batches is None else list(batches)
+    Or, Lr = oracle.attention_paged_fp64(f64(q), f64(kv.k_cache), f64(kv.v_cache), kv.block_table.numpy(),
+                                         kv.seqlens_k.numpy(), causal, scale, batches=bs)
+    Og = f64(O[bs])
+    assert np.isfinite(Og).all(), f"{tag}: non-finite output (a read outside the sequences?)"
+    dO = np.abs(Og - Or)
+    assert dO.max() <= TOL_O_MAX and dO.mean() <= TOL_O_MEAN, f"{tag}: max {dO.max()} mean {dO.mean()}"
+    Lg = f64(L[bs])
+    fin = np.isfinite(Lr)
+    assert np.array_equal(fin, np.isfinite(Lg)), f"{tag}: -inf pattern of LSE differs"
+    if fin.any():
+        assert np.abs(Lg[fin] - Lr[fin]).max() <= TOL_LSE, f"{tag}: LSE"
+
+
+LENGTHS = [0, 1, 15, 16, 17, 31, 32, 33, 100, 257, 1000]
+
+
+@pytest.mark.parametrize("page_size", [16, 32, 48, 64, 256])
+@pytest.mark.parametrize("d", [64, 128])
+def test_paged_decode_parity(page_size, d):
+    """Ragged and empty sequences, causal and not, 1 and 4 new tokens, ns 1 / 3 / 8."""
+    Hq, Hk = 8, 2
+    kv = gi.paged_kv(7000 + page_size + d, LENGTHS, page_size, Hk, d, spare_pages=3)
+    scale = gi.fp32(1 / math.sqrt(d))
+    for Sq in (1, 4):
+        q = gi.random_bf16(7100 + page_size + d + Sq, (len(LENGTHS), Sq, Hq, d))
+        for causal in (False, True):
+            for ns in (1, 3, 8):
+                O, L = run_paged(q, kv, causal, scale, 1, ns)
+                compare_paged(O, L, q, kv, causal, scale, tag=f"ps={page_size} d={d} Sq={Sq} causal={causal} ns={ns}")
+
+
+def test_paged_unpacked_and_auto():
+    """One head per workgroup (pack 0, 4 rows of one head) and the library's own choice."""
+    kv = gi.paged_kv(7200, [300, 64, 5], 64, 2, 128)
+    q = gi.random_bf16(7201, (3, 4, 8, 128))
+    for pack, ns in ((0, 1), (0, 2), (-1, 0)):
+        O, L = run_paged(q, kv, True, 0.0883883461356163, pack, ns)
+        compare_paged(O, L, q, kv, True, 0.0883883461356163, tag=f"pack={pack} ns={ns}")
+
+
+def test_paged_equals_contiguous_bitwise():
+    """Pages laid out in order (page b*P + p holds keys p*ps.. of sequence b) and equal lengths:
+    the paged kernel reads the same keys in the same tile order as the contiguous call."""
+    import grouped_query_exact_amd as g
+    B, Sk, Hq, Hk, d, ps = 4, 1000, 32, 8, 128, 64
+    P = -(-Sk // ps)
+    q, k, v = gi.random_bf16(7300, (B, 1, Hq, d)), gi.random_bf16(7301, (B, Sk, Hk, d)), gi.random_bf16(7302, (B, Sk, Hk, d))
+    kc = torch.zeros((B * P, ps, Hk, d), dtype=torch.bfloat16)
+    vc = torch.zeros_like(kc)
+    kc.view(B, P * ps, Hk, d)[:, :Sk] = k
+    vc.view(B, P * ps, Hk, d)[:, :Sk] = v
+    kv = gi.PagedKV(kc, vc, torch.arange(B * P, dtype=torch.int32).view(B, P), torch.full((B,), Sk, dtype=torch.int32))
+    for causal in (False, True):
+        for ns in (1, 4):
+            Op, Lp = run_paged(q, kv, causal, 0.0883883461356163, 1, ns)
+            out = torch.empty((B, 1, Hq, d), dtype=torch.bfloat16, device=DEV)
+            lse = torch.empty((B, Hq, 1), dtype=torch.float32, device=DEV)
+            g.gqa_attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), out, lse, causal, 0.0883883461356163, 1, ns)
+            torch.cuda.synchronize()
+            assert torch.equal(Op, out) and torch.equal(Lp, lse), f"causal={causal} ns={ns}"
+
+
+def test_paged_decode_full_size_sampled():
+    """The decode workload's shape (B=64, Hq=32, Hk=8, d=128) with sequence lengths up to 8192
+    in pages of 256 keys, library's choice of pack and splits; oracle on 6 sampled sequences."""
+    rs = np.random.RandomState(7400)
+    lens = [int(x) for x in rs.randint(1, 8193, size=64)]
+    lens[0], lens[1] = 8192, 1
+    kv = gi.paged_kv(7400, lens, 256, 8, 128, spare_pages=5)
+    q = gi.random_bf16(7401, (64, 1, 32, 128))
+    O, L = run_paged(q, kv, False, gi.fp32(1 / math.sqrt(128)))
+    assert torch.isfinite(O.float()).all()
+    compare_paged(O, L, q, kv, False, gi.fp32(1 / math.sqrt(128)), batches=[0, 1, 17, 33, 48, 63], tag="full size")

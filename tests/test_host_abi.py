@@ -33,7 +33,7 @@ def lib():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    assert names == ["gqa_attn_choose", "gqa_attn_fwd", "gqa_attn_plan", "gqa_attn_strerror"]
+    assert names == ["gqa_attn_choose", "gqa_attn_fwd", "gqa_attn_fwd_paged", "gqa_attn_plan", "gqa_attn_strerror"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -96,6 +96,56 @@ def test_misaligned_pointer_is_unsupported():
     st = L.gqa_attn_fwd(ctypes.c_void_p(4096 + 8), ctypes.c_void_p(4096), ctypes.c_void_p(4096),
                         ctypes.c_void_p(8192), None, 1, 4, 4, 2, 1, 64, 0, 0.125, 1, 1, None)
     assert st == g.GQA_ERR_UNSUPPORTED
+
+
+def _paged(q=1, kc=1, vc=1, bt=1, sl=1, out=1, lse=None, B=2, Sq=1, Hq=8, Hk=2, d=128, num_pages=10,
+           page_size=32, max_pages=4, causal=0, scale=0.125, pack=-1, ns=0):
+    """Call gqa_attn_fwd_paged with fake (never dereferenced) pointers; only invalid calls are allowed."""
+    L = lib()
+    P = lambda x: None if x is None else ctypes.c_void_p(x * 4096)
+    return L.gqa_attn_fwd_paged(P(q), P(kc), P(vc), P(bt), P(sl), P(out), P(lse), B, Sq, Hq, Hk, d,
+                                num_pages, page_size, max_pages, causal, scale, pack, ns, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(page_size=0), "INVALID_ARG"),
+    (dict(page_size=-16), "INVALID_ARG"),
+    (dict(max_pages=0), "INVALID_ARG"),
+    (dict(num_pages=0), "INVALID_ARG"),
+    (dict(max_pages=2 ** 30), "INVALID_ARG"),      # table capacity overflows int
+    (dict(bt=None), "INVALID_ARG"),
+    (dict(sl=None), "INVALID_ARG"),
+    (dict(kc=None), "INVALID_ARG"),
+    (dict(Hq=6, Hk=4), "INVALID_ARG"),
+    (dict(scale=float("nan")), "INVALID_ARG"),
+    (dict(page_size=24), "UNSUPPORTED"),            # not a multiple of 16
+    (dict(page_size=8), "UNSUPPORTED"),
+    (dict(d=96), "UNSUPPORTED"),
+    (dict(Sq=9, Hq=8, Hk=2), "UNSUPPORTED"),        # 36 packed rows: not decode-shaped
+    (dict(Sq=33, Hq=2, Hk=2), "UNSUPPORTED"),       # 33 rows of one head
+    (dict(Sq=9, pack=0), "OK_OR_DEVICE"),           # 9 unpacked rows per head: accepted up to the launch
+])
+def test_paged_argument_checks(kw, status):
+    import grouped_query_exact_amd as g
+    st = _paged(**kw)
+    if status == "OK_OR_DEVICE":
+        assert st in (g.GQA_OK, g.GQA_ERR_HIP)  # no GPU here: the first HIP call fails
+    else:
+        assert st == getattr(g, "GQA_ERR_" + status), (kw, st)
+
+
+def test_paged_misaligned_table_is_unsupported():
+    import grouped_query_exact_amd as g
+    L = lib()
+    st = L.gqa_attn_fwd_paged(ctypes.c_void_p(4096), ctypes.c_void_p(4096), ctypes.c_void_p(4096),
+                              ctypes.c_void_p(4096 + 2), ctypes.c_void_p(4096), ctypes.c_void_p(8192), None,
+                              2, 1, 8, 2, 128, 10, 32, 4, 0, 0.125, -1, 0, None)
+    assert st == g.GQA_ERR_UNSUPPORTED
+
+
+def test_paged_empty_problem_is_a_no_op():
+    import grouped_query_exact_amd as g
+    assert _paged(q=None, kc=None, vc=None, bt=None, sl=None, out=None, B=0) == g.GQA_OK
 
 
 def test_empty_problem_is_a_no_op():
