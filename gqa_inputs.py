@@ -188,3 +188,16 @@ def paged_kv(seed: int, seqlens: Sequence[int], page_size: int, Hk: int, d: int,
             k_cache[page, :rows] = kb[p * page_size:p * page_size + rows]
             v_cache[page, :rows] = vb[p * page_size:p * page_size + rows]
     return PagedKV(k_cache, v_cache, table, torch.tensor(lens, dtype=torch.int32))
+
+
+def random_fp8(seed: int, shape: Sequence[int], std: float = 1.0) -> torch.Tensor:
+    """Seeded fp8 e4m3 bytes (uint8): N(0, std^2) draws rounded to float8_e4m3fn."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed * 1_000_003 + 17)
+    x = torch.randn(list(shape), generator=g, dtype=torch.float32) * std
+    return x.to(torch.float8_e4m3fn).view(torch.uint8)
+
+
+def to_fp8_bytes(x: torch.Tensor) -> torch.Tensor:
+    """Round a tensor to float8_e4m3fn and return its bytes (uint8), e.g. a paged pool (NaN stays NaN)."""
+    return x.to(torch.float32).to(torch.float8_e4m3fn).view(torch.uint8)
