@@ -262,7 +262,19 @@ def main():
             "frac_hbm_peak": round(wd.io_bytes / (msp * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
             "kernel": "attn_decode_kernel (paged)"}
         print(f"[bench] paged decode ps={ps}: {msp*1e3:.1f} us", file=sys.stderr, flush=True)
-        del qd, kc, vc, table, lens, outp, lsep
+        del kc, vc, table, lens
+        # the same decode with fp8 e4m3 K/V (half the K/V bytes)
+        k8 = torch.randn((wd.B, wd.Sk, wd.Hk, wd.d), generator=gen, device=dev).to(torch.float8_e4m3fn).view(torch.uint8)
+        v8 = torch.randn((wd.B, wd.Sk, wd.Hk, wd.d), generator=gen, device=dev).to(torch.float8_e4m3fn).view(torch.uint8)
+        ms8, _ = time_calls(lambda: g.gqa_attn_fwd_kv8(qd, k8, v8, 1.0, 1.0, outp, lsep, wd.causal, wd.scale),
+                            args.steps, 5)
+        bytes8 = wd.io_bytes - (k8.numel() + v8.numel())  # K and V at one byte per element
+        extra["decode_kv8_b64_sk8192"] = {
+            "us": round(ms8 * 1e3, 2), "GB_per_s": round(bytes8 / (ms8 * 1e-3) / 1e9, 1),
+            "frac_hbm_peak": round(bytes8 / (ms8 * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "algorithmic_bytes": bytes8, "kernel": "attn_decode_kernel (fp8 K/V)"}
+        print(f"[bench] fp8 decode: {ms8*1e3:.1f} us", file=sys.stderr, flush=True)
+        del qd, k8, v8, outp, lsep
         torch.cuda.empty_cache()
         result["extra"] = extra
 

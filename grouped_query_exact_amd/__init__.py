@@ -15,6 +15,7 @@ import os
 from typing import Optional, Tuple
 
 __all__ = ["GqaAttnError", "gqa_attn_fwd", "gqa_attn_func", "gqa_attn_fwd_paged", "gqa_attn_func_paged",
+           "gqa_attn_fwd_kv8", "gqa_attn_fwd_paged_kv8",
            "gqa_attn_choose", "gqa_attn_plan",
            "gqa_attn_strerror", "library_path", "load_library",
            "GQA_OK", "GQA_ERR_INVALID_ARG", "GQA_ERR_UNSUPPORTED", "GQA_ERR_NOMEM", "GQA_ERR_HIP"]
@@ -60,6 +61,11 @@ def load_library():
     lib.gqa_attn_fwd.restype = c_int
     lib.gqa_attn_fwd_paged.argtypes = [vp] * 7 + [c_int] * 8 + [c_int, c_float, c_int, c_int, vp]
     lib.gqa_attn_fwd_paged.restype = c_int
+    lib.gqa_attn_fwd_kv8.argtypes = [vp] * 3 + [c_float, c_float] + [vp, vp] + [c_int] * 7 + [c_float, c_int, c_int, vp]
+    lib.gqa_attn_fwd_kv8.restype = c_int
+    lib.gqa_attn_fwd_paged_kv8.argtypes = [vp] * 3 + [c_float, c_float] + [vp] * 4 + [c_int] * 8 + \
+        [c_int, c_float, c_int, c_int, vp]
+    lib.gqa_attn_fwd_paged_kv8.restype = c_int
     lib.gqa_attn_choose.argtypes = [c_int] * 8 + [ctypes.POINTER(c_int), ctypes.POINTER(c_int)]
     lib.gqa_attn_choose.restype = c_int
     lib.gqa_attn_plan.argtypes = [c_int] * 10 + [ctypes.POINTER(_Plan)]
@@ -143,22 +149,52 @@ def gqa_attn_func(q, k, v, causal: bool = False, softmax_scale: Optional[float] 
     return (out, lse) if return_lse else out
 
 
-def gqa_attn_fwd_paged(q, k_cache, v_cache, block_table, seqlens_k, out, lse, causal: bool, scale: float,
-                       pack_gqa: int = -1, num_splits: int = 0, stream=None) -> None:
-    """Run the forward pass over a paged KV cache into ``out`` (and ``lse`` or None).
-
-    q/out: [B, Sq, Hq, d] bf16; k_cache/v_cache: [num_pages, page_size, Hk, d] bf16;
-    block_table: [B, max_pages] int32; seqlens_k: [B] int32; lse: [B, Hq, Sq] fp32.
-    All contiguous on the same GPU.
-    """
+def _check_kv8(**tensors):
     import torch
-    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("out", out)):
+    for name, t in tensors.items():
+        if t.dtype not in (torch.uint8, torch.float8_e4m3fn) or not t.is_contiguous() or t.dim() != 4 or not t.is_cuda:
+            raise ValueError(f"{name} must be a contiguous 4-d GPU tensor of float8_e4m3fn (or uint8) bytes")
+
+
+def _check_bf16(**tensors):
+    import torch
+    for name, t in tensors.items():
         if t.dtype != torch.bfloat16 or not t.is_contiguous() or t.dim() != 4 or not t.is_cuda:
             raise ValueError(f"{name} must be a contiguous 4-d bfloat16 GPU tensor")
+
+
+def gqa_attn_fwd_kv8(q, k, v, k_scale: float, v_scale: float, out, lse, causal: bool, scale: float,
+                     pack_gqa: int = -1, num_splits: int = 0, stream=None) -> None:
+    """Forward pass with fp8 e4m3 K/V ([B, Sk, Hk, d] bytes) and per-tensor factors, into ``out``/``lse``."""
+    import torch
+    _check_bf16(q=q, out=out)
+    _check_kv8(k=k, v=v)
     B, Sq, Hq, d = q.shape
-    num_pages, page_size, Hk, dk = k_cache.shape
-    if dk != d or tuple(v_cache.shape) != tuple(k_cache.shape) or tuple(out.shape) != tuple(q.shape):
-        raise ValueError("shape mismatch between q, k_cache, v_cache and out")
+    _, Sk, Hk, _ = k.shape
+    if tuple(k.shape) != (B, Sk, Hk, d) or tuple(v.shape) != tuple(k.shape) or tuple(out.shape) != tuple(q.shape):
+        raise ValueError("shape mismatch between q, k, v and out")
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()
+                            or tuple(lse.shape) != (B, Hq, Sq) or not lse.is_cuda):
+        raise ValueError("lse must be a contiguous [B, Hq, Sq] float32 GPU tensor")
+    stream = _stream(q, stream)
+    with torch.cuda.device(q.device):
+        st = load_library().gqa_attn_fwd_kv8(_ptr(q), _ptr(k), _ptr(v), float(k_scale), float(v_scale), _ptr(out),
+                                             _ptr(lse), B, Sq, Sk, Hq, Hk, d, int(bool(causal)), float(scale),
+                                             int(pack_gqa), int(num_splits), stream)
+    if st != GQA_OK:
+        raise GqaAttnError(st)
+
+
+def _stream(q, stream):
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream(q.device).cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+
+
+def _check_paged(q, k_cache, block_table, seqlens_k, lse):
+    import torch
+    B, Sq, Hq, d = q.shape
     if (block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != B
             or not block_table.is_contiguous() or not block_table.is_cuda):
         raise ValueError("block_table must be a contiguous [B, max_pages] int32 GPU tensor")
@@ -168,10 +204,46 @@ def gqa_attn_fwd_paged(q, k_cache, v_cache, block_table, seqlens_k, out, lse, ca
     if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()
                             or tuple(lse.shape) != (B, Hq, Sq) or not lse.is_cuda):
         raise ValueError("lse must be a contiguous [B, Hq, Sq] float32 GPU tensor")
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device).cuda_stream
-    elif hasattr(stream, "cuda_stream"):
-        stream = stream.cuda_stream
+
+
+def gqa_attn_fwd_paged_kv8(q, k_cache, v_cache, k_scale: float, v_scale: float, block_table, seqlens_k, out, lse,
+                           causal: bool, scale: float, pack_gqa: int = -1, num_splits: int = 0, stream=None) -> None:
+    """gqa_attn_fwd_paged over fp8 e4m3 page pools with per-tensor factors."""
+    import torch
+    _check_bf16(q=q, out=out)
+    _check_kv8(k_cache=k_cache, v_cache=v_cache)
+    B, Sq, Hq, d = q.shape
+    num_pages, page_size, Hk, dk = k_cache.shape
+    if dk != d or tuple(v_cache.shape) != tuple(k_cache.shape) or tuple(out.shape) != tuple(q.shape):
+        raise ValueError("shape mismatch between q, k_cache, v_cache and out")
+    _check_paged(q, k_cache, block_table, seqlens_k, lse)
+    stream = _stream(q, stream)
+    with torch.cuda.device(q.device):
+        st = load_library().gqa_attn_fwd_paged_kv8(_ptr(q), _ptr(k_cache), _ptr(v_cache), float(k_scale),
+                                                   float(v_scale), _ptr(block_table), _ptr(seqlens_k), _ptr(out),
+                                                   _ptr(lse), B, Sq, Hq, Hk, d, num_pages, page_size,
+                                                   block_table.shape[1], int(bool(causal)), float(scale),
+                                                   int(pack_gqa), int(num_splits), stream)
+    if st != GQA_OK:
+        raise GqaAttnError(st)
+
+
+def gqa_attn_fwd_paged(q, k_cache, v_cache, block_table, seqlens_k, out, lse, causal: bool, scale: float,
+                       pack_gqa: int = -1, num_splits: int = 0, stream=None) -> None:
+    """Run the forward pass over a paged KV cache into ``out`` (and ``lse`` or None).
+
+    q/out: [B, Sq, Hq, d] bf16; k_cache/v_cache: [num_pages, page_size, Hk, d] bf16;
+    block_table: [B, max_pages] int32; seqlens_k: [B] int32; lse: [B, Hq, Sq] fp32.
+    All contiguous on the same GPU.
+    """
+    import torch
+    _check_bf16(q=q, k_cache=k_cache, v_cache=v_cache, out=out)
+    B, Sq, Hq, d = q.shape
+    num_pages, page_size, Hk, dk = k_cache.shape
+    if dk != d or tuple(v_cache.shape) != tuple(k_cache.shape) or tuple(out.shape) != tuple(q.shape):
+        raise ValueError("shape mismatch between q, k_cache, v_cache and out")
+    _check_paged(q, k_cache, block_table, seqlens_k, lse)
+    stream = _stream(q, stream)
     with torch.cuda.device(q.device):
         st = load_library().gqa_attn_fwd_paged(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
                                                _ptr(seqlens_k), _ptr(out), _ptr(lse), B, Sq, Hq, Hk, d,

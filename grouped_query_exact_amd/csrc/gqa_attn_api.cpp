@@ -124,6 +124,8 @@ struct Call {
     const int* seqlens_k;
     int page_size, max_pages, num_pages;
     hipStream_t stream;
+    bool kv8 = false;       // fp8 e4m3 K/V with per-tensor factors
+    float k_scale = 1.f, v_scale = 1.f;
 };
 
 int run(const Call& c) {
@@ -136,7 +138,7 @@ int run(const Call& c) {
     gqa::Plan plan;
     int st = gqa::make_plan(s, c.pack_gqa, c.num_splits, cus, &plan);
     if (st != GQA_OK) return st;
-    if (c.paged && !plan.decode) return GQA_ERR_UNSUPPORTED;
+    if ((c.paged || c.kv8) && !plan.decode) return GQA_ERR_UNSUPPORTED;
 
     gqa::FwdParams p{};
     p.q = (const uint16_t*)c.q;
@@ -164,11 +166,14 @@ int run(const Call& c) {
     // the score 0, which the kernel reproduces exactly by reading Q as 0.
     // A scale so small that |scale|*log2(e) is not a normal fp32 number
     // also gives every visible key exactly the same weight in fp32.
-    const double cd = std::fabs((double)c.scale) * 1.4426950408889634;
+    // fp8 K/V: the scores are (scale * k_scale) * q.k8, the output v_scale * P.v8.
+    const double score_scale = c.kv8 ? (double)c.scale * (double)c.k_scale : (double)c.scale;
+    const double cd = std::fabs(score_scale) * 1.4426950408889634;
     const bool zero_scale = cd < 1.1754943508222875e-38;
     p.c = zero_scale ? 1.0f : (float)cd;
     p.qand = zero_scale ? 0u : 0xFFFFFFFFu;
-    p.qsign = c.scale < 0.f ? 0x80008000u : 0u;
+    p.qsign = score_scale < 0.0 ? 0x80008000u : 0u;
+    p.vscale = c.kv8 ? c.v_scale : 1.f;
     if (c.paged) {
         p.block_table = c.block_table;
         p.seqlens_k = c.seqlens_k;
@@ -182,14 +187,14 @@ int run(const Call& c) {
 
     if (log_enabled())
         std::fprintf(stderr,
-                     "[gqa_attn] B=%d Sq=%d Sk=%d Hq=%d Hk=%d d=%d causal=%d paged=%d -> pack=%d ns=%d "
+                     "[gqa_attn] B=%d Sq=%d Sk=%d Hq=%d Hk=%d d=%d causal=%d paged=%d kv8=%d -> pack=%d ns=%d "
                      "kernel=%s row_tiles=%d key_tiles=%d grid=%lld combine_grid=%lld ws=%lld\n",
-                     s.B, s.Sq, s.Sk, s.Hq, s.Hk, d, s.causal, c.paged ? 1 : 0, plan.pack, plan.ns,
+                     s.B, s.Sq, s.Sk, s.Hq, s.Hk, d, s.causal, c.paged ? 1 : 0, c.kv8 ? 1 : 0, plan.pack, plan.ns,
                      plan.decode ? "decode" : "tiled", plan.row_tiles, plan.key_tiles, plan.grid,
                      plan.combine_grid, plan.workspace_bytes);
 
     auto launch = [&](bool split) {
-        return plan.decode ? gqa::launch_decode(p, d, s.causal != 0, split, c.paged, c.stream)
+        return plan.decode ? gqa::launch_decode(p, d, s.causal != 0, split, c.paged, c.kv8, c.stream)
                            : gqa::launch_attention(p, d, s.causal != 0, split, c.stream);
     };
     if (plan.ns == 1) {
@@ -247,18 +252,19 @@ int gqa_attn_fwd(const void* q, const void* k, const void* v, void* out, float* 
     }
 }
 
-int gqa_attn_fwd_paged(const void* q, const void* k_cache, const void* v_cache, const int* block_table,
-                       const int* seqlens_k, void* out, float* lse, int B, int Sq, int Hq, int Hk, int d,
-                       int num_pages, int page_size, int max_pages, int causal, float scale, int pack_gqa,
-                       int num_splits, hipStream_t stream) {
+static int fwd_paged(const void* q, const void* k_cache, const void* v_cache, const int* block_table,
+                     const int* seqlens_k, void* out, float* lse, int B, int Sq, int Hq, int Hk, int d,
+                     int num_pages, int page_size, int max_pages, int causal, float scale, int pack_gqa,
+                     int num_splits, hipStream_t stream, bool kv8, float k_scale, float v_scale) {
     try {
         if (page_size <= 0 || max_pages <= 0 || num_pages <= 0) return GQA_ERR_INVALID_ARG;
         if ((long long)max_pages * page_size > INT_MAX / 2) return GQA_ERR_INVALID_ARG;
-        const gqa::Shape s{B, Sq, max_pages * page_size, Hq, Hk, d, causal ? 1 : 0};
+        if (kv8 && (!std::isfinite(k_scale) || !std::isfinite(v_scale))) return GQA_ERR_INVALID_ARG;
+        const gqa::Shape s{B, Sq, max_pages * page_size, Hq, Hk, d, causal ? 1 : 0, kv8 ? 1 : 2};
         int st = gqa::check_sizes(s, scale, pack_gqa, num_splits);
         if (st != GQA_OK) return st;
         if (page_size % 16 != 0) return GQA_ERR_UNSUPPORTED;
-        if ((long long)page_size * Hk * d * 2 > INT_MAX) return GQA_ERR_INVALID_ARG;  // 32-bit in-page offsets
+        if ((long long)page_size * Hk * d * (kv8 ? 1 : 2) > INT_MAX) return GQA_ERR_INVALID_ARG;  // 32-bit in-page offsets
         {  // decode-shaped calls only (the pack decision does not depend on the CU count)
             gqa::Plan probe;
             st = gqa::make_plan(s, pack_gqa, num_splits, 256, &probe);
@@ -271,11 +277,52 @@ int gqa_attn_fwd_paged(const void* q, const void* k_cache, const void* v_cache, 
             !aligned4(block_table) || !aligned4(seqlens_k))
             return GQA_ERR_UNSUPPORTED;
         Call c{q, k_cache, v_cache, out, lse, s, scale, pack_gqa, num_splits, true, block_table, seqlens_k,
-               page_size, max_pages, num_pages, stream};
+               page_size, max_pages, num_pages, stream, kv8, k_scale, v_scale};
         return run(c);
     } catch (...) {
         return GQA_ERR_HIP;
     }
+}
+
+int gqa_attn_fwd_paged(const void* q, const void* k_cache, const void* v_cache, const int* block_table,
+                       const int* seqlens_k, void* out, float* lse, int B, int Sq, int Hq, int Hk, int d,
+                       int num_pages, int page_size, int max_pages, int causal, float scale, int pack_gqa,
+                       int num_splits, hipStream_t stream) {
+    return fwd_paged(q, k_cache, v_cache, block_table, seqlens_k, out, lse, B, Sq, Hq, Hk, d, num_pages, page_size,
+                     max_pages, causal, scale, pack_gqa, num_splits, stream, false, 1.f, 1.f);
+}
+
+int gqa_attn_fwd_kv8(const void* q, const void* k, const void* v, float k_scale, float v_scale, void* out,
+                     float* lse, int B, int Sq, int Sk, int Hq, int Hk, int d, int causal, float scale,
+                     int pack_gqa, int num_splits, hipStream_t stream) {
+    try {
+        if (!std::isfinite(k_scale) || !std::isfinite(v_scale)) return GQA_ERR_INVALID_ARG;
+        const gqa::Shape s{B, Sq, Sk, Hq, Hk, d, causal ? 1 : 0, 1};
+        int st = gqa::check_sizes(s, scale, pack_gqa, num_splits);
+        if (st != GQA_OK) return st;
+        {
+            gqa::Plan probe;
+            st = gqa::make_plan(s, pack_gqa, num_splits, 256, &probe);
+            if (st != GQA_OK) return st;
+            if (!probe.decode) return GQA_ERR_UNSUPPORTED;
+        }
+        if ((long long)B * Sq == 0) return GQA_OK;
+        if (!q || !k || !v || !out) return GQA_ERR_INVALID_ARG;
+        if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return GQA_ERR_UNSUPPORTED;
+        Call c{q, k, v, out, lse, s, scale, pack_gqa, num_splits, false, nullptr, nullptr, 0, 0, 0, stream,
+               true, k_scale, v_scale};
+        return run(c);
+    } catch (...) {
+        return GQA_ERR_HIP;
+    }
+}
+
+int gqa_attn_fwd_paged_kv8(const void* q, const void* k_cache, const void* v_cache, float k_scale, float v_scale,
+                           const int* block_table, const int* seqlens_k, void* out, float* lse, int B, int Sq,
+                           int Hq, int Hk, int d, int num_pages, int page_size, int max_pages, int causal,
+                           float scale, int pack_gqa, int num_splits, hipStream_t stream) {
+    return fwd_paged(q, k_cache, v_cache, block_table, seqlens_k, out, lse, B, Sq, Hq, Hk, d, num_pages, page_size,
+                     max_pages, causal, scale, pack_gqa, num_splits, stream, true, k_scale, v_scale);
 }
 
 }  // extern "C"

@@ -424,15 +424,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // 16-key half of a tile lies in one page and each copy instruction (4 or 8
 // key rows) reads from one page. Lengths are clamped to the table's capacity
 // and page numbers to the pool, so no input makes a read leave the buffers.
-template <int D, bool CAUSAL, bool SPLIT, bool PAGED, int STAGES>
+//
+// KV8: K and V are stored as fp8 e4m3 (the pages' FP8 e4m3 to halve the
+// bandwidth pressure, rise-and-fall tuning article, "verification and
+// further directions") with per-tensor factors: the scores use
+// scale * k_scale, the output is multiplied by v_scale. The ring holds the
+// raw fp8 tiles (half the bytes per key); before a tile is used, the wave
+// converts it into a bf16 staging tile laid out exactly like a bf16 ring
+// tile, so the products are the same as for bf16 K/V holding the fp8 values
+// (every e4m3 value is exact in bf16).
+template <int D, bool CAUSAL, bool SPLIT, bool PAGED, bool KV8, int STAGES>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void attn_decode_kernel(const FwdParams p) {
     constexpr int BN = kDecBlockN;                 // keys per tile
-    constexpr int TILE_B = BN * D * 2;             // bytes of one K or V tile
-    constexpr int NCH = D / 8;                     // 16-byte chunks per row
+    constexpr int EB = KV8 ? 1 : 2;                // bytes per stored K/V element
+    constexpr int TILE_B = BN * D * EB;            // ring bytes of one K or V tile
+    constexpr int NCH = D * EB / 16;               // 16-byte chunks per stored row
     constexpr int NLOAD = BN * NCH / 64;           // 16-byte copies per lane per tensor and tile
+    constexpr int BF_TILE = BN * D * 2;            // bytes of a bf16 tile
+    constexpr int RING_B = STAGES * 2 * TILE_B;
+    constexpr int SMEM_B = RING_B + (KV8 ? 2 * BF_TILE : 0);
     static_assert(BN == 32, "one 32-key MFMA block per tile");
-    __shared__ __attribute__((aligned(16))) uint16_t smem[STAGES * 2 * BN * D];
-    LDS char* lds = (LDS char*)smem;               // stage s: K tile, then V tile
+    __shared__ u32x4 smem[SMEM_B / 16];
+    LDS char* lds = (LDS char*)smem;               // ring stage s: K tile, then V tile; then (KV8) bf16 K, V
 
     const int lane = threadIdx.x;
     const int col = lane & 31, half = lane >> 5;
@@ -478,18 +491,20 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
     }
     const int n = t_end - t_begin;
 
-    // ---- tile copies: per-lane byte offsets inside a tile
-    const int64_t kv_stride_b = (int64_t)p.Hk * D * 2;
+    // ---- tile copies: per-lane byte offsets inside a tile. bf16 tiles are
+    // stored swizzled (chunk c of row r at c ^ swz(r)); fp8 tiles in order.
+    const int64_t kv_stride_b = (int64_t)p.Hk * D * EB;
     // contiguous: this sequence's rows of head g; paged: head g of page 0
     const int64_t seq_off = PAGED ? (int64_t)g * D : ((int64_t)b * p.Sk * p.Hk + g) * D;
-    const char* kbase = (const char*)(p.k + seq_off);
-    const char* vbase = (const char*)(p.v + seq_off);
+    const char* kbase = (const char*)p.k + seq_off * EB;
+    const char* vbase = (const char*)p.v + seq_off * EB;
+    auto ring_chunk = [&](int ci, int row) { return KV8 ? (ci % NCH) : ((ci % NCH) ^ swz<D>(row)); };
     uint32_t goff[NLOAD];
 #pragma unroll
     for (int u = 0; u < NLOAD; ++u) {
         const int ci = u * 64 + lane;
         const int row = ci / NCH;
-        goff[u] = (uint32_t)(row * kv_stride_b + (((ci % NCH) ^ swz<D>(row)) * 16));
+        goff[u] = (uint32_t)(row * kv_stride_b + ring_chunk(ci, row) * 16);
     }
     auto issue = [&](int t, int stage) {
         const int kv0 = t * BN;
@@ -518,7 +533,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
                     const int ci = u * 64 + lane;
                     const int row = ci / NCH;
                     const int key = min(kv0 + row, Sk - 1) - pstart;
-                    const uint32_t o = (uint32_t)(key * kv_stride_b + (((ci % NCH) ^ swz<D>(row)) * 16));
+                    const uint32_t o = (uint32_t)(key * kv_stride_b + ring_chunk(ci, row) * 16);
                     lds_dma16(kg, o, kt + u * 1024);
                     lds_dma16(vg, o, vt + u * 1024);
                 }
@@ -539,11 +554,38 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
                 const int ci = u * 64 + lane;
                 const int row = ci / NCH;
                 const int key = min(kv0 + row, Sk - 1) - kv0;
-                const uint32_t o = (uint32_t)(key * kv_stride_b + (((ci % NCH) ^ swz<D>(row)) * 16));
+                const uint32_t o = (uint32_t)(key * kv_stride_b + ring_chunk(ci, row) * 16);
                 lds_dma16(kg, o, kt + u * 1024);
                 lds_dma16(vg, o, vt + u * 1024);
             }
         }
+    };
+
+    // fp8 ring tile -> bf16 staging tile (swizzled like a bf16 ring tile):
+    // each lane converts 16-byte fp8 chunks (16 keys' worth of one row) into
+    // two 16-byte bf16 chunks. The wave's LDS operations run in order, so
+    // the reads that follow see these writes.
+    auto convert = [&](const LDS char* src, LDS char* dst) {
+        constexpr int C8 = D / 16;  // fp8 chunks per row
+#pragma unroll
+        for (int u = 0; u < BN * C8 / 64; ++u) {
+            const int ci = u * 64 + lane;
+            const int row = ci / C8, c8 = ci % C8;
+            const u32x4 w = *(const LDS u32x4*)(src + ci * 16);
+            u32x4 lo, hi;
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                lo[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, false));
+                lo[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, true));
+                hi[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[2 + i], 1.0f, false));
+                hi[2 * i + 1] =
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[2 + i], 1.0f, true));
+            }
+            LDS char* drow = dst + row * (D * 2);
+            *(LDS u32x4*)(drow + (((2 * c8) ^ swz<D>(row)) * 16)) = lo;
+            *(LDS u32x4*)(drow + (((2 * c8 + 1) ^ swz<D>(row)) * 16)) = hi;
+        }
+        asm volatile("" ::: "memory");
     };
 
     // ---- per-lane LDS operand offsets (as in the tiled kernel, one key block)
@@ -574,6 +616,14 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
     auto compute = [&](int stage, int kv0) {
         const LDS char* kt = lds + stage * 2 * TILE_B;
         const LDS char* vt = kt + TILE_B;
+        if (KV8) {
+            LDS char* kbf = lds + RING_B;
+            LDS char* vbf = kbf + BF_TILE;
+            convert(kt, kbf);
+            convert(vt, vbf);
+            kt = kbf;
+            vt = vbf;
+        }
         f32x16 sacc = f32x16{};
 #pragma unroll
         for (int dc = 0; dc < D / 16; ++dc) {
@@ -649,7 +699,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
     // ---- epilogue
     const float l_tot = xhalf_sum((l_part[0] + l_part[1]) + (l_part[2] + l_part[3]));
     const bool live = l_tot > 0.f;
-    const float inv = live ? 1.f / l_tot : 0.f;
+    const float inv = live ? (KV8 ? p.vscale : 1.f) / l_tot : 0.f;
     const float lse_val = live ? (m_run + __log2f(l_tot)) * kLn2 : -__builtin_inff();
     const int64_t grow = ((int64_t)b * p.Sq + ti) * p.Hq + hh;
     if (!row_valid) return;
@@ -740,23 +790,30 @@ hipError_t launch_attention(const FwdParams& p, int d, bool causal, bool split, 
     return split ? launch_attn<64, false, true>(p, stream) : launch_attn<64, false, false>(p, stream);
 }
 
-template <int D, bool CAUSAL, bool SPLIT, bool PAGED>
+template <int D, bool CAUSAL, bool SPLIT, bool PAGED, bool KV8>
 static hipError_t launch_dec(const FwdParams& p, hipStream_t stream) {
-    hipLaunchKernelGGL((attn_decode_kernel<D, CAUSAL, SPLIT, PAGED, kDecStages>), dim3(p.grid), dim3(kDecThreads), 0,
-                       stream, p);
+    hipLaunchKernelGGL((attn_decode_kernel<D, CAUSAL, SPLIT, PAGED, KV8, KV8 ? kDecStagesKV8 : kDecStages>),
+                       dim3(p.grid), dim3(kDecThreads), 0, stream, p);
     return hipGetLastError();
 }
 
-template <int D, bool PAGED>
+template <int D, bool PAGED, bool KV8>
 static hipError_t launch_dec_d(const FwdParams& p, bool causal, bool split, hipStream_t stream) {
-    if (causal) return split ? launch_dec<D, true, true, PAGED>(p, stream) : launch_dec<D, true, false, PAGED>(p, stream);
-    return split ? launch_dec<D, false, true, PAGED>(p, stream) : launch_dec<D, false, false, PAGED>(p, stream);
+    if (causal)
+        return split ? launch_dec<D, true, true, PAGED, KV8>(p, stream) : launch_dec<D, true, false, PAGED, KV8>(p, stream);
+    return split ? launch_dec<D, false, true, PAGED, KV8>(p, stream) : launch_dec<D, false, false, PAGED, KV8>(p, stream);
 }
 
-hipError_t launch_decode(const FwdParams& p, int d, bool causal, bool split, bool paged, hipStream_t stream) {
-    if (d == 128)
-        return paged ? launch_dec_d<128, true>(p, causal, split, stream) : launch_dec_d<128, false>(p, causal, split, stream);
-    return paged ? launch_dec_d<64, true>(p, causal, split, stream) : launch_dec_d<64, false>(p, causal, split, stream);
+template <int D>
+static hipError_t launch_dec_dd(const FwdParams& p, bool causal, bool split, bool paged, bool kv8, hipStream_t stream) {
+    if (paged)
+        return kv8 ? launch_dec_d<D, true, true>(p, causal, split, stream) : launch_dec_d<D, true, false>(p, causal, split, stream);
+    return kv8 ? launch_dec_d<D, false, true>(p, causal, split, stream) : launch_dec_d<D, false, false>(p, causal, split, stream);
+}
+
+hipError_t launch_decode(const FwdParams& p, int d, bool causal, bool split, bool paged, bool kv8, hipStream_t stream) {
+    return d == 128 ? launch_dec_dd<128>(p, causal, split, paged, kv8, stream)
+                    : launch_dec_dd<64>(p, causal, split, paged, kv8, stream);
 }
 
 hipError_t launch_combine(const CombineParams& p, int d, long long grid, hipStream_t stream) {

@@ -61,14 +61,15 @@ void choose(const Shape& s, int num_cus, int* pack_gqa, int* num_splits) {
     // kernel wants two workgroups per compute unit. The decode kernel (at
     // most 32 rows, memory-bound) also wants two per compute unit, each with
     // kDecStages-1 tiles in flight: measured on MI355X, more and shorter
-    // workgroups only add tail and merge costs.
+    // workgroups only add tail and merge costs. With fp8 K/V its tiles cost
+    // more arithmetic per byte and four per compute unit are best.
     const int Gp = pack ? G : 1;
     const long long R = (long long)s.Sq * Gp;
     const bool decode = R <= kDecBlockM;
     const int bm = decode ? kDecBlockM : kBlockM, bn = decode ? kDecBlockN : kBlockN;
     const long long units = (long long)s.B * (pack ? s.Hk : s.Hq) * ceil_div(R, bm);
     const int T = R > 0 ? key_tiles_for(s, Gp, R, bn) : 0;
-    const long long target = 2LL * num_cus;
+    const long long target = (decode && s.kv_bytes == 1 ? 4LL : 2LL) * num_cus;
     int ns = 1;
     if (units > 0 && units < target && T > 1) {
         ns = (int)std::min<long long>(ceil_div(target, units), 16);

@@ -20,6 +20,10 @@ constexpr int kDecBlockM = 32;
 constexpr int kDecBlockN = 32;
 constexpr int kDecThreads = 64;
 constexpr int kDecStages = 4;
+// fp8 K/V: each tile is also converted to bf16 in LDS, which makes a
+// wavefront's tile slower than its copy; a shorter ring (40 KiB per
+// workgroup) lets four workgroups share a compute unit instead.
+constexpr int kDecStagesKV8 = 3;
 
 // Division by a runtime constant through a precomputed multiplier (the
 // batch-sensitivity article, "PackGQA" mechanism 3, precomputes the
@@ -39,6 +43,7 @@ inline uint32_t fastdiv_host(uint32_t n, const FastDiv& f) {
 
 struct Shape {
     int B, Sq, Sk, Hq, Hk, d, causal;
+    int kv_bytes = 2;  // bytes per stored K/V element: 2 (bf16) or 1 (fp8)
 };
 
 // Returns 0 or a gqa_status_t error for the sizes alone (no pointers).

@@ -34,6 +34,7 @@ struct FwdParams {
     const int* seqlens_k;    // [B] keys of each sequence
     int page_size, max_pages, num_pages;
     uint32_t pmul, pshift;   // magic divisor of page_size
+    float vscale;            // fp8 K/V (decode kernel): factor of the values
 };
 
 struct CombineParams {
@@ -46,7 +47,7 @@ struct CombineParams {
 };
 
 hipError_t launch_attention(const FwdParams& p, int d, bool causal, bool split, hipStream_t stream);
-hipError_t launch_decode(const FwdParams& p, int d, bool causal, bool split, bool paged, hipStream_t stream);
+hipError_t launch_decode(const FwdParams& p, int d, bool causal, bool split, bool paged, bool kv8, hipStream_t stream);
 hipError_t launch_combine(const CombineParams& p, int d, long long grid, hipStream_t stream);
 
 }  // namespace gqa

@@ -58,11 +58,12 @@ typedef enum {
     GQA_ERR_INVALID_ARG = -1, /* null tensor pointer, negative size, Hq % Hk != 0,
                                  Sk == 0 while B*Sq > 0, pack_gqa not in {-1,0,1},
                                  num_splits < 0, non-finite scale, size overflow;
-                                 paged: page_size, max_pages or num_pages <= 0 */
+                                 paged: page_size, max_pages or num_pages <= 0;
+                                 fp8: non-finite k_scale or v_scale */
     GQA_ERR_UNSUPPORTED = -2, /* d not in {64,128}, pointer not 16-byte aligned;
-                                 paged: page_size % 16 != 0, more than 32 query
-                                 rows per head unit, table pointers not 4-byte
-                                 aligned */
+                                 paged and fp8: more than 32 query rows per head
+                                 unit; paged: page_size % 16 != 0, table
+                                 pointers not 4-byte aligned */
     GQA_ERR_NOMEM = -3,       /* the split-KV workspace could not be allocated */
     GQA_ERR_HIP = -4          /* a HIP call or kernel launch failed */
 } gqa_status_t;
@@ -121,6 +122,34 @@ int gqa_attn_fwd_paged(const void* q, const void* k_cache, const void* v_cache,
                        int num_pages, int page_size, int max_pages,
                        int causal, float scale, int pack_gqa, int num_splits,
                        hipStream_t stream);
+
+/* Forward pass with K and V stored as fp8, for decode-shaped calls.
+ *
+ * The pages name FP8 e4m3 as the way to halve the bandwidth pressure of
+ * inference (rise-and-fall tuning article, "verification and further
+ * directions"; Stable-Diffusion GQA guide, FP8 intermediate precision). Here
+ * k and v hold OCP float8 e4m3 bytes (1 sign, 4 exponent bits with bias 7,
+ * 3 mantissa bits, subnormals, no infinity, S.1111.111 = NaN), layout
+ * [B, Sk, Hk, d] (one byte per element); q, out and lse are as for
+ * gqa_attn_fwd. With per-tensor factors k_scale and v_scale the operation is
+ * gqa_attn_fwd's over K = k_scale * k8 and V = v_scale * v8, computed as
+ * scores (scale * k_scale) * q.k8 and output v_scale * sum_j P_j v8_j:
+ * exact up to rounding like the bf16 path (every e4m3 value is exact in bf16).
+ * k_scale and v_scale: any finite fp32 values (INVALID_ARG otherwise).
+ * Decode-shaped calls only (at most 32 query rows per head unit, else
+ * GQA_ERR_UNSUPPORTED); other rules as for gqa_attn_fwd. */
+int gqa_attn_fwd_kv8(const void* q, const void* k, const void* v, float k_scale, float v_scale,
+                     void* out, float* lse, int B, int Sq, int Sk, int Hq, int Hk, int d,
+                     int causal, float scale, int pack_gqa, int num_splits, hipStream_t stream);
+
+/* gqa_attn_fwd_paged over fp8 page pools ([num_pages, page_size, Hk, d]
+ * e4m3 bytes), with gqa_attn_fwd_kv8's factors and rules. */
+int gqa_attn_fwd_paged_kv8(const void* q, const void* k_cache, const void* v_cache,
+                           float k_scale, float v_scale, const int* block_table, const int* seqlens_k,
+                           void* out, float* lse, int B, int Sq, int Hq, int Hk, int d,
+                           int num_pages, int page_size, int max_pages,
+                           int causal, float scale, int pack_gqa, int num_splits,
+                           hipStream_t stream);
 
 /* The host heuristic behind pack_gqa = -1 / num_splits = 0. It follows the
  * pages' rationale (rise-and-fall tuning article, "root cause" and "fix"

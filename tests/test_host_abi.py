@@ -33,7 +33,8 @@ def lib():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    assert names == ["gqa_attn_choose", "gqa_attn_fwd", "gqa_attn_fwd_paged", "gqa_attn_plan", "gqa_attn_strerror"]
+    assert names == ["gqa_attn_choose", "gqa_attn_fwd", "gqa_attn_fwd_kv8", "gqa_attn_fwd_paged",
+                     "gqa_attn_fwd_paged_kv8", "gqa_attn_plan", "gqa_attn_strerror"]
 
 
 def test_library_exports_every_declared_symbol():
