@@ -201,3 +201,17 @@ def random_fp8(seed: int, shape: Sequence[int], std: float = 1.0) -> torch.Tenso
 def to_fp8_bytes(x: torch.Tensor) -> torch.Tensor:
     """Round a tensor to float8_e4m3fn and return its bytes (uint8), e.g. a paged pool (NaN stays NaN)."""
     return x.to(torch.float32).to(torch.float8_e4m3fn).view(torch.uint8)
+
+
+def varlen_batch(seed: int, seqlens_q: Sequence[int], seqlens_k: Sequence[int], Hq: int, Hk: int, d: int):
+    """Packed variable-length inputs: q [total_q, Hq, d], k/v [total_k, Hk, d] bf16 and int32
+    cu_seqlens_q / cu_seqlens_k [B+1]. Sequence b's tokens are the draws of batch_slice for
+    batch element b, so a sequence can be regenerated on its own."""
+    qs, ks, vs = [], [], []
+    for b, (nq, nk) in enumerate(zip(seqlens_q, seqlens_k)):
+        qb, kb, vb = batch_slice(seed, b, int(nq), int(nk), Hq, Hk, d)
+        qs.append(qb)
+        ks.append(kb)
+        vs.append(vb)
+    cu = lambda lens: torch.tensor([0] + list(torch.tensor([int(x) for x in lens]).cumsum(0).tolist()), dtype=torch.int32)
+    return torch.cat(qs), torch.cat(ks), torch.cat(vs), cu(seqlens_q), cu(seqlens_k)
