@@ -231,6 +231,24 @@ def main():
                 "ms": round(msl, 4), "tflops": round(wl.flops / (msl * 1e-3) / 1e12, 1)}
         extra["llama_prefill_b4"] = llama
         del ql, kl, vl
+        # variable-length prefill: 16 packed sequences of 128 .. 2048 tokens, Llama-2 heads, causal
+        lens = [128 * (i + 1) for i in range(16)]
+        tot = sum(lens)
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(11)
+        qv = torch.randn((tot, wl.Hq, wl.d), generator=gen, device=dev).to(torch.bfloat16)
+        kv_ = torch.randn((tot, wl.Hk, wl.d), generator=gen, device=dev).to(torch.bfloat16)
+        vv = torch.randn((tot, wl.Hk, wl.d), generator=gen, device=dev).to(torch.bfloat16)
+        cu = torch.tensor([0] + list(torch.tensor(lens).cumsum(0).tolist()), dtype=torch.int32, device=dev)
+        ov = torch.empty_like(qv)
+        lv = torch.empty((wl.Hq, tot), dtype=torch.float32, device=dev)
+        msv, _ = time_calls(lambda: g.gqa_attn_fwd_varlen(qv, kv_, vv, ov, lv, cu, cu, max(lens), max(lens), True,
+                                                          wl.scale), args.steps, 5)
+        fl = sum(4.0 * wl.Hq * L * L * wl.d / 2 for L in lens)
+        extra["varlen_prefill_16seq_128to2048"] = {"ms": round(msv, 4), "tflops": round(fl / (msv * 1e-3) / 1e12, 1),
+                                                   "tokens": tot}
+        print(f"[bench] varlen prefill: {msv:.4f} ms", file=sys.stderr, flush=True)
+        del qv, kv_, vv, ov, lv
         # split-KV decode
         wd = gi.DECODE
         qd, kd, vd = gpu_randn_inputs(wd, dev, 9)

@@ -15,7 +15,7 @@ import os
 from typing import Optional, Tuple
 
 __all__ = ["GqaAttnError", "gqa_attn_fwd", "gqa_attn_func", "gqa_attn_fwd_paged", "gqa_attn_func_paged",
-           "gqa_attn_fwd_kv8", "gqa_attn_fwd_paged_kv8",
+           "gqa_attn_fwd_kv8", "gqa_attn_fwd_paged_kv8", "gqa_attn_fwd_varlen",
            "gqa_attn_choose", "gqa_attn_plan",
            "gqa_attn_strerror", "library_path", "load_library",
            "GQA_OK", "GQA_ERR_INVALID_ARG", "GQA_ERR_UNSUPPORTED", "GQA_ERR_NOMEM", "GQA_ERR_HIP"]
@@ -66,6 +66,8 @@ def load_library():
     lib.gqa_attn_fwd_paged_kv8.argtypes = [vp] * 3 + [c_float, c_float] + [vp] * 4 + [c_int] * 8 + \
         [c_int, c_float, c_int, c_int, vp]
     lib.gqa_attn_fwd_paged_kv8.restype = c_int
+    lib.gqa_attn_fwd_varlen.argtypes = [vp] * 7 + [c_int] * 8 + [c_int, c_float, c_int, c_int, vp]
+    lib.gqa_attn_fwd_varlen.restype = c_int
     lib.gqa_attn_choose.argtypes = [c_int] * 8 + [ctypes.POINTER(c_int), ctypes.POINTER(c_int)]
     lib.gqa_attn_choose.restype = c_int
     lib.gqa_attn_plan.argtypes = [c_int] * 10 + [ctypes.POINTER(_Plan)]
@@ -266,3 +268,37 @@ def gqa_attn_func_paged(q, k_cache, v_cache, block_table, seqlens_k, causal: boo
     gqa_attn_fwd_paged(q, k_cache, v_cache, block_table, seqlens_k, out, lse, causal, softmax_scale, pack_gqa,
                        num_splits)
     return (out, lse) if return_lse else out
+
+
+def gqa_attn_fwd_varlen(q, k, v, out, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int,
+                        causal: bool, scale: float, pack_gqa: int = -1, num_splits: int = 0, stream=None) -> None:
+    """Forward pass over packed variable-length sequences.
+
+    q/out: [total_q, Hq, d] bf16; k/v: [total_k, Hk, d] bf16; lse: [Hq, total_q] fp32 or None;
+    cu_seqlens_q / cu_seqlens_k: [B+1] int32 cumulative lengths. All contiguous on the same GPU.
+    """
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+        if t.dtype != torch.bfloat16 or not t.is_contiguous() or t.dim() != 3 or not t.is_cuda:
+            raise ValueError(f"{name} must be a contiguous 3-d bfloat16 GPU tensor")
+    total_q, Hq, d = q.shape
+    total_k, Hk, dk = k.shape
+    if dk != d or tuple(v.shape) != tuple(k.shape) or tuple(out.shape) != tuple(q.shape):
+        raise ValueError("shape mismatch between q, k, v and out")
+    for name, t in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k)):
+        if t.dtype != torch.int32 or t.dim() != 1 or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError(f"{name} must be a contiguous 1-d int32 GPU tensor")
+    if cu_seqlens_k.shape[0] != cu_seqlens_q.shape[0]:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must have the same length B+1")
+    B = cu_seqlens_q.shape[0] - 1
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()
+                            or tuple(lse.shape) != (Hq, total_q) or not lse.is_cuda):
+        raise ValueError("lse must be a contiguous [Hq, total_q] float32 GPU tensor")
+    stream = _stream(q, stream)
+    with torch.cuda.device(q.device):
+        st = load_library().gqa_attn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(cu_seqlens_q),
+                                                _ptr(cu_seqlens_k), B, int(max_seqlen_q), int(max_seqlen_k), total_q,
+                                                total_k, Hq, Hk, d, int(bool(causal)), float(scale), int(pack_gqa),
+                                                int(num_splits), stream)
+    if st != GQA_OK:
+        raise GqaAttnError(st)

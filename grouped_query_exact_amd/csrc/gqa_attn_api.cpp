@@ -126,6 +126,10 @@ struct Call {
     hipStream_t stream;
     bool kv8 = false;       // fp8 e4m3 K/V with per-tensor factors
     float k_scale = 1.f, v_scale = 1.f;
+    bool varlen = false;    // packed sequences (s.Sq, s.Sk = max_seqlen_q, max_seqlen_k)
+    const int* cu_q = nullptr;
+    const int* cu_k = nullptr;
+    int total_q = 0, total_k = 0;
 };
 
 int run(const Call& c) {
@@ -174,6 +178,12 @@ int run(const Call& c) {
     p.qand = zero_scale ? 0u : 0xFFFFFFFFu;
     p.qsign = score_scale < 0.0 ? 0x80008000u : 0u;
     p.vscale = c.kv8 ? c.v_scale : 1.f;
+    if (c.varlen) {
+        p.cu_q = c.cu_q;
+        p.cu_k = c.cu_k;
+        p.total_q = c.total_q;
+        p.total_k = c.total_k;
+    }
     if (c.paged) {
         p.block_table = c.block_table;
         p.seqlens_k = c.seqlens_k;
@@ -194,8 +204,8 @@ int run(const Call& c) {
                      plan.combine_grid, plan.workspace_bytes);
 
     auto launch = [&](bool split) {
-        return plan.decode ? gqa::launch_decode(p, d, s.causal != 0, split, c.paged, c.kv8, c.stream)
-                           : gqa::launch_attention(p, d, s.causal != 0, split, c.stream);
+        return plan.decode ? gqa::launch_decode(p, d, s.causal != 0, split, c.paged, c.kv8, c.varlen, c.stream)
+                           : gqa::launch_attention(p, d, s.causal != 0, split, c.varlen, c.stream);
     };
     if (plan.ns == 1) {
         hipError_t e = launch(false);
@@ -204,11 +214,13 @@ int run(const Call& c) {
 
     keep_pool(dev);
     void* ws = nullptr;
-    if (hipMallocAsync(&ws, (size_t)plan.workspace_bytes, c.stream) != hipSuccess || !ws) {
+    const size_t ws_bytes = c.varlen ? (size_t)plan.ns * (size_t)c.total_q * s.Hq * ((size_t)d * 4 + 4)
+                                     : (size_t)plan.workspace_bytes;
+    if (hipMallocAsync(&ws, ws_bytes, c.stream) != hipSuccess || !ws) {
         (void)hipGetLastError();
         return GQA_ERR_NOMEM;
     }
-    const int64_t rows = (int64_t)s.B * s.Sq * s.Hq;
+    const int64_t rows = c.varlen ? (int64_t)c.total_q * s.Hq : (int64_t)s.B * s.Sq * s.Hq;
     p.opart = (float*)ws;
     p.lpart = (float*)ws + (int64_t)plan.ns * rows * d;
     hipError_t e = launch(true);
@@ -220,7 +232,7 @@ int run(const Call& c) {
         cp.lse = c.lse;
         cp.rows = rows;
         cp.ns = plan.ns;
-        cp.Sq = s.Sq;
+        cp.Sq = c.varlen ? c.total_q : s.Sq;  // varlen: lse [Hq, total_q] = one batch of total_q tokens
         cp.Hq = s.Hq;
         e = gqa::launch_combine(cp, d, plan.combine_grid, c.stream);
     }
@@ -246,6 +258,32 @@ int gqa_attn_fwd(const void* q, const void* k, const void* v, void* out, float* 
         if (!q || !k || !v || !out) return GQA_ERR_INVALID_ARG;
         if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return GQA_ERR_UNSUPPORTED;
         Call c{q, k, v, out, lse, s, scale, pack_gqa, num_splits, false, nullptr, nullptr, 0, 0, 0, stream};
+        return run(c);
+    } catch (...) {
+        return GQA_ERR_HIP;
+    }
+}
+
+int gqa_attn_fwd_varlen(const void* q, const void* k, const void* v, void* out, float* lse,
+                        const int* cu_seqlens_q, const int* cu_seqlens_k, int B, int max_seqlen_q,
+                        int max_seqlen_k, int total_q, int total_k, int Hq, int Hk, int d, int causal,
+                        float scale, int pack_gqa, int num_splits, hipStream_t stream) {
+    try {
+        if (total_q < 0 || total_k < 0) return GQA_ERR_INVALID_ARG;
+        const gqa::Shape s{B, max_seqlen_q, max_seqlen_k, Hq, Hk, d, causal ? 1 : 0};
+        int st = gqa::check_sizes(s, scale, pack_gqa, num_splits);
+        if (st != GQA_OK) return st;
+        if ((long long)B * max_seqlen_q == 0 || total_q == 0) return GQA_OK;
+        if (!q || !k || !v || !out || !cu_seqlens_q || !cu_seqlens_k) return GQA_ERR_INVALID_ARG;
+        if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned4(cu_seqlens_q) ||
+            !aligned4(cu_seqlens_k))
+            return GQA_ERR_UNSUPPORTED;
+        Call c{q, k, v, out, lse, s, scale, pack_gqa, num_splits, false, nullptr, nullptr, 0, 0, 0, stream};
+        c.varlen = true;
+        c.cu_q = cu_seqlens_q;
+        c.cu_k = cu_seqlens_k;
+        c.total_q = total_q;
+        c.total_k = total_k;
         return run(c);
     } catch (...) {
         return GQA_ERR_HIP;

@@ -133,7 +133,32 @@ __device__ __forceinline__ float xhalf_sum(float v) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <int D, bool CAUSAL, bool SPLIT>
+// Extent of sequence b of a variable-length (packed) call: query tokens
+// [qtok0, qtok0 + Sq) of q, keys [ktok0, ktok0 + Sk) of k and v. The offsets
+// are clamped into the packed tensors and Sq to the grid's max_seqlen_q, so
+// no offsets make a read or a write leave the buffers. Scalar loads
+// (constant address space): the values are wave-uniform.
+__device__ __forceinline__ void seq_extent(const FwdParams& p, int b, int64_t& qtok0, int& Sq, int64_t& ktok0, int& Sk) {
+    typedef const __attribute__((address_space(4))) int* cint_p;
+    const cint_p cq = (cint_p)p.cu_q;
+    const cint_p ck = (cint_p)p.cu_k;
+    const int q0 = min(max(cq[b], 0), p.total_q);
+    const int q1 = min(max(cq[b + 1], q0), p.total_q);
+    const int k0 = min(max(ck[b], 0), p.total_k);
+    const int k1 = min(max(ck[b + 1], k0), p.total_k);
+    qtok0 = __builtin_amdgcn_readfirstlane(q0);
+    Sq = __builtin_amdgcn_readfirstlane(min(q1 - q0, p.Sq));
+    ktok0 = __builtin_amdgcn_readfirstlane(k0);
+    Sk = __builtin_amdgcn_readfirstlane(k1 - k0);
+}
+
+// LSE element of (batch b, head hh, token ti): [B, Hq, Sq], or [Hq, total_q]
+// for variable-length calls (token qtok0 + ti of the packed axis).
+__device__ __forceinline__ int64_t lse_index(const FwdParams& p, int b, int hh, int64_t qtok0, int ti, bool varlen) {
+    return varlen ? (int64_t)hh * p.total_q + qtok0 + ti : ((int64_t)b * p.Hq + hh) * p.Sq + ti;
+}
+
+template <int D, bool CAUSAL, bool SPLIT, bool VARLEN>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_kernel(const FwdParams p) {
     constexpr int TILE = kBlockN * D;                 // elements of one K or V tile
     constexpr int TILE_B = TILE * 2;                  // bytes
@@ -159,18 +184,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int h0 = p.Gp > 1 ? unit * p.G : unit;  // first query head of the tile
     const int r0 = rt * kBlockM;
 
+    // ---- this sequence: query tokens qtok0 .. qtok0+Sq-1, keys ktok0 .. ktok0+Sk-1
+    int Sq = p.Sq, Sk = p.Sk;
+    int64_t qtok0 = (int64_t)b * p.Sq, ktok0 = (int64_t)b * p.Sk;
+    if (VARLEN) seq_extent(p, b, qtok0, Sq, ktok0, Sk);
+    const int R = VARLEN ? Sq * p.Gp : p.R;  // rows of this head unit
+    if (VARLEN && r0 >= R) return;            // row tile past the end of this sequence
+
     // ---- this lane's row: token ti, head hh
     const int r = r0 + wave * 32 + col;
-    const bool row_valid = r < p.R;
-    const int rc = min(r, p.R - 1);
+    const bool row_valid = r < R;
+    const int rc = min(r, R - 1);
     const int ti = (int)fdiv((uint32_t)rc, p.gmul, p.gshift);
     const int hh = h0 + (rc - ti * p.Gp);
-    const int koff = p.Sk - p.Sq;  // bottom-right causal offset
+    const int koff = Sk - Sq;  // bottom-right causal offset
 
     // ---- Q rows -> registers (B operand of S^T = K Q^T)
     bf16x8 qreg[D / 16];
     {
-        const uint16_t* qrow = p.q + (((int64_t)b * p.Sq + ti) * p.Hq + hh) * D;
+        const uint16_t* qrow = p.q + ((qtok0 + ti) * p.Hq + hh) * D;
 #pragma unroll
         for (int dc = 0; dc < D / 16; ++dc) {
             u32x4 w = *(const u32x4*)(qrow + dc * 16 + half * 8);
@@ -180,10 +212,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
 
     // ---- key tile range of this work item
-    const int r_last = min(r0 + kBlockM, p.R) - 1;
+    const int r_last = min(r0 + kBlockM, R) - 1;
     const int i_max = (int)fdiv((uint32_t)r_last, p.gmul, p.gshift);
-    int kv_end = p.Sk;
-    if (CAUSAL) kv_end = min(p.Sk, i_max + koff + 1);
+    int kv_end = Sk;
+    if (CAUSAL) kv_end = min(Sk, i_max + koff + 1);
     const int T = kv_end > 0 ? (kv_end + kBlockN - 1) / kBlockN : 0;
     int t_begin = 0, t_end = T;
     if (SPLIT) {
@@ -193,14 +225,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
     // rows of this wave: tokens [iw_min, iw_max]
     const int rw0 = r0 + wave * 32;
-    const bool wave_active = rw0 < p.R;
-    const int iw_min = (int)fdiv((uint32_t)min(rw0, p.R - 1), p.gmul, p.gshift);
-    const int iw_max = (int)fdiv((uint32_t)(min(rw0 + 32, p.R) - 1), p.gmul, p.gshift);
+    const bool wave_active = rw0 < R;
+    const int iw_min = (int)fdiv((uint32_t)min(rw0, R - 1), p.gmul, p.gshift);
+    const int iw_max = (int)fdiv((uint32_t)(min(rw0 + 32, R) - 1), p.gmul, p.gshift);
 
     // ---- K/V tile loads: per-lane byte offsets inside a tile, scalar tile base
     const int64_t kv_stride_b = (int64_t)p.Hk * D * 2;
-    const char* kbase = (const char*)(p.k + ((int64_t)b * p.Sk * p.Hk + g) * D);
-    const char* vbase = (const char*)(p.v + ((int64_t)b * p.Sk * p.Hk + g) * D);
+    const char* kbase = (const char*)(p.k + (ktok0 * p.Hk + g) * D);
+    const char* vbase = (const char*)(p.v + (ktok0 * p.Hk + g) * D);
     uint32_t goff[NLOAD];
 #pragma unroll
     for (int u = 0; u < NLOAD; ++u) {
@@ -214,7 +246,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         LDS char* vt = kt + TILE_B;
         const char* kg = kbase + kv0 * kv_stride_b;
         const char* vg = vbase + kv0 * kv_stride_b;
-        if (kv0 + kBlockN <= p.Sk) {
+        if (kv0 + kBlockN <= Sk) {
 #pragma unroll
             for (int u = 0; u < NLOAD; ++u) {
                 const int dst = (u * 4 + wave) * 1024;
@@ -228,7 +260,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 const int ci = (u * 4 + wave) * 64 + lane;
                 const int row = ci / NCH;
                 const int logical_ch = (ci % NCH) ^ swz<D>(row);
-                const int key = min(kv0 + row, p.Sk - 1) - kv0;
+                const int key = min(kv0 + row, Sk - 1) - kv0;
                 const uint32_t o = (uint32_t)(key * kv_stride_b + logical_ch * 16);
                 lds_dma16(kg, o, kt + dst);
                 lds_dma16(vg, o, vt + dst);
@@ -259,7 +291,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     float m_run = -__builtin_inff();  // running max, scaled log2 units
     float l_part[4] = {0.f, 0.f, 0.f, 0.f};  // this lane's partial row sums
     const float c = p.c;
-    const int jlim = CAUSAL ? min(p.Sk - 1, ti + koff) : p.Sk - 1;  // last key visible to this row
+    const int jlim = CAUSAL ? min(Sk - 1, ti + koff) : Sk - 1;  // last key visible to this row
 
     // One key tile: scores, online softmax, output update. `buf` selects the
     // LDS stage; `need_mask` is uniform across the wave.
@@ -357,7 +389,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const int kv0 = t * kBlockN;
         // waves whose rows see none of these keys skip the arithmetic
         if (wave_active && !(CAUSAL && kv0 > iw_max + koff)) {
-            const bool need_mask = (kv0 + kBlockN > p.Sk) || (CAUSAL && kv0 + kBlockN - 1 > iw_min + koff);
+            const bool need_mask = (kv0 + kBlockN > Sk) || (CAUSAL && kv0 + kBlockN - 1 > iw_min + koff);
             compute(buf, kv0, need_mask);
         }
     }
@@ -367,7 +399,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const bool live = l_tot > 0.f;
     const float inv = live ? 1.f / l_tot : 0.f;
     const float lse_val = live ? (m_run + __log2f(l_tot)) * kLn2 : -__builtin_inff();
-    const int64_t grow = ((int64_t)b * p.Sq + ti) * p.Hq + hh;  // row of [B, Sq, Hq]
+    const int64_t grow = (qtok0 + ti) * p.Hq + hh;  // row of [B*Sq or total_q, Hq]
     if (!SPLIT) {
         if (row_valid) {
             uint16_t* orow = p.o + grow * D;
@@ -380,11 +412,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                     for (int i = 0; i < 8; ++i) ov[i] = (__bf16)(oacc[cb][run * 8 + i] * inv);
                     *(bf16x8*)(orow + cb * 32 + run * 16 + half * 8) = ov;
                 }
-            if (half == 0 && p.lse) p.lse[((int64_t)b * p.Hq + hh) * p.Sq + ti] = lse_val;
+            if (half == 0 && p.lse) p.lse[lse_index(p, b, hh, qtok0, ti, VARLEN)] = lse_val;
         }
     } else {
         if (row_valid) {
-            const int64_t rows = (int64_t)p.B * p.Sq * p.Hq;
+            const int64_t rows = VARLEN ? (int64_t)p.total_q * p.Hq : (int64_t)p.B * p.Sq * p.Hq;
             float* orow = p.opart + ((int64_t)s * rows + grow) * D;
 #pragma unroll
             for (int cb = 0; cb < D / 32; ++cb)
@@ -433,7 +465,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // converts it into a bf16 staging tile laid out exactly like a bf16 ring
 // tile, so the products are the same as for bf16 K/V holding the fp8 values
 // (every e4m3 value is exact in bf16).
-template <int D, bool CAUSAL, bool SPLIT, bool PAGED, bool KV8, int STAGES>
+template <int D, bool CAUSAL, bool SPLIT, bool PAGED, bool KV8, bool VARLEN, int STAGES>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void attn_decode_kernel(const FwdParams p) {
     constexpr int BN = kDecBlockN;                 // keys per tile
     constexpr int EB = KV8 ? 1 : 2;                // bytes per stored K/V element
@@ -459,19 +491,25 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
     const int g = p.Gp > 1 ? unit : unit / p.G;   // KV head
     const int h0 = p.Gp > 1 ? unit * p.G : unit;  // first query head of the unit
 
+    // ---- this sequence: query tokens qtok0 .. qtok0+Sq-1, keys ktok0 .. ktok0+Sk-1
+    int Sq = p.Sq, Sk = p.Sk;
+    int64_t qtok0 = (int64_t)b * p.Sq, ktok0 = (int64_t)b * p.Sk;
+    if (VARLEN) seq_extent(p, b, qtok0, Sq, ktok0, Sk);
+    if (PAGED) Sk = __builtin_amdgcn_readfirstlane(min(max(p.seqlens_k[b], 0), p.max_pages * p.page_size));
+    const int R = VARLEN ? Sq * p.Gp : p.R;  // rows of this head unit
+    if (VARLEN && R == 0) return;             // a sequence without queries
+
     // ---- this lane's row (all R <= 32 rows of the head unit): token ti, head hh
     const int r = col;
-    const bool row_valid = r < p.R;
-    const int rc = min(r, p.R - 1);
+    const bool row_valid = r < R;
+    const int rc = min(r, R - 1);
     const int ti = (int)fdiv((uint32_t)rc, p.gmul, p.gshift);
     const int hh = h0 + (rc - ti * p.Gp);
-    int Sk = p.Sk;  // keys of this sequence
-    if (PAGED) Sk = __builtin_amdgcn_readfirstlane(min(max(p.seqlens_k[b], 0), p.max_pages * p.page_size));
-    const int koff = Sk - p.Sq;  // bottom-right causal offset
+    const int koff = Sk - Sq;  // bottom-right causal offset
 
     bf16x8 qreg[D / 16];
     {
-        const uint16_t* qrow = p.q + (((int64_t)b * p.Sq + ti) * p.Hq + hh) * D;
+        const uint16_t* qrow = p.q + ((qtok0 + ti) * p.Hq + hh) * D;
 #pragma unroll
         for (int dc = 0; dc < D / 16; ++dc) {
             u32x4 w = *(const u32x4*)(qrow + dc * 16 + half * 8);
@@ -482,7 +520,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
 
     // ---- key tiles of this split. The unit's rows are tokens 0 .. Sq-1.
     int kv_end = Sk;
-    if (CAUSAL) kv_end = min(Sk, p.Sq - 1 + koff + 1);
+    if (CAUSAL) kv_end = min(Sk, Sq - 1 + koff + 1);
     const int T = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
     int t_begin = 0, t_end = T;
     if (SPLIT) {
@@ -495,7 +533,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
     // stored swizzled (chunk c of row r at c ^ swz(r)); fp8 tiles in order.
     const int64_t kv_stride_b = (int64_t)p.Hk * D * EB;
     // contiguous: this sequence's rows of head g; paged: head g of page 0
-    const int64_t seq_off = PAGED ? (int64_t)g * D : ((int64_t)b * p.Sk * p.Hk + g) * D;
+    const int64_t seq_off = PAGED ? (int64_t)g * D : (ktok0 * p.Hk + g) * D;
     const char* kbase = (const char*)p.k + seq_off * EB;
     const char* vbase = (const char*)p.v + seq_off * EB;
     auto ring_chunk = [&](int ci, int row) { return KV8 ? (ci % NCH) : ((ci % NCH) ^ swz<D>(row)); };
@@ -701,7 +739,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
     const bool live = l_tot > 0.f;
     const float inv = live ? (KV8 ? p.vscale : 1.f) / l_tot : 0.f;
     const float lse_val = live ? (m_run + __log2f(l_tot)) * kLn2 : -__builtin_inff();
-    const int64_t grow = ((int64_t)b * p.Sq + ti) * p.Hq + hh;
+    const int64_t grow = (qtok0 + ti) * p.Hq + hh;
     if (!row_valid) return;
     if (!SPLIT) {
         uint16_t* orow = p.o + grow * D;
@@ -714,9 +752,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
                 for (int i = 0; i < 8; ++i) ov[i] = (__bf16)(oacc[cb][run * 8 + i] * inv);
                 *(bf16x8*)(orow + cb * 32 + run * 16 + half * 8) = ov;
             }
-        if (half == 0 && p.lse) p.lse[((int64_t)b * p.Hq + hh) * p.Sq + ti] = lse_val;
+        if (half == 0 && p.lse) p.lse[lse_index(p, b, hh, qtok0, ti, VARLEN)] = lse_val;
     } else {
-        const int64_t rows = (int64_t)p.B * p.Sq * p.Hq;
+        const int64_t rows = VARLEN ? (int64_t)p.total_q * p.Hq : (int64_t)p.B * p.Sq * p.Hq;
         float* orow = p.opart + ((int64_t)s * rows + grow) * D;
 #pragma unroll
         for (int cb = 0; cb < D / 32; ++cb)
@@ -775,45 +813,56 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombineParams p) {
 }
 
 // ---------------------------------------------------------------- launchers
-template <int D, bool CAUSAL, bool SPLIT>
+template <int D, bool CAUSAL, bool SPLIT, bool VARLEN>
 static hipError_t launch_attn(const FwdParams& p, hipStream_t stream) {
-    hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, SPLIT>), dim3(p.grid), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, SPLIT, VARLEN>), dim3(p.grid), dim3(kThreads), 0, stream, p);
     return hipGetLastError();
 }
 
-hipError_t launch_attention(const FwdParams& p, int d, bool causal, bool split, hipStream_t stream) {
-    if (d == 128) {
-        if (causal) return split ? launch_attn<128, true, true>(p, stream) : launch_attn<128, true, false>(p, stream);
-        return split ? launch_attn<128, false, true>(p, stream) : launch_attn<128, false, false>(p, stream);
-    }
-    if (causal) return split ? launch_attn<64, true, true>(p, stream) : launch_attn<64, true, false>(p, stream);
-    return split ? launch_attn<64, false, true>(p, stream) : launch_attn<64, false, false>(p, stream);
+template <int D, bool VARLEN>
+static hipError_t launch_attn_d(const FwdParams& p, bool causal, bool split, hipStream_t stream) {
+    if (causal) return split ? launch_attn<D, true, true, VARLEN>(p, stream) : launch_attn<D, true, false, VARLEN>(p, stream);
+    return split ? launch_attn<D, false, true, VARLEN>(p, stream) : launch_attn<D, false, false, VARLEN>(p, stream);
 }
 
-template <int D, bool CAUSAL, bool SPLIT, bool PAGED, bool KV8>
+hipError_t launch_attention(const FwdParams& p, int d, bool causal, bool split, bool varlen, hipStream_t stream) {
+    if (d == 128)
+        return varlen ? launch_attn_d<128, true>(p, causal, split, stream) : launch_attn_d<128, false>(p, causal, split, stream);
+    return varlen ? launch_attn_d<64, true>(p, causal, split, stream) : launch_attn_d<64, false>(p, causal, split, stream);
+}
+
+template <int D, bool CAUSAL, bool SPLIT, bool PAGED, bool KV8, bool VARLEN>
 static hipError_t launch_dec(const FwdParams& p, hipStream_t stream) {
-    hipLaunchKernelGGL((attn_decode_kernel<D, CAUSAL, SPLIT, PAGED, KV8, KV8 ? kDecStagesKV8 : kDecStages>),
+    hipLaunchKernelGGL((attn_decode_kernel<D, CAUSAL, SPLIT, PAGED, KV8, VARLEN, KV8 ? kDecStagesKV8 : kDecStages>),
                        dim3(p.grid), dim3(kDecThreads), 0, stream, p);
     return hipGetLastError();
 }
 
-template <int D, bool PAGED, bool KV8>
+template <int D, bool PAGED, bool KV8, bool VARLEN>
 static hipError_t launch_dec_d(const FwdParams& p, bool causal, bool split, hipStream_t stream) {
     if (causal)
-        return split ? launch_dec<D, true, true, PAGED, KV8>(p, stream) : launch_dec<D, true, false, PAGED, KV8>(p, stream);
-    return split ? launch_dec<D, false, true, PAGED, KV8>(p, stream) : launch_dec<D, false, false, PAGED, KV8>(p, stream);
+        return split ? launch_dec<D, true, true, PAGED, KV8, VARLEN>(p, stream)
+                     : launch_dec<D, true, false, PAGED, KV8, VARLEN>(p, stream);
+    return split ? launch_dec<D, false, true, PAGED, KV8, VARLEN>(p, stream)
+                 : launch_dec<D, false, false, PAGED, KV8, VARLEN>(p, stream);
 }
 
+// Instantiated combinations: contiguous, paged, fp8, paged fp8, variable-length (bf16).
 template <int D>
-static hipError_t launch_dec_dd(const FwdParams& p, bool causal, bool split, bool paged, bool kv8, hipStream_t stream) {
+static hipError_t launch_dec_dd(const FwdParams& p, bool causal, bool split, bool paged, bool kv8, bool varlen,
+                                hipStream_t stream) {
+    if (varlen) return launch_dec_d<D, false, false, true>(p, causal, split, stream);
     if (paged)
-        return kv8 ? launch_dec_d<D, true, true>(p, causal, split, stream) : launch_dec_d<D, true, false>(p, causal, split, stream);
-    return kv8 ? launch_dec_d<D, false, true>(p, causal, split, stream) : launch_dec_d<D, false, false>(p, causal, split, stream);
+        return kv8 ? launch_dec_d<D, true, true, false>(p, causal, split, stream)
+                   : launch_dec_d<D, true, false, false>(p, causal, split, stream);
+    return kv8 ? launch_dec_d<D, false, true, false>(p, causal, split, stream)
+               : launch_dec_d<D, false, false, false>(p, causal, split, stream);
 }
 
-hipError_t launch_decode(const FwdParams& p, int d, bool causal, bool split, bool paged, bool kv8, hipStream_t stream) {
-    return d == 128 ? launch_dec_dd<128>(p, causal, split, paged, kv8, stream)
-                    : launch_dec_dd<64>(p, causal, split, paged, kv8, stream);
+hipError_t launch_decode(const FwdParams& p, int d, bool causal, bool split, bool paged, bool kv8, bool varlen,
+                         hipStream_t stream) {
+    return d == 128 ? launch_dec_dd<128>(p, causal, split, paged, kv8, varlen, stream)
+                    : launch_dec_dd<64>(p, causal, split, paged, kv8, varlen, stream);
 }
 
 hipError_t launch_combine(const CombineParams& p, int d, long long grid, hipStream_t stream) {

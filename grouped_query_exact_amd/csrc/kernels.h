@@ -35,6 +35,11 @@ struct FwdParams {
     int page_size, max_pages, num_pages;
     uint32_t pmul, pshift;   // magic divisor of page_size
     float vscale;            // fp8 K/V (decode kernel): factor of the values
+    // variable-length calls: q/o [total_q, Hq, D], k/v [total_k, Hk, D], lse
+    // [Hq, total_q]; Sq is max_seqlen_q (the grid's row tiles), Sk unused.
+    const int* cu_q;         // [B+1] cumulative query lengths
+    const int* cu_k;         // [B+1] cumulative key lengths
+    int total_q, total_k;
 };
 
 struct CombineParams {
@@ -46,8 +51,9 @@ struct CombineParams {
     int ns, Sq, Hq;
 };
 
-hipError_t launch_attention(const FwdParams& p, int d, bool causal, bool split, hipStream_t stream);
-hipError_t launch_decode(const FwdParams& p, int d, bool causal, bool split, bool paged, bool kv8, hipStream_t stream);
+hipError_t launch_attention(const FwdParams& p, int d, bool causal, bool split, bool varlen, hipStream_t stream);
+hipError_t launch_decode(const FwdParams& p, int d, bool causal, bool split, bool paged, bool kv8, bool varlen,
+                         hipStream_t stream);
 hipError_t launch_combine(const CombineParams& p, int d, long long grid, hipStream_t stream);
 
 }  // namespace gqa

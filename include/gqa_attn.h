@@ -86,6 +86,35 @@ int gqa_attn_fwd(const void* q, const void* k, const void* v, void* out, float* 
                  int causal, float scale, int pack_gqa, int num_splits,
                  hipStream_t stream);
 
+/* Forward pass over a batch of sequences of different lengths, packed along
+ * the token axis.
+ *
+ * The pages list variable-length sequences among the uses of grouped-query
+ * attention (batch-sensitivity article, "applicable scenarios") and the
+ * continuous batching of generation requests (Llama-2 GQA article, section
+ * 4.1), without a layout; this is the plainest reading:
+ *   q, out        : [total_q, Hq, d] bf16, the B sequences' tokens one after another
+ *   k, v          : [total_k, Hk, d] bf16
+ *   lse           : [Hq, total_q] fp32, or NULL
+ *   cu_seqlens_q  : [B+1] int32 device memory: sequence b owns query tokens
+ *                   cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 (non-decreasing, from 0)
+ *   cu_seqlens_k  : [B+1] int32 device memory, the same for keys
+ *   max_seqlen_q  : upper bound of every sequence's query count (sizes the grid)
+ *   max_seqlen_k  : upper bound of every key count (used by the heuristic)
+ * Every sequence is computed exactly as gqa_attn_fwd would compute it alone,
+ * with its own lengths and bottom-right causal alignment; a sequence without
+ * keys gives O = 0 and LSE = -inf. The offsets live on the device and are not
+ * validated on the host: the kernels clamp them into [0, total] and a query
+ * count to max_seqlen_q, so bad offsets give wrong results (tokens past
+ * max_seqlen_q of a sequence are not written), never an out-of-bounds
+ * access. Pointers as for gqa_attn_fwd (the offset arrays 4-byte aligned).
+ * Returns a gqa_status_t (B*max_seqlen_q == 0 or total_q == 0: no-op). */
+int gqa_attn_fwd_varlen(const void* q, const void* k, const void* v, void* out, float* lse,
+                        const int* cu_seqlens_q, const int* cu_seqlens_k,
+                        int B, int max_seqlen_q, int max_seqlen_k, int total_q, int total_k,
+                        int Hq, int Hk, int d, int causal, float scale, int pack_gqa, int num_splits,
+                        hipStream_t stream);
+
 /* Forward pass over a paged KV cache, for decode-shaped calls.
  *
  * The pages serve dynamic-length sequences (and caches of sequences longer

@@ -34,7 +34,7 @@ def lib():
 def test_header_declares_the_boundary():
     names = declared_functions()
     assert names == ["gqa_attn_choose", "gqa_attn_fwd", "gqa_attn_fwd_kv8", "gqa_attn_fwd_paged",
-                     "gqa_attn_fwd_paged_kv8", "gqa_attn_plan", "gqa_attn_strerror"]
+                     "gqa_attn_fwd_paged_kv8", "gqa_attn_fwd_varlen", "gqa_attn_plan", "gqa_attn_strerror"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -133,6 +133,28 @@ def test_paged_argument_checks(kw, status):
         assert st in (g.GQA_OK, g.GQA_ERR_HIP)  # no GPU here: the first HIP call fails
     else:
         assert st == getattr(g, "GQA_ERR_" + status), (kw, st)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(total_q=-1), "INVALID_ARG"),
+    (dict(total_k=-1), "INVALID_ARG"),
+    (dict(msk=0), "INVALID_ARG"),                   # queries but no key anywhere
+    (dict(cq=None), "INVALID_ARG"),
+    (dict(ck=None), "INVALID_ARG"),
+    (dict(Hq=6, Hk=4), "INVALID_ARG"),
+    (dict(d=32), "UNSUPPORTED"),
+    (dict(cq=1.0005), "UNSUPPORTED"),              # offsets not 4-byte aligned
+])
+def test_varlen_argument_checks(kw, status):
+    import grouped_query_exact_amd as g
+    a = dict(q=1, k=1, v=1, out=1, lse=None, cq=1, ck=1, B=2, msq=9, msk=9, total_q=12, total_k=12, Hq=4, Hk=2,
+             d=64, causal=0, scale=0.125, pack=-1, ns=0)
+    a.update(kw)
+    P = lambda x: None if x is None else ctypes.c_void_p(int(x * 4096))
+    st = lib().gqa_attn_fwd_varlen(P(a["q"]), P(a["k"]), P(a["v"]), P(a["out"]), P(a["lse"]), P(a["cq"]), P(a["ck"]),
+                                   a["B"], a["msq"], a["msk"], a["total_q"], a["total_k"], a["Hq"], a["Hk"], a["d"],
+                                   a["causal"], a["scale"], a["pack"], a["ns"], None)
+    assert st == getattr(g, "GQA_ERR_" + status), (kw, st)
 
 
 def test_paged_misaligned_table_is_unsupported():
