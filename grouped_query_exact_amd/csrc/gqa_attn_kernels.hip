@@ -173,13 +173,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int col = lane & 31, half = lane >> 5;
 
     // ---- work item
-    const int logical = xcd_remap(blockIdx.x, p.grid);
-    const int s = logical % p.ns;
-    int tmp = logical / p.ns;
-    const int rt = p.row_tiles - 1 - (tmp % p.row_tiles);  // heaviest causal tiles first
-    tmp /= p.row_tiles;
-    const int unit = tmp % p.units_per_b;
-    const int b = tmp / p.units_per_b;
+    int s, rt, unit, b;
+    if (!VARLEN) {
+        const int logical = xcd_remap(blockIdx.x, p.grid);
+        s = logical % p.ns;
+        int tmp = logical / p.ns;
+        rt = p.row_tiles - 1 - (tmp % p.row_tiles);  // heaviest causal tiles first
+        tmp /= p.row_tiles;
+        unit = tmp % p.units_per_b;
+        b = tmp / p.units_per_b;
+    } else {
+        // sequences of different lengths: the row tile is the slowest index,
+        // so the heaviest causal tiles of all sequences start first; items are
+        // not of equal cost, so they are dealt round-robin over the XCDs
+        s = blockIdx.x % p.ns;
+        const int tmp = blockIdx.x / p.ns;
+        const int nbu = p.B * p.units_per_b;
+        rt = p.row_tiles - 1 - tmp / nbu;
+        unit = (tmp % nbu) % p.units_per_b;
+        b = (tmp % nbu) / p.units_per_b;
+    }
     const int g = p.Gp > 1 ? unit : unit / p.G;   // KV head
     const int h0 = p.Gp > 1 ? unit * p.G : unit;  // first query head of the tile
     const int r0 = rt * kBlockM;
