@@ -15,7 +15,7 @@ import os
 from typing import Optional, Tuple
 
 __all__ = ["GqaAttnError", "gqa_attn_fwd", "gqa_attn_func", "gqa_attn_fwd_paged", "gqa_attn_func_paged",
-           "gqa_attn_fwd_kv8", "gqa_attn_fwd_paged_kv8", "gqa_attn_fwd_varlen",
+           "gqa_attn_fwd_kv8", "gqa_attn_fwd_paged_kv8", "gqa_attn_fwd_varlen", "gqa_attn_bwd",
            "gqa_attn_choose", "gqa_attn_plan",
            "gqa_attn_strerror", "library_path", "load_library",
            "GQA_OK", "GQA_ERR_INVALID_ARG", "GQA_ERR_UNSUPPORTED", "GQA_ERR_NOMEM", "GQA_ERR_HIP"]
@@ -68,6 +68,8 @@ def load_library():
     lib.gqa_attn_fwd_paged_kv8.restype = c_int
     lib.gqa_attn_fwd_varlen.argtypes = [vp] * 7 + [c_int] * 8 + [c_int, c_float, c_int, c_int, vp]
     lib.gqa_attn_fwd_varlen.restype = c_int
+    lib.gqa_attn_bwd.argtypes = [vp] * 9 + [c_int] * 7 + [c_float, vp]
+    lib.gqa_attn_bwd.restype = c_int
     lib.gqa_attn_choose.argtypes = [c_int] * 8 + [ctypes.POINTER(c_int), ctypes.POINTER(c_int)]
     lib.gqa_attn_choose.restype = c_int
     lib.gqa_attn_plan.argtypes = [c_int] * 10 + [ctypes.POINTER(_Plan)]
@@ -300,5 +302,32 @@ def gqa_attn_fwd_varlen(q, k, v, out, lse, cu_seqlens_q, cu_seqlens_k, max_seqle
                                                 _ptr(cu_seqlens_k), B, int(max_seqlen_q), int(max_seqlen_k), total_q,
                                                 total_k, Hq, Hk, d, int(bool(causal)), float(scale), int(pack_gqa),
                                                 int(num_splits), stream)
+    if st != GQA_OK:
+        raise GqaAttnError(st)
+
+
+def gqa_attn_bwd(q, k, v, out, lse, dout, dq, dk, dv, causal: bool, scale: float, stream=None) -> None:
+    """Gradients of the forward pass into ``dq``, ``dk``, ``dv`` (caller-allocated).
+
+    q/out/dout/dq: [B, Sq, Hq, d] bf16; k/v/dk/dv: [B, Sk, Hk, d] bf16; lse: [B, Hq, Sq] fp32 from the
+    forward call on the same inputs. All contiguous on the same GPU.
+    """
+    import torch
+    _check_bf16(q=q, k=k, v=v, out=out, dout=dout, dq=dq, dk=dk, dv=dv)
+    B, Sq, Hq, d = q.shape
+    _, Sk, Hk, _ = k.shape
+    for name, t, shape in (("out", out, q.shape), ("dout", dout, q.shape), ("dq", dq, q.shape),
+                           ("v", v, k.shape), ("dk", dk, k.shape), ("dv", dv, k.shape)):
+        if tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{name} has the wrong shape")
+    if tuple(k.shape) != (B, Sk, Hk, d):
+        raise ValueError("k must be [B, Sk, Hk, d]")
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != (B, Hq, Sq) or not lse.is_cuda:
+        raise ValueError("lse must be a contiguous [B, Hq, Sq] float32 GPU tensor")
+    stream = _stream(q, stream)
+    with torch.cuda.device(q.device):
+        st = load_library().gqa_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq),
+                                         _ptr(dk), _ptr(dv), B, Sq, Sk, Hq, Hk, d, int(bool(causal)), float(scale),
+                                         stream)
     if st != GQA_OK:
         raise GqaAttnError(st)

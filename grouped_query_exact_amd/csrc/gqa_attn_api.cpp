@@ -264,6 +264,69 @@ int gqa_attn_fwd(const void* q, const void* k, const void* v, void* out, float* 
     }
 }
 
+int gqa_attn_bwd(const void* q, const void* k, const void* v, const void* out, const float* lse, const void* dout,
+                 void* dq, void* dk, void* dv, int B, int Sq, int Sk, int Hq, int Hk, int d, int causal, float scale,
+                 hipStream_t stream) {
+    try {
+        const gqa::Shape s{B, Sq, Sk, Hq, Hk, d, causal ? 1 : 0};
+        int st = gqa::check_sizes(s, scale, -1, 0);
+        if (st != GQA_OK) return st;
+        if ((long long)B * Sq == 0 && (long long)B * Sk == 0) return GQA_OK;
+        if (!q || !k || !v || !out || !lse || !dout || !dq || !dk || !dv) return GQA_ERR_INVALID_ARG;
+        if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(dout) || !aligned16(dq) ||
+            !aligned16(dk) || !aligned16(dv) || !aligned4(lse))
+            return GQA_ERR_UNSUPPORTED;
+        // per-batch byte offsets of the query tiles are 32-bit
+        if ((long long)Sq * Hq * d * 2 > 0x7FFFFFFFLL || (long long)Hq * Sq * 4 > 0x7FFFFFFFLL) return GQA_ERR_INVALID_ARG;
+        const int G = Hq / Hk;
+        if ((long long)Sq * G > INT_MAX / 2) return GQA_ERR_INVALID_ARG;
+        gqa::BwdParams p{};
+        p.q = (const uint16_t*)q;
+        p.k = (const uint16_t*)k;
+        p.v = (const uint16_t*)v;
+        p.o = (const uint16_t*)out;
+        p.dout = (const uint16_t*)dout;
+        p.lse = lse;
+        p.dq = (uint16_t*)dq;
+        p.dk = (uint16_t*)dk;
+        p.dv = (uint16_t*)dv;
+        p.B = B;
+        p.Sq = Sq;
+        p.Sk = Sk;
+        p.Hq = Hq;
+        p.Hk = Hk;
+        p.G = G;
+        const gqa::FastDiv fd = gqa::make_fastdiv((uint32_t)G);
+        p.gmul = fd.mul;
+        p.gshift = fd.shift;
+        p.R = Sq * G;
+        p.row_tiles = (p.R + gqa::kBlockM - 1) / gqa::kBlockM;
+        p.key_blocks = (Sk + gqa::kBwdKeys - 1) / gqa::kBwdKeys;
+        const long long gdq = (long long)B * Hk * p.row_tiles, gkv = (long long)B * Hk * p.key_blocks;
+        if (gdq > INT_MAX || gkv > INT_MAX) return GQA_ERR_INVALID_ARG;
+        p.grid_dq = (int)gdq;
+        p.grid_dkdv = (int)gkv;
+        p.c = (float)((double)scale * 1.4426950408889634);
+        p.scale = scale;
+        if (current_device() < 0) return GQA_ERR_HIP;
+        const int dev = current_device();
+        keep_pool(dev);
+        void* ws = nullptr;
+        const size_t ws_bytes = (size_t)B * Hq * (size_t)(Sq > 0 ? Sq : 1) * 4;
+        if (hipMallocAsync(&ws, ws_bytes, stream) != hipSuccess || !ws) {
+            (void)hipGetLastError();
+            return GQA_ERR_NOMEM;
+        }
+        p.drow = (float*)ws;
+        const hipError_t e = gqa::launch_backward(p, d, causal != 0, stream);
+        const hipError_t ef = hipFreeAsync(ws, stream);
+        if (e != hipSuccess || ef != hipSuccess) return GQA_ERR_HIP;
+        return GQA_OK;
+    } catch (...) {
+        return GQA_ERR_HIP;
+    }
+}
+
 int gqa_attn_fwd_varlen(const void* q, const void* k, const void* v, void* out, float* lse,
                         const int* cu_seqlens_q, const int* cu_seqlens_k, int B, int max_seqlen_q,
                         int max_seqlen_k, int total_q, int total_k, int Hq, int Hk, int d, int causal,

@@ -25,6 +25,11 @@ constexpr int kDecStages = 4;
 // workgroup) lets four workgroups share a compute unit instead.
 constexpr int kDecStagesKV8 = 3;
 
+// Backward pass: the dK/dV kernel takes 128 keys per workgroup (32 per
+// wavefront) against query tiles of 32 packed rows.
+constexpr int kBwdKeys = 128;
+constexpr int kBwdRows = 32;
+
 // Division by a runtime constant through a precomputed multiplier (the
 // batch-sensitivity article, "PackGQA" mechanism 3, precomputes the
 // query-head -> KV-head map with a fast divide-and-modulo). Round-up method:

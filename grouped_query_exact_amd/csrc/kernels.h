@@ -51,6 +51,30 @@ struct CombineParams {
     int ns, Sq, Hq;
 };
 
+// Backward pass (always PackGQA rows: the G query heads of a KV group).
+struct BwdParams {
+    const uint16_t* q;     // [B, Sq, Hq, D] bf16
+    const uint16_t* k;     // [B, Sk, Hk, D]
+    const uint16_t* v;     // [B, Sk, Hk, D]
+    const uint16_t* o;     // [B, Sq, Hq, D] forward output
+    const uint16_t* dout;  // [B, Sq, Hq, D] upstream gradient
+    const float* lse;      // [B, Hq, Sq] forward log-sum-exp (natural log)
+    float* drow;           // [B, Hq, Sq] workspace: D = rowsum(dO * O)
+    uint16_t* dq;          // [B, Sq, Hq, D]
+    uint16_t* dk;          // [B, Sk, Hk, D]
+    uint16_t* dv;          // [B, Sk, Hk, D]
+    int B, Sq, Sk, Hq, Hk, G;
+    uint32_t gmul, gshift; // magic divisor of G
+    int R;                 // packed rows per KV group: Sq * G
+    int row_tiles;         // dQ kernel: ceil(R / kBlockM)
+    int key_blocks;        // dK/dV kernel: ceil(Sk / kBwdKeys)
+    int grid_dq, grid_dkdv;
+    float c;               // scale * log2(e), with the sign of scale
+    float scale;
+};
+
+hipError_t launch_backward(const BwdParams& p, int d, bool causal, hipStream_t stream);
+
 hipError_t launch_attention(const FwdParams& p, int d, bool causal, bool split, bool varlen, hipStream_t stream);
 hipError_t launch_decode(const FwdParams& p, int d, bool causal, bool split, bool paged, bool kv8, bool varlen,
                          hipStream_t stream);

@@ -86,6 +86,29 @@ int gqa_attn_fwd(const void* q, const void* k, const void* v, void* out, float* 
                  int causal, float scale, int pack_gqa, int num_splits,
                  hipStream_t stream);
 
+/* Backward pass: gradients of the forward pass for an upstream gradient dout.
+ *
+ * The pages time the forward and backward passes of flash attention
+ * together (batch-sensitivity article, "performance analysis"); the
+ * gradients follow from the forward definition by the chain rule. With
+ * P = softmax(scale * Q K^T) over the visible keys (recomputed from q, k and
+ * the forward's lse), O = out and dO = dout, for query head h of KV head g:
+ *   dV_g = sum_{h in g} P^T dO,  dK_g = scale * sum_{h in g} dS^T Q_h,
+ *   dQ_h = scale * dS K_g,  dS = P * (dO V^T - D),  D_i = sum_c dO[i,c] O[i,c].
+ * The query heads of a group share K and V, so their contributions add up.
+ *   q, out, dout, dq : [B, Sq, Hq, d] bf16;  k, v, dk, dv : [B, Sk, Hk, d] bf16
+ *   lse              : [B, Hq, Sq] fp32, the forward's log-sum-exp (required)
+ *   causal, scale    : as passed to the forward call
+ * out and lse must come from gqa_attn_fwd on the same inputs. The library
+ * allocates a stream-ordered fp32 workspace of B*Hq*Sq values for D. dq, dk
+ * and dv are overwritten (keys no query sees get 0). Same validation,
+ * alignment and stream rules as gqa_attn_fwd; additionally Sq*Hq*d*2 must
+ * be below 2^31. */
+int gqa_attn_bwd(const void* q, const void* k, const void* v, const void* out, const float* lse,
+                 const void* dout, void* dq, void* dk, void* dv,
+                 int B, int Sq, int Sk, int Hq, int Hk, int d, int causal, float scale,
+                 hipStream_t stream);
+
 /* Forward pass over a batch of sequences of different lengths, packed along
  * the token axis.
  *

@@ -33,7 +33,7 @@ def lib():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    assert names == ["gqa_attn_choose", "gqa_attn_fwd", "gqa_attn_fwd_kv8", "gqa_attn_fwd_paged",
+    assert names == ["gqa_attn_bwd", "gqa_attn_choose", "gqa_attn_fwd", "gqa_attn_fwd_kv8", "gqa_attn_fwd_paged",
                      "gqa_attn_fwd_paged_kv8", "gqa_attn_fwd_varlen", "gqa_attn_plan", "gqa_attn_strerror"]
 
 
@@ -154,6 +154,28 @@ def test_varlen_argument_checks(kw, status):
     st = lib().gqa_attn_fwd_varlen(P(a["q"]), P(a["k"]), P(a["v"]), P(a["out"]), P(a["lse"]), P(a["cq"]), P(a["ck"]),
                                    a["B"], a["msq"], a["msk"], a["total_q"], a["total_k"], a["Hq"], a["Hk"], a["d"],
                                    a["causal"], a["scale"], a["pack"], a["ns"], None)
+    assert st == getattr(g, "GQA_ERR_" + status), (kw, st)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Hq=6, Hk=4), "INVALID_ARG"),
+    (dict(Sk=0), "INVALID_ARG"),
+    (dict(lse=None), "INVALID_ARG"),
+    (dict(dq=None), "INVALID_ARG"),
+    (dict(scale=float("inf")), "INVALID_ARG"),
+    (dict(d=96), "UNSUPPORTED"),
+    (dict(lse=1.0005), "UNSUPPORTED"),
+    (dict(dk=1.0005), "UNSUPPORTED"),
+])
+def test_backward_argument_checks(kw, status):
+    import grouped_query_exact_amd as g
+    a = dict(q=1, k=1, v=1, out=1, lse=1, do=1, dq=1, dk=1, dv=1, B=1, Sq=8, Sk=8, Hq=4, Hk=2, d=64, causal=1,
+             scale=0.125)
+    a.update(kw)
+    P = lambda x: None if x is None else ctypes.c_void_p(int(x * 4096))
+    st = lib().gqa_attn_bwd(P(a["q"]), P(a["k"]), P(a["v"]), P(a["out"]), P(a["lse"]), P(a["do"]), P(a["dq"]),
+                            P(a["dk"]), P(a["dv"]), a["B"], a["Sq"], a["Sk"], a["Hq"], a["Hk"], a["d"], a["causal"],
+                            a["scale"], None)
     assert st == getattr(g, "GQA_ERR_" + status), (kw, st)
 
 
