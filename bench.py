@@ -249,6 +249,19 @@ def main():
                                                    "tokens": tot}
         print(f"[bench] varlen prefill: {msv:.4f} ms", file=sys.stderr, flush=True)
         del qv, kv_, vv, ov, lv
+        # backward at the Llama-2 prefill shape (B=4, causal): dQ, dK, dV from the forward's O and LSE
+        ql, kl, vl = gpu_randn_inputs(wl, dev, 12)
+        dol = torch.randn_like(ql, dtype=torch.float32).to(torch.bfloat16)
+        ol = torch.empty_like(ql)
+        ll = torch.empty((wl.B, wl.Hq, wl.Sq), dtype=torch.float32, device=dev)
+        g.gqa_attn_fwd(ql, kl, vl, ol, ll, wl.causal, wl.scale)
+        dql, dkl, dvl = torch.empty_like(ql), torch.empty_like(kl), torch.empty_like(vl)
+        msbw, _ = time_calls(lambda: g.gqa_attn_bwd(ql, kl, vl, ol, ll, dol, dql, dkl, dvl, wl.causal, wl.scale),
+                             args.steps, 5)
+        extra["backward_llama_b4"] = {"ms": round(msbw, 4), "tflops": round(2.5 * wl.flops / (msbw * 1e-3) / 1e12, 1),
+                                      "flops_convention": "2.5x forward (5 products of the causal band)"}
+        print(f"[bench] backward llama b4: {msbw:.4f} ms", file=sys.stderr, flush=True)
+        del ql, kl, vl, dol, ol, ll, dql, dkl, dvl
         # split-KV decode
         wd = gi.DECODE
         qd, kd, vd = gpu_randn_inputs(wd, dev, 9)
