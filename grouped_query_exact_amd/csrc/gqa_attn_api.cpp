@@ -312,12 +312,14 @@ int gqa_attn_bwd(const void* q, const void* k, const void* v, const void* out, c
         const int dev = current_device();
         keep_pool(dev);
         void* ws = nullptr;
-        const size_t ws_bytes = (size_t)B * Hq * (size_t)(Sq > 0 ? Sq : 1) * 4;
+        const size_t rows = (size_t)B * Hq * (size_t)(Sq > 0 ? Sq : 1);
+        const size_t ws_bytes = 2 * rows * 4;  // D, then -LSE*log2(e)
         if (hipMallocAsync(&ws, ws_bytes, stream) != hipSuccess || !ws) {
             (void)hipGetLastError();
             return GQA_ERR_NOMEM;
         }
         p.drow = (float*)ws;
+        p.nlse2 = (float*)ws + rows;
         const hipError_t e = gqa::launch_backward(p, d, causal != 0, stream);
         const hipError_t ef = hipFreeAsync(ws, stream);
         if (e != hipSuccess || ef != hipSuccess) return GQA_ERR_HIP;

@@ -13,21 +13,24 @@
 //
 // Three kernels, all on PackGQA rows (row r of a KV group is token r / G,
 // query head g*G + r % G):
-//  * bwd_dot_kernel: D for every row (memory-bound).
+//  * bwd_dot_kernel: D and -LSE*log2(e) for every row (memory-bound).
 //  * bwd_dq_kernel: the forward kernel's tiling (128 rows, 64-key tiles
 //    through a double-buffered LDS ring): S^T = K Q^T and dP^T = V dO^T with
 //    Q and dO rows in registers, dS in registers as the B operand of
 //    dQ^T += K^T dS^T, K^T read with the transposing LDS read.
-//  * bwd_dkdv_kernel: 128 keys per workgroup, 32 per wavefront with its K and
-//    V rows in registers; the workgroup streams every query tile (32 packed
-//    rows of Q and dO) of the KV group through LDS, so dK and dV collect all
-//    G heads without atomics. S = Q K^T and dP = dO V^T come out of the
-//    matrix cores with one key per lane, which is already the A-operand
-//    layout of dV += P^T dO and dK += dS^T Q; dO and Q enter those products
-//    through the transposing LDS read, with their rows read in the order the
-//    score registers hold them.
+//  * bwd_dkdv_kernel: 128 keys per workgroup of eight wavefronts, four for
+//    dK and four for dV, 32 keys each with their K (and V) rows in
+//    registers; the workgroup streams every query tile (32 packed rows of Q
+//    and dO) of the KV group through a ring of LDS stages, so dK and dV
+//    collect all G heads without atomics. S = Q K^T and dP = dO V^T come out
+//    of the matrix cores with one key per lane, which is already the
+//    A-operand layout of dV += P^T dO and dK += dS^T Q; dO and Q enter those
+//    products through the transposing LDS read, with their rows read in the
+//    order the score registers hold them.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "device_common.h"
 #include "kernels.h"
@@ -71,7 +74,9 @@ __global__ __launch_bounds__(256) void bwd_dot_kernel(const BwdParams p) {
     }
     const int64_t h = row % p.Hq, bi = row / p.Hq;
     const int64_t i = bi % p.Sq, bb = bi / p.Sq;
-    p.drow[(bb * p.Hq + h) * p.Sq + i] = acc;
+    const int64_t lrow = (bb * p.Hq + h) * p.Sq + i;
+    p.drow[lrow] = acc;
+    p.nlse2[lrow] = -lse2_of(p.lse[lrow]);
 }
 
 // ---------------------------------------------------------------- dQ
@@ -261,18 +266,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 }
 
 // ---------------------------------------------------------------- dK, dV
-// d=128 keeps 4 x 32 (K, V, dK, dV) + 64 VGPRs of operands live per lane:
-// one wavefront per SIMD (512 VGPRs); d=64 fits two.
+// Eight wavefronts over 128 keys: waves 0-3 accumulate dK, waves 4-7 dV, for
+// the same 32 keys each (wave w and w+4 share a SIMD). Both recompute S; a
+// dK wave also forms dP and dS. Split this way a wave holds one 32 x d
+// accumulator (not two), which leaves room for two wavefronts per SIMD. The
+// two kinds run separate copies of the tile loop (same barriers), so neither
+// accumulator is ever moved between registers.
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 128 ? 1 : 2, D == 128 ? 1 : 2)))
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dkdv_kernel(const BwdParams p) {
-    constexpr int BM = kBwdRows;                 // packed query rows per tile
-    constexpr int NCH = D / 8;                   // 16-byte chunks per row
-    constexpr int TILE_B = BM * D * 2;           // bytes of a Q or dO tile
-    constexpr int NLOAD = BM * NCH / kThreads;   // 16-byte copies per thread per tensor and tile
-    static_assert(NLOAD >= 1, "tile too small for the workgroup");
-    constexpr int STAGE_B = 2 * TILE_B + 2 * 64 * 4;  // Q, dO, 64 LSE and 64 D slots
-    __shared__ __attribute__((aligned(16))) char smem_raw[2 * STAGE_B];
+    constexpr int BM = kBwdRows;                      // packed query rows per tile
+    constexpr int NCH = D / 8;                        // 16-byte chunks per row
+    constexpr int TILE_B = BM * D * 2;                // bytes of a Q or dO tile
+    constexpr int NCOPY = 2 * BM * NCH / kBwdThreads; // 16-byte copies per thread and tile (Q and dO)
+    static_assert(NCOPY >= 1 && (BM * NCH) % 64 == 0, "a wave's copies stay inside one tensor");
+    constexpr int STAGE_B = 2 * TILE_B + 2 * 64 * 4;  // Q, dO, 64 -LSE*log2(e) and 64 D slots
+    constexpr int STAGES = kBwdStages;
+    static_assert(STAGES >= 2, "ring of at least two stages");
+    // copies per wave and tile: its Q / dO chunks, plus the LSE / D row for waves 0 and 1
+    constexpr int COPIES_LO = NCOPY + 1, COPIES_HI = NCOPY;
+    static_assert(COPIES_LO * (STAGES - 2) < 64, "vmcnt is a 6-bit field");
+    __shared__ __attribute__((aligned(16))) char smem_raw[STAGES * STAGE_B];
     LDS char* lds = (LDS char*)smem_raw;
 
     const int tid = threadIdx.x;
@@ -286,21 +300,10 @@ void bwd_dkdv_kernel(const BwdParams p) {
     const int g = tmp % p.Hk;
     const int b = tmp / p.Hk;
     const int k0 = kb * kBwdKeys;
-    const int kw0 = k0 + wave * 32;                  // this wave's keys kw0 .. kw0+31
+    const int kw0 = k0 + (wave & 3) * 32;            // this wave's keys kw0 .. kw0+31
     const int key = kw0 + col;                       // this lane's key (column of S)
     const int keyc = min(key, p.Sk - 1);
     const int koff = p.Sk - p.Sq;
-
-    // K and V rows of this wave's keys -> registers (B operands of S = Q K^T, dP = dO V^T)
-    bf16x8 kreg[D / 16], vreg[D / 16];
-    {
-        const int64_t krow = ((int64_t)b * p.Sk + keyc) * p.Hk + g;
-#pragma unroll
-        for (int dc = 0; dc < D / 16; ++dc) {
-            kreg[dc] = __builtin_bit_cast(bf16x8, *(const u32x4*)(p.k + krow * D + dc * 16 + half * 8));
-            vreg[dc] = __builtin_bit_cast(bf16x8, *(const u32x4*)(p.v + krow * D + dc * 16 + half * 8));
-        }
-    }
 
     // query tiles: from the first row whose token sees key k0 (causal) to the end
     int tile_begin = 0;
@@ -308,31 +311,59 @@ void bwd_dkdv_kernel(const BwdParams p) {
     const int tile_end = (p.R + BM - 1) / BM;
     const int n = max(0, tile_end - tile_begin);
 
-    // tile copies: packed row -> (token, head) -> [B, Sq, Hq, D] offset
+    // Tile copies: packed row -> (token, head) -> [B, Sq, Hq, D] offset. The
+    // Q and dO chunks of a tile are numbered 0 .. 2*BM*NCH-1 (Q first) and
+    // chunk cc lands at byte 16*cc of the stage; a wave's 64 chunks belong to
+    // one tensor. Wave 0 copies the rows' -LSE*log2(e), wave 1 their D
+    // (lanes 32..63 repeat rows 0..31).
     const char* qb = (const char*)(p.q + (int64_t)b * p.Sq * p.Hq * D);
     const char* ob = (const char*)(p.dout + (int64_t)b * p.Sq * p.Hq * D);
-    const char* lb = (const char*)(p.lse + (int64_t)b * p.Hq * p.Sq);
-    const char* db = (const char*)(p.drow + (int64_t)b * p.Hq * p.Sq);
+    const char* lb = (const char*)(wave == 0 ? p.nlse2 : p.drow) + (int64_t)b * p.Hq * p.Sq * 4;
+    auto chunk_offset = [&](int r0, int u, int& cw) {  // byte offset of this lane's chunk u of tile rows r0..
+        cw = (u * (kBwdThreads / 64) + wave) * 64;
+        const int ci = cw - (cw >= BM * NCH ? BM * NCH : 0) + lane;
+        const int row = ci / NCH;
+        const int rr = min(r0 + row, p.R - 1);
+        const int tok = (int)fdiv((uint32_t)rr, p.gmul, p.gshift);
+        const int head = g * p.G + (rr - tok * p.G);
+        return (uint32_t)((((int64_t)tok * p.Hq + head) * D + (((ci % NCH) ^ swz<D>(row)) * 8)) * 2);
+    };
+    auto row_offset = [&](int r0) {
+        const int rr = min(r0 + (lane & 31), p.R - 1);
+        const int tok = (int)fdiv((uint32_t)rr, p.gmul, p.gshift);
+        const int head = g * p.G + (rr - tok * p.G);
+        return (uint32_t)(((int64_t)head * p.Sq + tok) * 4);
+    };
+    // When G divides the tile height, tile t holds the rows of tile 0 moved by
+    // t*BM/G tokens: its copies use tile 0's offsets and a scalar base step.
+    const bool shifted = (BM % p.G) == 0;
+    const int64_t qstep = shifted ? (int64_t)(BM / p.G) * p.Hq * D * 2 : 0;
+    const int64_t lstep = shifted ? (int64_t)(BM / p.G) * 4 : 0;
+    uint32_t off0[NCOPY];
+#pragma unroll
+    for (int u = 0; u < NCOPY; ++u) {
+        int cw;
+        off0[u] = chunk_offset(0, u, cw);
+    }
+    const uint32_t loff0 = row_offset(0);
     auto issue = [&](int tile, int stage) {
         LDS char* st = lds + stage * STAGE_B;
         const int r0 = tile * BM;
+        if (shifted && r0 + BM <= p.R) {
 #pragma unroll
-        for (int u = 0; u < NLOAD; ++u) {
-            const int ci = (u * 4 + wave) * 64 + lane;
-            const int row = ci / NCH;
-            const int rr = min(r0 + row, p.R - 1);
-            const int tok = (int)fdiv((uint32_t)rr, p.gmul, p.gshift);
-            const int head = g * p.G + (rr - tok * p.G);
-            const uint32_t off = (uint32_t)((((int64_t)tok * p.Hq + head) * D + (((ci % NCH) ^ swz<D>(row)) * 8)) * 2);
-            lds_dma16(qb, off, st + (u * 4 + wave) * 1024);
-            lds_dma16(ob, off, st + TILE_B + (u * 4 + wave) * 1024);
-        }
-        if (wave < 2) {  // wave 0: LSE, wave 1: D of the tile's rows (lanes 32..63 repeat rows 0..31)
-            const int rr = min(r0 + (lane & 31), p.R - 1);
-            const int tok = (int)fdiv((uint32_t)rr, p.gmul, p.gshift);
-            const int head = g * p.G + (rr - tok * p.G);
-            const uint32_t off = (uint32_t)(((int64_t)head * p.Sq + tok) * 4);
-            lds_dma4(wave == 0 ? lb : db, off, st + 2 * TILE_B + wave * 256);
+            for (int u = 0; u < NCOPY; ++u) {
+                const int cw = (u * (kBwdThreads / 64) + wave) * 64;
+                lds_dma16((cw >= BM * NCH ? ob : qb) + tile * qstep, off0[u], st + cw * 16);
+            }
+            if (wave < 2) lds_dma4(lb + tile * lstep, loff0, st + 2 * TILE_B + wave * 256);
+        } else {  // G does not divide the tile, or the ragged last tile (rows clamped)
+#pragma unroll
+            for (int u = 0; u < NCOPY; ++u) {
+                int cw;
+                const uint32_t off = chunk_offset(r0, u, cw);
+                lds_dma16(cw >= BM * NCH ? ob : qb, off, st + cw * 16);
+            }
+            if (wave < 2) lds_dma4(lb, row_offset(r0), st + 2 * TILE_B + wave * 256);
         }
     };
 
@@ -355,96 +386,147 @@ void bwd_dkdv_kernel(const BwdParams p) {
             const int bcol = cb * 32 + qq * 16 + (u16 & 3) * 4;
             bofs[cb][rr] = brow * (D * 2) + (((bcol >> 3) ^ swz<D>(brow)) * 16) + (bcol & 7) * 2;
         }
-
-    f32x16 dkacc[D / 32], dvacc[D / 32];
-#pragma unroll
-    for (int cb = 0; cb < D / 32; ++cb) {
-        dkacc[cb] = f32x16{};
-        dvacc[cb] = f32x16{};
-    }
     const float c = p.c;
 
-    // score register i of this lane: tile row m_i = 8*(i/4) + 4*half + (i%4), key `key`
-    auto compute = [&](int stage, int r0, bool need_mask) {
-        const LDS char* qt = lds + stage * STAGE_B;
-        const LDS char* ot = qt + TILE_B;
-        const LDS float* lt = (const LDS float*)(qt + 2 * TILE_B);
-        const LDS float* dt = lt + 64;
-        f32x16 s = f32x16{}, dp = f32x16{};
-#pragma unroll
-        for (int dc = 0; dc < D / 16; ++dc) {
-            const bf16x8 aq = *(const LDS bf16x8*)(qt + aofs[dc]);
-            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kreg[dc], s, 0, 0, 0);
-            const bf16x8 ao = *(const LDS bf16x8*)(ot + aofs[dc]);
-            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, vreg[dc], dp, 0, 0, 0);
-        }
-        bf16x8 pa[2], da[2];
+    // P of this lane's 16 scores: score register i holds tile row
+    // m_i = 8*(i/4) + 4*half + (i%4) and key `key`; lt holds -LSE*log2(e).
+    auto probs = [&](const f32x16& s, const LDS float* lt, int r0, bool need_mask, float* pv) {
+        float x[16];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int m0 = 8 * j + 4 * half;
-            const f32x4 l4 = *(const LDS f32x4*)(lt + m0);
-            const f32x4 d4 = *(const LDS f32x4*)(dt + m0);
+            const f32x4 l4 = *(const LDS f32x4*)(lt + 8 * j + 4 * half);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int i = 4 * j + e;
-                float x = __builtin_fmaf(s[i], c, -lse2_of(l4[e]));
-                if (need_mask) {
-                    const int rr = r0 + m0 + e;
-                    const int tok = (int)fdiv((uint32_t)min(rr, p.R - 1), p.gmul, p.gshift);
-                    if (rr >= p.R || key >= p.Sk || (CAUSAL && key > tok + koff)) x = -__builtin_inff();
-                }
-                const float pv = __builtin_amdgcn_exp2f(x);
-                pa[i >> 3][i & 7] = (__bf16)pv;
-                da[i >> 3][i & 7] = (__bf16)(pv * (dp[i] - d4[e]));
+            for (int e = 0; e < 4; ++e) x[4 * j + e] = __builtin_fmaf(s[4 * j + e], c, l4[e]);
+        }
+        if (need_mask) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int rr = r0 + 8 * (i >> 2) + 4 * half + (i & 3);
+                const int tok = (int)fdiv((uint32_t)min(rr, p.R - 1), p.gmul, p.gshift);
+                if (rr >= p.R || key >= p.Sk || (CAUSAL && key > tok + koff)) x[i] = -__builtin_inff();
             }
         }
-        // dV += P^T dO, dK += dS^T Q (two 16-row blocks of the tile)
 #pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2) {
+        for (int i = 0; i < 16; ++i) pv[i] = __builtin_amdgcn_exp2f(x[i]);
+    };
+
+    // The tile loop of one kind of wave (DK: dK, else dV).
+    auto run = [&](auto dk_tag) {
+        constexpr bool DK = decltype(dk_tag)::value;
+        // ring: tile j sits in stage j % STAGES; tiles j+1 .. j+STAGES-2 stay
+        // in flight while tile j is computed, and tile j+STAGES-1 is started
+        // into the stage tile j-1 used once every wave has passed the barrier.
 #pragma unroll
-            for (int cb = 0; cb < D / 32; ++cb) {
-                const s16x4 olo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS s16x4*)(ot + bofs[cb][0] + kb2 * 16 * D * 2));
-                const s16x4 ohi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS s16x4*)(ot + bofs[cb][1] + kb2 * 16 * D * 2));
-                const s16x8 bo = __builtin_shufflevector(olo, ohi, 0, 1, 2, 3, 4, 5, 6, 7);
-                dvacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[kb2], __builtin_bit_cast(bf16x8, bo), dvacc[cb], 0, 0, 0);
-                const s16x4 qlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS s16x4*)(qt + bofs[cb][0] + kb2 * 16 * D * 2));
-                const s16x4 qhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS s16x4*)(qt + bofs[cb][1] + kb2 * 16 * D * 2));
-                const s16x8 bq = __builtin_shufflevector(qlo, qhi, 0, 1, 2, 3, 4, 5, 6, 7);
-                dkacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[kb2], __builtin_bit_cast(bf16x8, bq), dkacc[cb], 0, 0, 0);
+        for (int j = 0; j < STAGES - 1; ++j)
+            if (j < n) issue(tile_begin + j, j);
+
+        // K (and V) rows of this wave's keys -> registers (B operands of
+        // S = Q K^T, dP = dO V^T), loaded after the first tiles' copies so
+        // that one latency covers both. The empty asm makes the compiler wait
+        // for these loads here, once, rather than at their first use inside
+        // the loop, where its wait would also drain the copies in flight.
+        constexpr int NV = DK ? D / 16 : 1;
+        bf16x8 kreg[D / 16], vreg[NV];
+        {
+            const int64_t krow = ((int64_t)b * p.Sk + keyc) * p.Hk + g;
+#pragma unroll
+            for (int dc = 0; dc < D / 16; ++dc) {
+                kreg[dc] = __builtin_bit_cast(bf16x8, *(const u32x4*)(p.k + krow * D + dc * 16 + half * 8));
+                if (DK) vreg[dc % NV] = __builtin_bit_cast(bf16x8, *(const u32x4*)(p.v + krow * D + dc * 16 + half * 8));
+            }
+#pragma unroll
+            for (int dc = 0; dc < D / 16; ++dc) asm volatile("" ::"v"(kreg[dc]));
+            if (DK) {
+#pragma unroll
+                for (int dc = 0; dc < NV; ++dc) asm volatile("" ::"v"(vreg[dc]));
+            }
+        }
+
+        f32x16 acc[D / 32];  // dK (unscaled) or dV
+#pragma unroll
+        for (int cb = 0; cb < D / 32; ++cb) acc[cb] = f32x16{};
+
+        int stage = 0, next_stage = STAGES - 1;
+        for (int j = 0; j < n; ++j) {
+            const int t = tile_begin + j;
+            const int r0 = t * BM;
+            if (j + STAGES - 2 < n) {  // copies complete in issue order: leave the later tiles' in flight
+                if (wave < 2) wait_vmem_n<COPIES_LO * (STAGES - 2)>();
+                else wait_vmem_n<COPIES_HI * (STAGES - 2)>();
+            } else {
+                wait_vmem();
+            }
+            __syncthreads();
+            if (j + STAGES - 1 < n) issue(t + STAGES - 1, next_stage);
+            next_stage = next_stage + 1 == STAGES ? 0 : next_stage + 1;
+            // tokens of this tile; a wave computes only if one of its keys is visible
+            const int tok_min = (int)fdiv((uint32_t)r0, p.gmul, p.gshift);
+            const int tok_max = (int)fdiv((uint32_t)(min(r0 + BM, p.R) - 1), p.gmul, p.gshift);
+            if (kw0 < p.Sk && !(CAUSAL && kw0 > tok_max + koff)) {
+                const bool need_mask = (r0 + BM > p.R) || (kw0 + 32 > p.Sk) || (CAUSAL && kw0 + 31 > tok_min + koff);
+                const LDS char* qt = lds + stage * STAGE_B;
+                const LDS char* ot = qt + TILE_B;
+                const LDS float* lt = (const LDS float*)(qt + 2 * TILE_B);
+                f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+                for (int dc = 0; dc < D / 16; ++dc) {
+                    const bf16x8 aq = *(const LDS bf16x8*)(qt + aofs[dc]);
+                    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kreg[dc], s, 0, 0, 0);
+                    if (DK) {
+                        const bf16x8 ao = *(const LDS bf16x8*)(ot + aofs[dc]);
+                        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, vreg[dc % NV], dp, 0, 0, 0);
+                    }
+                }
+                float pv[16];
+                probs(s, lt, r0, need_mask, pv);
+                bf16x8 a[2];  // dK: dS, dV: P (bf16, A operand)
+                if (DK) {
+                    const LDS float* dt = lt + 64;
+#pragma unroll
+                    for (int j4 = 0; j4 < 4; ++j4) {
+                        const f32x4 d4 = *(const LDS f32x4*)(dt + 8 * j4 + 4 * half);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int i = 4 * j4 + e;
+                            a[i >> 3][i & 7] = (__bf16)(pv[i] * (dp[i] - d4[e]));
+                        }
+                    }
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) a[i >> 3][i & 7] = (__bf16)pv[i];
+                }
+                // dK += dS^T Q or dV += P^T dO, X read transposed
+                const LDS char* xt = DK ? qt : ot;
+#pragma unroll
+                for (int kb2 = 0; kb2 < 2; ++kb2) {
+#pragma unroll
+                    for (int cb = 0; cb < D / 32; ++cb) {
+                        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS s16x4*)(xt + bofs[cb][0] + kb2 * 16 * D * 2));
+                        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS s16x4*)(xt + bofs[cb][1] + kb2 * 16 * D * 2));
+                        const s16x8 bx = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                        acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kb2], __builtin_bit_cast(bf16x8, bx), acc[cb], 0, 0, 0);
+                    }
+                }
+            }
+            stage = stage + 1 == STAGES ? 0 : stage + 1;
+        }
+
+        // dK = scale * acc, dV = acc: lane holds column 32*cb + col of keys kw0 + 8*(i/4) + 4*half + (i%4)
+        const float sc = DK ? p.scale : 1.0f;
+        uint16_t* dst = DK ? p.dk : p.dv;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int kk = kw0 + 8 * (i >> 2) + 4 * half + (i & 3);
+            if (kk < p.Sk) {
+                const int64_t krow = (((int64_t)b * p.Sk + kk) * p.Hk + g) * D;
+#pragma unroll
+                for (int cb = 0; cb < D / 32; ++cb)
+                    dst[krow + cb * 32 + col] = __builtin_bit_cast(uint16_t, (__bf16)(acc[cb][i] * sc));
             }
         }
     };
-
-    if (n > 0) issue(tile_begin, 0);
-    for (int j = 0; j < n; ++j) {
-        const int t = tile_begin + j;
-        const int r0 = t * BM;
-        wait_vmem();
-        __syncthreads();
-        if (j + 1 < n) issue(t + 1, (j + 1) & 1);
-        // tokens of this tile; a wave computes only if one of its keys is visible
-        const int tok_min = (int)fdiv((uint32_t)r0, p.gmul, p.gshift);
-        const int tok_max = (int)fdiv((uint32_t)(min(r0 + BM, p.R) - 1), p.gmul, p.gshift);
-        if (kw0 < p.Sk && !(CAUSAL && kw0 > tok_max + koff)) {
-            const bool need_mask = (r0 + BM > p.R) || (kw0 + 32 > p.Sk) || (CAUSAL && kw0 + 31 > tok_min + koff);
-            compute(j & 1, r0, need_mask);
-        }
-    }
-
-    // dK = scale * acc, dV = acc: lane holds column 32*cb + col of keys kw0 + 8*(i/4) + 4*half + (i%4)
-    const float sc = p.scale;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const int kk = kw0 + 8 * (i >> 2) + 4 * half + (i & 3);
-        if (kk < p.Sk) {
-            const int64_t krow = (((int64_t)b * p.Sk + kk) * p.Hk + g) * D;
-#pragma unroll
-            for (int cb = 0; cb < D / 32; ++cb) {
-                p.dk[krow + cb * 32 + col] = __builtin_bit_cast(uint16_t, (__bf16)(dkacc[cb][i] * sc));
-                p.dv[krow + cb * 32 + col] = __builtin_bit_cast(uint16_t, (__bf16)dvacc[cb][i]);
-            }
-        }
-    }
+    if (wave < 4) run(std::true_type{});
+    else run(std::false_type{});
 }
 
 // ---------------------------------------------------------------- launcher
@@ -462,7 +544,7 @@ static hipError_t launch_bwd_d(const BwdParams& p, hipStream_t stream) {
         if (e != hipSuccess) return e;
     }
     if (p.grid_dkdv > 0)
-        hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3(p.grid_dkdv), dim3(kThreads), 0, stream, p);
+        hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3(p.grid_dkdv), dim3(kBwdThreads), 0, stream, p);
     return hipGetLastError();
 }
 

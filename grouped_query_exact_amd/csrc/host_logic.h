@@ -25,10 +25,15 @@ constexpr int kDecStages = 4;
 // workgroup) lets four workgroups share a compute unit instead.
 constexpr int kDecStagesKV8 = 3;
 
-// Backward pass: the dK/dV kernel takes 128 keys per workgroup (32 per
-// wavefront) against query tiles of 32 packed rows.
+// Backward pass: the dK/dV kernel takes 128 keys per workgroup of
+// kBwdThreads (32 keys per wavefront, one wavefront for dK and one for dV)
+// against query tiles of 32 packed rows, streamed through a ring of
+// kBwdStages LDS stages (kBwdStages - 2 tiles in flight while one is
+// computed).
 constexpr int kBwdKeys = 128;
 constexpr int kBwdRows = 32;
+constexpr int kBwdThreads = 512;
+constexpr int kBwdStages = 4;
 
 // Division by a runtime constant through a precomputed multiplier (the
 // batch-sensitivity article, "PackGQA" mechanism 3, precomputes the

@@ -60,6 +60,7 @@ struct BwdParams {
     const uint16_t* dout;  // [B, Sq, Hq, D] upstream gradient
     const float* lse;      // [B, Hq, Sq] forward log-sum-exp (natural log)
     float* drow;           // [B, Hq, Sq] workspace: D = rowsum(dO * O)
+    float* nlse2;          // [B, Hq, Sq] workspace: -LSE * log2(e), -inf for rows without keys
     uint16_t* dq;          // [B, Sq, Hq, D]
     uint16_t* dk;          // [B, Sk, Hk, D]
     uint16_t* dv;          // [B, Sk, Hk, D]

@@ -100,7 +100,8 @@ int gqa_attn_fwd(const void* q, const void* k, const void* v, void* out, float* 
  *   lse              : [B, Hq, Sq] fp32, the forward's log-sum-exp (required)
  *   causal, scale    : as passed to the forward call
  * out and lse must come from gqa_attn_fwd on the same inputs. The library
- * allocates a stream-ordered fp32 workspace of B*Hq*Sq values for D. dq, dk
+ * allocates a stream-ordered fp32 workspace of 2*B*Hq*Sq values (D and the
+ * log-sum-exp in base 2). dq, dk
  * and dv are overwritten (keys no query sees get 0). Same validation,
  * alignment and stream rules as gqa_attn_fwd; additionally Sq*Hq*d*2 must
  * be below 2^31. */
