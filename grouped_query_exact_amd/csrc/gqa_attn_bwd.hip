@@ -266,12 +266,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 }
 
 // ---------------------------------------------------------------- dK, dV
-// Eight wavefronts over 128 keys: waves 0-3 accumulate dK, waves 4-7 dV, for
-// the same 32 keys each (wave w and w+4 share a SIMD). Both recompute S; a
-// dK wave also forms dP and dS. Split this way a wave holds one 32 x d
-// accumulator (not two), which leaves room for two wavefronts per SIMD. The
-// two kinds run separate copies of the tile loop (same barriers), so neither
-// accumulator is ever moved between registers.
+// Eight wavefronts over 128 keys, 32 keys per pair of wavefronts w and w+4
+// (which share a SIMD): wave w+4 computes S = Q K^T and P for query tile j,
+// adds P^T dO to dV and hands P (fp32) to wave w through LDS; one tile later
+// wave w forms dP = dO V^T, dS = P (dP - D) and adds dS^T Q to dK. Each wave
+// issues 16 matrix products per tile, holds one accumulator, and has room
+// for the second wavefront on its SIMD to hide its latencies. The two kinds
+// run separate copies of the tile loop with the same barriers.
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dkdv_kernel(const BwdParams p) {
@@ -282,11 +283,12 @@ void bwd_dkdv_kernel(const BwdParams p) {
     static_assert(NCOPY >= 1 && (BM * NCH) % 64 == 0, "a wave's copies stay inside one tensor");
     constexpr int STAGE_B = 2 * TILE_B + 2 * 64 * 4;  // Q, dO, 64 -LSE*log2(e) and 64 D slots
     constexpr int STAGES = kBwdStages;
-    static_assert(STAGES >= 2, "ring of at least two stages");
+    static_assert(STAGES >= 3, "tiles j-1 and j are in use while j+STAGES-2 is copied");
+    constexpr int PB = 4 * 16 * 64 * 4;               // P of one tile for the four pairs (fp32)
     // copies per wave and tile: its Q / dO chunks, plus the LSE / D row for waves 0 and 1
     constexpr int COPIES_LO = NCOPY + 1, COPIES_HI = NCOPY;
-    static_assert(COPIES_LO * (STAGES - 2) < 64, "vmcnt is a 6-bit field");
-    __shared__ __attribute__((aligned(16))) char smem_raw[STAGES * STAGE_B];
+    static_assert(COPIES_LO * (STAGES - 3) < 64, "vmcnt is a 6-bit field");
+    __shared__ __attribute__((aligned(16))) char smem_raw[STAGES * STAGE_B + 2 * PB];
     LDS char* lds = (LDS char*)smem_raw;
 
     const int tid = threadIdx.x;
@@ -300,7 +302,8 @@ void bwd_dkdv_kernel(const BwdParams p) {
     const int g = tmp % p.Hk;
     const int b = tmp / p.Hk;
     const int k0 = kb * kBwdKeys;
-    const int kw0 = k0 + (wave & 3) * 32;            // this wave's keys kw0 .. kw0+31
+    const int pair = wave & 3;
+    const int kw0 = k0 + pair * 32;                  // this pair's keys kw0 .. kw0+31
     const int key = kw0 + col;                       // this lane's key (column of S)
     const int keyc = min(key, p.Sk - 1);
     const int koff = p.Sk - p.Sq;
@@ -386,129 +389,121 @@ void bwd_dkdv_kernel(const BwdParams p) {
             const int bcol = cb * 32 + qq * 16 + (u16 & 3) * 4;
             bofs[cb][rr] = brow * (D * 2) + (((bcol >> 3) ^ swz<D>(brow)) * 16) + (bcol & 7) * 2;
         }
+    // P hand-over: 16 fp32 per lane, slot k (registers 4k .. 4k+3) of lane l at
+    // 1024*k + 16*l of the pair's 4 KiB, two tiles' worth (by tile parity)
+    LDS char* pslot = lds + STAGES * STAGE_B + pair * 4096 + lane * 16;
     const float c = p.c;
 
-    // P of this lane's 16 scores: score register i holds tile row
-    // m_i = 8*(i/4) + 4*half + (i%4) and key `key`; lt holds -LSE*log2(e).
-    auto probs = [&](const f32x16& s, const LDS float* lt, int r0, bool need_mask, float* pv) {
-        float x[16];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const f32x4 l4 = *(const LDS f32x4*)(lt + 8 * j + 4 * half);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) x[4 * j + e] = __builtin_fmaf(s[4 * j + e], c, l4[e]);
-        }
-        if (need_mask) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int rr = r0 + 8 * (i >> 2) + 4 * half + (i & 3);
-                const int tok = (int)fdiv((uint32_t)min(rr, p.R - 1), p.gmul, p.gshift);
-                if (rr >= p.R || key >= p.Sk || (CAUSAL && key > tok + koff)) x[i] = -__builtin_inff();
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < 16; ++i) pv[i] = __builtin_amdgcn_exp2f(x[i]);
-    };
-
-    // The tile loop of one kind of wave (DK: dK, else dV).
+    // The tile loop of one kind of wave (DK: dK, else dV). Iteration j: the
+    // dV waves compute tile j, the dK waves tile j-1 (whose P the barrier of
+    // iteration j publishes). Tile j+STAGES-2 is copied into the stage of
+    // tile j-2, which no wave uses after that barrier.
     auto run = [&](auto dk_tag) {
         constexpr bool DK = decltype(dk_tag)::value;
-        // ring: tile j sits in stage j % STAGES; tiles j+1 .. j+STAGES-2 stay
-        // in flight while tile j is computed, and tile j+STAGES-1 is started
-        // into the stage tile j-1 used once every wave has passed the barrier.
 #pragma unroll
-        for (int j = 0; j < STAGES - 1; ++j)
+        for (int j = 0; j < STAGES - 2; ++j)
             if (j < n) issue(tile_begin + j, j);
 
-        // K (and V) rows of this wave's keys -> registers (B operands of
-        // S = Q K^T, dP = dO V^T), loaded after the first tiles' copies so
-        // that one latency covers both. The empty asm makes the compiler wait
-        // for these loads here, once, rather than at their first use inside
-        // the loop, where its wait would also drain the copies in flight.
-        constexpr int NV = DK ? D / 16 : 1;
-        bf16x8 kreg[D / 16], vreg[NV];
+        // K (dV waves) or V (dK waves) rows of the pair's keys -> registers
+        // (B operand of S = Q K^T or dP = dO V^T), loaded after the first
+        // tiles' copies so that one latency covers both. The empty asm makes
+        // the compiler wait for these loads here, once, rather than at their
+        // first use inside the loop, where its wait would also drain the
+        // copies in flight.
+        bf16x8 breg[D / 16];
         {
-            const int64_t krow = ((int64_t)b * p.Sk + keyc) * p.Hk + g;
+            const uint16_t* src = (DK ? p.v : p.k) + (((int64_t)b * p.Sk + keyc) * p.Hk + g) * D;
 #pragma unroll
-            for (int dc = 0; dc < D / 16; ++dc) {
-                kreg[dc] = __builtin_bit_cast(bf16x8, *(const u32x4*)(p.k + krow * D + dc * 16 + half * 8));
-                if (DK) vreg[dc % NV] = __builtin_bit_cast(bf16x8, *(const u32x4*)(p.v + krow * D + dc * 16 + half * 8));
-            }
+            for (int dc = 0; dc < D / 16; ++dc)
+                breg[dc] = __builtin_bit_cast(bf16x8, *(const u32x4*)(src + dc * 16 + half * 8));
 #pragma unroll
-            for (int dc = 0; dc < D / 16; ++dc) asm volatile("" ::"v"(kreg[dc]));
-            if (DK) {
-#pragma unroll
-                for (int dc = 0; dc < NV; ++dc) asm volatile("" ::"v"(vreg[dc]));
-            }
+            for (int dc = 0; dc < D / 16; ++dc) asm volatile("" ::"v"(breg[dc]));
         }
 
         f32x16 acc[D / 32];  // dK (unscaled) or dV
 #pragma unroll
         for (int cb = 0; cb < D / 32; ++cb) acc[cb] = f32x16{};
 
-        int stage = 0, next_stage = STAGES - 1;
-        for (int j = 0; j < n; ++j) {
-            const int t = tile_begin + j;
-            const int r0 = t * BM;
-            if (j + STAGES - 2 < n) {  // copies complete in issue order: leave the later tiles' in flight
-                if (wave < 2) wait_vmem_n<COPIES_LO * (STAGES - 2)>();
-                else wait_vmem_n<COPIES_HI * (STAGES - 2)>();
-            } else {
-                wait_vmem();
+        for (int j = 0; j <= n; ++j) {
+            if (j < n) {  // copies complete in issue order: leave the later tiles' in flight
+                if (j + STAGES - 3 < n) {
+                    if (wave < 2) wait_vmem_n<COPIES_LO * (STAGES - 3)>();
+                    else wait_vmem_n<COPIES_HI * (STAGES - 3)>();
+                } else {
+                    wait_vmem();
+                }
             }
             __syncthreads();
-            if (j + STAGES - 1 < n) issue(t + STAGES - 1, next_stage);
-            next_stage = next_stage + 1 == STAGES ? 0 : next_stage + 1;
-            // tokens of this tile; a wave computes only if one of its keys is visible
+            if (j + STAGES - 2 < n) issue(tile_begin + j + STAGES - 2, (j + STAGES - 2) % STAGES);
+            const int jt = DK ? j - 1 : j;
+            if (jt < 0 || jt >= n) continue;
+            const int r0 = (tile_begin + jt) * BM;
+            // tokens of the tile; a pair computes only if one of its keys is visible
             const int tok_min = (int)fdiv((uint32_t)r0, p.gmul, p.gshift);
             const int tok_max = (int)fdiv((uint32_t)(min(r0 + BM, p.R) - 1), p.gmul, p.gshift);
-            if (kw0 < p.Sk && !(CAUSAL && kw0 > tok_max + koff)) {
+            if (kw0 >= p.Sk || (CAUSAL && kw0 > tok_max + koff)) continue;
+            const LDS char* qt = lds + (jt % STAGES) * STAGE_B;
+            const LDS char* ot = qt + TILE_B;
+            const LDS float* lt = (const LDS float*)(qt + 2 * TILE_B);
+            LDS char* ps = pslot + (jt & 1) * (4 * 4096);
+            // S = Q K^T (dV) or dP = dO V^T (dK); register i holds tile row
+            // m_i = 8*(i/4) + 4*half + (i%4) and key `key`
+            f32x16 s = f32x16{};
+#pragma unroll
+            for (int dc = 0; dc < D / 16; ++dc) {
+                const bf16x8 a = *(const LDS bf16x8*)((DK ? ot : qt) + aofs[dc]);
+                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, breg[dc], s, 0, 0, 0);
+            }
+            bf16x8 a[2];  // dV: P, dK: dS (bf16, A operand)
+            if (!DK) {
                 const bool need_mask = (r0 + BM > p.R) || (kw0 + 32 > p.Sk) || (CAUSAL && kw0 + 31 > tok_min + koff);
-                const LDS char* qt = lds + stage * STAGE_B;
-                const LDS char* ot = qt + TILE_B;
-                const LDS float* lt = (const LDS float*)(qt + 2 * TILE_B);
-                f32x16 s = f32x16{}, dp = f32x16{};
+                float x[16];
 #pragma unroll
-                for (int dc = 0; dc < D / 16; ++dc) {
-                    const bf16x8 aq = *(const LDS bf16x8*)(qt + aofs[dc]);
-                    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kreg[dc], s, 0, 0, 0);
-                    if (DK) {
-                        const bf16x8 ao = *(const LDS bf16x8*)(ot + aofs[dc]);
-                        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, vreg[dc % NV], dp, 0, 0, 0);
+                for (int j4 = 0; j4 < 4; ++j4) {
+                    const f32x4 l4 = *(const LDS f32x4*)(lt + 8 * j4 + 4 * half);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) x[4 * j4 + e] = __builtin_fmaf(s[4 * j4 + e], c, l4[e]);
+                }
+                if (need_mask) {
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int rr = r0 + 8 * (i >> 2) + 4 * half + (i & 3);
+                        const int tok = (int)fdiv((uint32_t)min(rr, p.R - 1), p.gmul, p.gshift);
+                        if (rr >= p.R || key >= p.Sk || (CAUSAL && key > tok + koff)) x[i] = -__builtin_inff();
                     }
                 }
-                float pv[16];
-                probs(s, lt, r0, need_mask, pv);
-                bf16x8 a[2];  // dK: dS, dV: P (bf16, A operand)
-                if (DK) {
-                    const LDS float* dt = lt + 64;
+                f32x4 pv[4];
 #pragma unroll
-                    for (int j4 = 0; j4 < 4; ++j4) {
-                        const f32x4 d4 = *(const LDS f32x4*)(dt + 8 * j4 + 4 * half);
+                for (int i = 0; i < 16; ++i) pv[i >> 2][i & 3] = __builtin_amdgcn_exp2f(x[i]);
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const int i = 4 * j4 + e;
-                            a[i >> 3][i & 7] = (__bf16)(pv[i] * (dp[i] - d4[e]));
-                        }
-                    }
-                } else {
+                for (int k4 = 0; k4 < 4; ++k4) *(LDS f32x4*)(ps + k4 * 1024) = pv[k4];
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) a[i >> 3][i & 7] = (__bf16)pv[i];
-                }
-                // dK += dS^T Q or dV += P^T dO, X read transposed
-                const LDS char* xt = DK ? qt : ot;
+                for (int i = 0; i < 16; ++i) a[i >> 3][i & 7] = (__bf16)pv[i >> 2][i & 3];
+            } else {
+                const LDS float* dt = lt + 64;
 #pragma unroll
-                for (int kb2 = 0; kb2 < 2; ++kb2) {
+                for (int k4 = 0; k4 < 4; ++k4) {
+                    const f32x4 pv = *(const LDS f32x4*)(ps + k4 * 1024);
+                    const f32x4 d4 = *(const LDS f32x4*)(dt + 8 * k4 + 4 * half);
 #pragma unroll
-                    for (int cb = 0; cb < D / 32; ++cb) {
-                        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS s16x4*)(xt + bofs[cb][0] + kb2 * 16 * D * 2));
-                        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS s16x4*)(xt + bofs[cb][1] + kb2 * 16 * D * 2));
-                        const s16x8 bx = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-                        acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kb2], __builtin_bit_cast(bf16x8, bx), acc[cb], 0, 0, 0);
+                    for (int e = 0; e < 4; ++e) {
+                        const int i = 4 * k4 + e;
+                        a[i >> 3][i & 7] = (__bf16)(pv[e] * (s[i] - d4[e]));
                     }
                 }
             }
-            stage = stage + 1 == STAGES ? 0 : stage + 1;
+            // dV += P^T dO or dK += dS^T Q, the second factor read transposed
+            const LDS char* xt = DK ? qt : ot;
+#pragma unroll
+            for (int kb2 = 0; kb2 < 2; ++kb2) {
+#pragma unroll
+                for (int cb = 0; cb < D / 32; ++cb) {
+                    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS s16x4*)(xt + bofs[cb][0] + kb2 * 16 * D * 2));
+                    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS s16x4*)(xt + bofs[cb][1] + kb2 * 16 * D * 2));
+                    const s16x8 bx = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                    acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kb2], __builtin_bit_cast(bf16x8, bx), acc[cb], 0, 0, 0);
+                }
+            }
         }
 
         // dK = scale * acc, dV = acc: lane holds column 32*cb + col of keys kw0 + 8*(i/4) + 4*half + (i%4)
