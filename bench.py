@@ -11,9 +11,10 @@ in HBM before the timed region. The metric is TFLOP/s = 4*B*Hq*Sq*Sk*d/2/t
 Also measured in the same run and reported in the same JSON line (unless
 --quick): the rest of the sweep (B = 16, 64, 128, 256 with (pack 1, ns 1)
 and (pack 0, ns 4)), the Llama-2 prefill shape (B=4), and split-KV decode
-(B=64, Sq=1, Sk=8192) as HBM GB/s of Q+K+V+O+LSE bytes; those inputs are
-drawn on the GPU from N(0,1) (the timing does not depend on the values'
-seeds).
+(B=64, Sq=1, Sk=8192) as HBM GB/s of Q+K+V+O+LSE bytes, the same decode
+over a paged cache and with fp8 K/V, a variable-length prefill batch, and
+the backward pass at the Llama-2 shape; those inputs are drawn on the GPU
+from N(0,1) (the timing does not depend on the values' seeds).
 
 cpu_baseline: the fp64 numpy oracle on a bounded sample (the first batch
 elements of the headline workload, all heads, until >= 10 s of CPU time),
@@ -35,13 +36,18 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
-KERNEL_SRC = os.path.join(ROOT, "grouped_query_exact_amd", "csrc", "gqa_attn_kernels.hip")
+# the forward kernels' sources: the traffic counters are valid while these are unchanged
+KERNEL_SRCS = [os.path.join(ROOT, "grouped_query_exact_amd", "csrc", f)
+               for f in ("gqa_attn_kernels.hip", "device_common.h", "kernels.h", "host_logic.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
 def kernel_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def time_calls(fn, steps: int, warmup: int):

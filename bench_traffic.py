@@ -15,7 +15,13 @@ into <out-dir>/profiles/ (to be copied into profiles/):
     ratio), keyed by a hash of the kernel source so bench.py drops the figure
     once the kernel changes;
   * attn_fwd_<workload>.md: the trace and counter summary with the
-    commands that produced it.
+    commands that produced it;
+  * attn_fwd_sweep_b128_s2048_bench.md: a ``--kernel-trace --stats`` pass
+    over the headline measurement itself (``bench.py --quick`` with its
+    default steps and warm-up), whose average kernel time is the one
+    bench.py reports;
+  * attn_bwd_llama2_prefill_b4_s2048.md: trace and counters of the
+    backward kernels at the Llama-2 prefill shape (``--run-bwd``).
 
 It never touches the GPU itself; the profiled children do.
 """
@@ -35,10 +41,13 @@ import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
-KERNEL_SRC = os.path.join(ROOT, "grouped_query_exact_amd", "csrc", "gqa_attn_kernels.hip")
+# the forward kernels' sources: the traffic counters are valid while these are unchanged
+KERNEL_SRCS = [os.path.join(ROOT, "grouped_query_exact_amd", "csrc", f)
+               for f in ("gqa_attn_kernels.hip", "device_common.h", "kernels.h", "host_logic.h")]
 PROFILES = os.path.join(ROOT, "profiles")
 COPY_BYTES = 1 << 30
 KERNEL_NAMES = ("attn_fwd_kernel", "attn_decode_kernel", "combine_kernel")
+BWD_KERNEL_NAMES = ("bwd_dot_kernel", "bwd_dq_kernel", "bwd_dkdv_kernel")
 RUN_LAUNCHES = 4
 
 # name -> (workload factory, pack_gqa, num_splits); -1 / 0 = the library's choice
@@ -51,8 +60,11 @@ WORKLOADS = {
 
 
 def kernel_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def workload(name):
@@ -80,6 +92,27 @@ def run_workload(name):
     print(json.dumps({"workload": name, "launches": RUN_LAUNCHES, "plan": plan}), flush=True)
 
 
+def run_backward():
+    """Forward once, then RUN_LAUNCHES backward calls at the Llama-2 prefill shape (B=4, causal)."""
+    import torch
+    import grouped_query_exact_amd as g
+    import gqa_inputs as gi
+    w = gi.LLAMA_PREFILL
+    dev = torch.device("cuda:0")
+    q, k, v = gi.make_qkv_device(w, dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(w.seed + 17)
+    do = torch.randn(q.shape, generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    out = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.Sq), dtype=torch.float32, device=dev)
+    g.gqa_attn_fwd(q, k, v, out, lse, w.causal, w.scale)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    for _ in range(RUN_LAUNCHES):
+        g.gqa_attn_bwd(q, k, v, out, lse, do, dq, dk, dv, w.causal, w.scale)
+    torch.cuda.synchronize()
+    print(json.dumps({"workload": "backward " + w.name, "launches": RUN_LAUNCHES}), flush=True)
+
+
 def run_copy():
     import torch
     a = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda:0")
@@ -92,9 +125,9 @@ def run_copy():
 
 
 # --------------------------------------------------------------- orchestrator
-def rocprof(args, out_dir, tag, child):
+def rocprof(args, out_dir, tag, child, script=None, keep_stdout=False):
     cmd = ["rocprofv3"] + args + ["--output-format", "csv", "-d", os.path.join(out_dir, tag), "-o", tag,
-                                  "--", sys.executable, os.path.abspath(__file__)] + child
+                                  "--", sys.executable, script or os.path.abspath(__file__)] + child
     env = dict(os.environ, TMPDIR="/tmp")
     t0 = time.time()
     r = subprocess.run(["timeout", "-s", "KILL", "300"] + cmd, cwd="/tmp", env=env, capture_output=True, text=True)
@@ -102,7 +135,7 @@ def rocprof(args, out_dir, tag, child):
     if r.returncode != 0:
         sys.stderr.write(r.stdout[-3000:] + r.stderr[-3000:])
         raise SystemExit(f"rocprofv3 pass {tag} failed")
-    return " ".join(cmd)
+    return (" ".join(cmd), r.stdout) if keep_stdout else " ".join(cmd)
 
 
 def read_counter(out_dir, tag, counter):
@@ -126,14 +159,86 @@ def read_trace(out_dir, tag):
     return rows
 
 
-def attention_only(d):
-    return {k: v for k, v in d.items() if any(n in k for n in KERNEL_NAMES)}
+def attention_only(d, names=KERNEL_NAMES):
+    return {k: v for k, v in d.items() if any(n in k for n in names)}
+
+
+def stats_table(stats):
+    md = ["| kernel | calls | average (us) | min (us) | max (us) |", "|---|---|---|---|---|"]
+    for r in stats:
+        md.append(f"| `{r['Name'][:90]}` | {r.get('Calls')} | {float(r.get('AverageNs', 0)) / 1e3:.2f} | "
+                  f"{float(r.get('MinNs', 0)) / 1e3:.2f} | {float(r.get('MaxNs', 0)) / 1e3:.2f} |")
+    return md
+
+
+def bench_trace(out, prof_out):
+    """Kernel trace of the headline measurement: bench.py --quick with its default steps and warm-up."""
+    bench = os.path.join(ROOT, "bench.py")
+    cmd, stdout = rocprof(["--kernel-trace", "--stats"], out, "bench_headline_trace", ["--quick"], script=bench,
+                          keep_stdout=True)
+    line = [l for l in stdout.splitlines() if l.startswith("{")][-1]
+    res = json.loads(line)
+    stats = [r for r in read_trace(out, "bench_headline_trace") if any(n in r["Name"] for n in KERNEL_NAMES)]
+    md = ["# sweep_b128_s2048: the headline measurement under the kernel trace", "",
+          "The command bench.py times (headline workload B=128, Sq=Sk=2048, Hq=32, Hk=8, d=128, causal; "
+          f"{res['warmup']} warm-up and {res['steps']} timed launches), traced. Kernel source hash {kernel_hash()}.", "",
+          "Command (REPO = repository root on the GPU box, run from /tmp with TMPDIR=/tmp):", "",
+          "    " + cmd.replace(ROOT, "$REPO"), "", "Kernel trace (rocprofv3 --stats):", ""] + stats_table(stats) + [
+          "", f"bench.py in the same run (HIP events over the {res['steps']} timed launches): "
+              f"{res['ms_per_step'] * 1e3:.1f} us per launch, {res['value']:.1f} TFLOP/s.", ""]
+    with open(os.path.join(prof_out, "attn_fwd_sweep_b128_s2048_bench.md"), "w") as f:
+        f.write("\n".join(md))
+    print(f"[traffic] bench trace: {res['ms_per_step']:.4f} ms per launch in bench.py", flush=True)
+
+
+def backward_profile(out, prof_out, fetch_scale, write_scale):
+    """Kernel trace and HBM counters of the backward kernels at the Llama-2 prefill shape."""
+    import gqa_inputs as gi
+    w = gi.LLAMA_PREFILL
+    cmd_t = rocprof(["--kernel-trace", "--stats"], out, "bwd_trace", ["--run-bwd"])
+    cmd_f = rocprof(["--pmc", "FETCH_SIZE"], out, "bwd_fetch", ["--run-bwd"])
+    cmd_w = rocprof(["--pmc", "WRITE_SIZE"], out, "bwd_write", ["--run-bwd"])
+    stats = [r for r in read_trace(out, "bwd_trace") if any(n in r["Name"] for n in BWD_KERNEL_NAMES)]
+    fetch = attention_only(read_counter(out, "bwd_fetch", "FETCH_SIZE"), BWD_KERNEL_NAMES)
+    write = attention_only(read_counter(out, "bwd_write", "WRITE_SIZE"), BWD_KERNEL_NAMES)
+    flops = {"bwd_dq_kernel": 3 * w.flops / 2, "bwd_dkdv_kernel": 4 * w.flops / 2}  # 3 and 4 products of the band
+    md = [f"# backward, {w.name}: B={w.B}, Sq=Sk={w.Sq}, Hq={w.Hq}, Hk={w.Hk}, d={w.d}, causal={w.causal}", "",
+          f"One forward call, then {RUN_LAUNCHES} gqa_attn_bwd calls on seeded bf16 N(0,1) inputs. "
+          f"Kernel source hash (forward files) {kernel_hash()}.", "",
+          "Commands (REPO = repository root on the GPU box, run from /tmp with TMPDIR=/tmp):", "",
+          "    " + cmd_t.replace(ROOT, "$REPO"), "    " + cmd_f.replace(ROOT, "$REPO"),
+          "    " + cmd_w.replace(ROOT, "$REPO"), "", "Kernel trace (rocprofv3 --stats):", ""] + stats_table(stats)
+    md += ["", "Matrix-product rate of each kernel (its products over the causal band, 2*d flops per (row, key) pair "
+               "and product):", "", "| kernel | products | TFLOP/s at the average time |", "|---|---|---|"]
+    for r in stats:
+        for kn, fl in flops.items():
+            if kn in r["Name"]:
+                md.append(f"| `{kn}` | {int(round(fl / (w.flops / 2)))} | {fl / (float(r['AverageNs']) * 1e-9) / 1e12:.1f} |")
+    md += ["", f"HBM counters per dispatch (FETCH x{fetch_scale:.3f}, WRITE x{write_scale:.3f} from a 1 GiB copy):", "",
+           "| kernel | FETCH_SIZE (KiB) | WRITE_SIZE (KiB) | HBM bytes (scaled) |", "|---|---|---|---|"]
+    for kname in sorted(set(fetch) | set(write)):
+        f_kib = sum(fetch.get(kname, [0])) / max(1, len(fetch.get(kname, [1])))
+        w_kib = sum(write.get(kname, [0])) / max(1, len(write.get(kname, [1])))
+        md.append(f"| `{kname[:90]}` | {f_kib:.0f} | {w_kib:.0f} | "
+                  f"{(f_kib * 1024 * fetch_scale + w_kib * 1024 * write_scale) / 1e9:.4f} GB |")
+    qb = w.B * w.Sq * w.Hq * w.d * 2   # Q, O, dO, dQ
+    kb = w.B * w.Sk * w.Hk * w.d * 2   # K, V, dK, dV
+    rb = w.B * w.Hq * w.Sq * 4         # LSE, D, base-2 LSE
+    alg = 4 * qb + 4 * kb + 5 * rb     # Q O dO read, dQ written; K V read, dK dV written; LSE read, D and L2 written + read
+    md += ["", f"Algorithmic bytes of the whole backward (Q, O, dO, K, V and LSE read once, dQ, dK, dV written once, "
+               f"D and the base-2 LSE written and read once): {alg / 1e9:.4f} GB.", ""]
+    with open(os.path.join(prof_out, f"attn_bwd_{w.name}.md"), "w") as f:
+        f.write("\n".join(md))
+    print("[traffic] backward profile written", flush=True)
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--run", help=argparse.SUPPRESS)
     ap.add_argument("--copy-ref", action="store_true", help=argparse.SUPPRESS)
+    ap.add_argument("--run-bwd", action="store_true", help=argparse.SUPPRESS)
+    ap.add_argument("--skip-bench-trace", action="store_true")
+    ap.add_argument("--skip-backward", action="store_true")
     ap.add_argument("--out-dir", default=os.path.join(ROOT, "gpurun_out", "traffic"))
     ap.add_argument("--workloads", nargs="*", default=list(WORKLOADS))
     a = ap.parse_args()
@@ -141,6 +246,8 @@ def main():
         return run_workload(a.run)
     if a.copy_ref:
         return run_copy()
+    if a.run_bwd:
+        return run_backward()
 
     out = os.path.abspath(a.out_dir)
     os.makedirs(out, exist_ok=True)
@@ -215,6 +322,10 @@ def main():
 
     with open(os.path.join(prof_out, "traffic.json"), "w") as f:
         json.dump(traffic, f, indent=1, sort_keys=True)
+    if not a.skip_backward:
+        backward_profile(out, prof_out, fetch_scale, write_scale)
+    if not a.skip_bench_trace:
+        bench_trace(out, prof_out)
     print(f"[traffic] wrote {prof_out}", flush=True)
 
 

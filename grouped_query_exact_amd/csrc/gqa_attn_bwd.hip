@@ -313,6 +313,13 @@ void bwd_dkdv_kernel(const BwdParams p) {
     if (CAUSAL) tile_begin = (int)(((int64_t)max(0, k0 - koff) * p.G) / BM);
     const int tile_end = (p.R + BM - 1) / BM;
     const int n = max(0, tile_end - tile_begin);
+    // The j-th tile of the loop, last tile first: the key blocks of a KV
+    // group start together, so each Q / dO tile is read by all of them at
+    // about the same time and leaves HBM once (in ascending order, where
+    // block kb starts at tile 16*kb, the group's 4 MB of Q and dO went
+    // through the L2 several times: 0.92 GB instead of 0.19 GB per call at
+    // the Llama-2 shape).
+    auto tile_of = [&](int j) { return tile_end - 1 - j; };
 
     // Tile copies: packed row -> (token, head) -> [B, Sq, Hq, D] offset. The
     // Q and dO chunks of a tile are numbered 0 .. 2*BM*NCH-1 (Q first) and
@@ -402,7 +409,7 @@ void bwd_dkdv_kernel(const BwdParams p) {
         constexpr bool DK = decltype(dk_tag)::value;
 #pragma unroll
         for (int j = 0; j < STAGES - 2; ++j)
-            if (j < n) issue(tile_begin + j, j);
+            if (j < n) issue(tile_of(j), j);
 
         // K (dV waves) or V (dK waves) rows of the pair's keys -> registers
         // (B operand of S = Q K^T or dP = dO V^T), loaded after the first
@@ -434,10 +441,10 @@ void bwd_dkdv_kernel(const BwdParams p) {
                 }
             }
             __syncthreads();
-            if (j + STAGES - 2 < n) issue(tile_begin + j + STAGES - 2, (j + STAGES - 2) % STAGES);
+            if (j + STAGES - 2 < n) issue(tile_of(j + STAGES - 2), (j + STAGES - 2) % STAGES);
             const int jt = DK ? j - 1 : j;
             if (jt < 0 || jt >= n) continue;
-            const int r0 = (tile_begin + jt) * BM;
+            const int r0 = tile_of(jt) * BM;
             // tokens of the tile; a pair computes only if one of its keys is visible
             const int tok_min = (int)fdiv((uint32_t)r0, p.gmul, p.gshift);
             const int tok_max = (int)fdiv((uint32_t)(min(r0 + BM, p.R) - 1), p.gmul, p.gshift);
