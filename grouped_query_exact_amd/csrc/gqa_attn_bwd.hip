@@ -268,15 +268,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // ---------------------------------------------------------------- dK, dV
 // Eight wavefronts over 128 keys, 32 keys per pair of wavefronts w and w+4
 // (which share a SIMD): wave w+4 computes S = Q K^T and P for query tile j,
-// adds P^T dO to dV and hands P (fp32) to wave w through LDS; one tile later
-// wave w forms dP = dO V^T, dS = P (dP - D) and adds dS^T Q to dK. Each wave
-// issues 16 matrix products per tile, holds one accumulator, and has room
-// for the second wavefront on its SIMD to hide its latencies. The two kinds
-// run separate copies of the tile loop with the same barriers.
+// adds P^T dO to dV and hands P (bf16, the operand it used) to wave w
+// through LDS; one tile later wave w forms dP = dO V^T, dS = P (dP - D) and
+// adds dS^T Q to dK. Each wave issues 8 matrix products per 16 query rows,
+// holds one accumulator, and has room for the second wavefront on its SIMD
+// to hide its latencies. The two kinds run separate copies of the tile loop
+// with the same barriers; a tile of BM rows is MB blocks of 32.
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dkdv_kernel(const BwdParams p) {
     constexpr int BM = kBwdRows;                      // packed query rows per tile
+    constexpr int MB = BM / 32;                       // 32-row blocks per tile
+    static_assert(BM == 32 || BM == 64, "32 or 64 rows per tile");
     constexpr int NCH = D / 8;                        // 16-byte chunks per row
     constexpr int TILE_B = BM * D * 2;                // bytes of a Q or dO tile
     constexpr int NCOPY = 2 * BM * NCH / kBwdThreads; // 16-byte copies per thread and tile (Q and dO)
@@ -284,11 +287,11 @@ void bwd_dkdv_kernel(const BwdParams p) {
     constexpr int STAGE_B = 2 * TILE_B + 2 * 64 * 4;  // Q, dO, 64 -LSE*log2(e) and 64 D slots
     constexpr int STAGES = kBwdStages;
     static_assert(STAGES >= 3, "tiles j-1 and j are in use while j+STAGES-2 is copied");
-    constexpr int PB = 4 * 16 * 64 * 4;               // P of one tile for the four pairs (fp32)
+    constexpr int PAIR_PB = MB * 2 * 64 * 16;         // bf16 P of one tile for one pair
     // copies per wave and tile: its Q / dO chunks, plus the LSE / D row for waves 0 and 1
     constexpr int COPIES_LO = NCOPY + 1, COPIES_HI = NCOPY;
     static_assert(COPIES_LO * (STAGES - 3) < 64, "vmcnt is a 6-bit field");
-    __shared__ __attribute__((aligned(16))) char smem_raw[STAGES * STAGE_B + 2 * PB];
+    __shared__ __attribute__((aligned(16))) char smem_raw[STAGES * STAGE_B + 2 * 4 * PAIR_PB];
     LDS char* lds = (LDS char*)smem_raw;
 
     const int tid = threadIdx.x;
@@ -316,16 +319,16 @@ void bwd_dkdv_kernel(const BwdParams p) {
     // The j-th tile of the loop, last tile first: the key blocks of a KV
     // group start together, so each Q / dO tile is read by all of them at
     // about the same time and leaves HBM once (in ascending order, where
-    // block kb starts at tile 16*kb, the group's 4 MB of Q and dO went
-    // through the L2 several times: 0.92 GB instead of 0.19 GB per call at
-    // the Llama-2 shape).
+    // block kb starts 128 keys' worth of tokens later, the group's 4 MB of Q
+    // and dO went through the L2 several times: 0.92 GB instead of 0.19 GB
+    // per call at the Llama-2 shape).
     auto tile_of = [&](int j) { return tile_end - 1 - j; };
 
     // Tile copies: packed row -> (token, head) -> [B, Sq, Hq, D] offset. The
     // Q and dO chunks of a tile are numbered 0 .. 2*BM*NCH-1 (Q first) and
     // chunk cc lands at byte 16*cc of the stage; a wave's 64 chunks belong to
     // one tensor. Wave 0 copies the rows' -LSE*log2(e), wave 1 their D
-    // (lanes 32..63 repeat rows 0..31).
+    // (with 32-row tiles lanes 32..63 repeat rows 0..31).
     const char* qb = (const char*)(p.q + (int64_t)b * p.Sq * p.Hq * D);
     const char* ob = (const char*)(p.dout + (int64_t)b * p.Sq * p.Hq * D);
     const char* lb = (const char*)(wave == 0 ? p.nlse2 : p.drow) + (int64_t)b * p.Hq * p.Sq * 4;
@@ -339,7 +342,7 @@ void bwd_dkdv_kernel(const BwdParams p) {
         return (uint32_t)((((int64_t)tok * p.Hq + head) * D + (((ci % NCH) ^ swz<D>(row)) * 8)) * 2);
     };
     auto row_offset = [&](int r0) {
-        const int rr = min(r0 + (lane & 31), p.R - 1);
+        const int rr = min(r0 + (lane & (BM - 1)), p.R - 1);
         const int tok = (int)fdiv((uint32_t)rr, p.gmul, p.gshift);
         const int head = g * p.G + (rr - tok * p.G);
         return (uint32_t)(((int64_t)head * p.Sq + tok) * 4);
@@ -377,7 +380,8 @@ void bwd_dkdv_kernel(const BwdParams p) {
         }
     };
 
-    // A operand (S = Q K^T, dP = dO V^T): tile row `col`, d chunk 2*dc + half
+    // A operand (S = Q K^T, dP = dO V^T): row 32*mb + col of the tile, d
+    // chunk 2*dc + half (the swizzle repeats every 16 rows)
     uint32_t aofs[D / 16];
 #pragma unroll
     for (int dc = 0; dc < D / 16; ++dc) aofs[dc] = col * (D * 2) + (((2 * dc + half) ^ swz<D>(col)) * 16);
@@ -385,7 +389,7 @@ void bwd_dkdv_kernel(const BwdParams p) {
     // 16-row block kb2, read rr, lane u16 of its 16-lane group addresses row
     // 16*kb2 + 8*rr + 4*half + u16/4, columns 32*cb + 16*qq + 4*(u16%4); the
     // read hands lane t column 32*cb + 16*qq + t of the rows that slots
-    // 4*rr .. 4*rr+3 of the score registers hold.
+    // 8*(kb2%2) + 4*rr .. +3 of the score registers of block kb2/2 hold.
     const int u16 = lane & 15, qq = (lane >> 4) & 1;
     uint32_t bofs[D / 32][2];
 #pragma unroll
@@ -396,9 +400,10 @@ void bwd_dkdv_kernel(const BwdParams p) {
             const int bcol = cb * 32 + qq * 16 + (u16 & 3) * 4;
             bofs[cb][rr] = brow * (D * 2) + (((bcol >> 3) ^ swz<D>(brow)) * 16) + (bcol & 7) * 2;
         }
-    // P hand-over: 16 fp32 per lane, slot k (registers 4k .. 4k+3) of lane l at
-    // 1024*k + 16*l of the pair's 4 KiB, two tiles' worth (by tile parity)
-    LDS char* pslot = lds + STAGES * STAGE_B + pair * 4096 + lane * 16;
+    // P hand-over: the bf16 A operand of block mb, slot h (registers 8h .. 8h+7)
+    // of lane l at 1024*(2*mb + h) + 16*l of the pair's area, two tiles' worth
+    // (by tile parity)
+    LDS char* pslot = lds + STAGES * STAGE_B + pair * PAIR_PB + lane * 16;
     const float c = p.c;
 
     // The tile loop of one kind of wave (DK: dK, else dV). Iteration j: the
@@ -452,57 +457,60 @@ void bwd_dkdv_kernel(const BwdParams p) {
             const LDS char* qt = lds + (jt % STAGES) * STAGE_B;
             const LDS char* ot = qt + TILE_B;
             const LDS float* lt = (const LDS float*)(qt + 2 * TILE_B);
-            LDS char* ps = pslot + (jt & 1) * (4 * 4096);
-            // S = Q K^T (dV) or dP = dO V^T (dK); register i holds tile row
-            // m_i = 8*(i/4) + 4*half + (i%4) and key `key`
-            f32x16 s = f32x16{};
+            LDS char* ps = pslot + (jt & 1) * (4 * PAIR_PB);
+            const bool need_mask = !DK && ((r0 + BM > p.R) || (kw0 + 32 > p.Sk) || (CAUSAL && kw0 + 31 > tok_min + koff));
+            bf16x8 a[2 * MB];  // dV: P, dK: dS (bf16 A operands), slot i of block mb in a[2*mb + i/8][i%8]
 #pragma unroll
-            for (int dc = 0; dc < D / 16; ++dc) {
-                const bf16x8 a = *(const LDS bf16x8*)((DK ? ot : qt) + aofs[dc]);
-                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, breg[dc], s, 0, 0, 0);
-            }
-            bf16x8 a[2];  // dV: P, dK: dS (bf16, A operand)
-            if (!DK) {
-                const bool need_mask = (r0 + BM > p.R) || (kw0 + 32 > p.Sk) || (CAUSAL && kw0 + 31 > tok_min + koff);
-                float x[16];
+            for (int mb = 0; mb < MB; ++mb) {
+                // S = Q K^T (dV) or dP = dO V^T (dK) of rows 32*mb..; register i
+                // holds row 32*mb + 8*(i/4) + 4*half + (i%4) and key `key`
+                f32x16 s = f32x16{};
 #pragma unroll
-                for (int j4 = 0; j4 < 4; ++j4) {
-                    const f32x4 l4 = *(const LDS f32x4*)(lt + 8 * j4 + 4 * half);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) x[4 * j4 + e] = __builtin_fmaf(s[4 * j4 + e], c, l4[e]);
+                for (int dc = 0; dc < D / 16; ++dc) {
+                    const bf16x8 x = *(const LDS bf16x8*)((DK ? ot : qt) + mb * 32 * D * 2 + aofs[dc]);
+                    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, breg[dc], s, 0, 0, 0);
                 }
-                if (need_mask) {
+                if (!DK) {
+                    float x[16];
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const int rr = r0 + 8 * (i >> 2) + 4 * half + (i & 3);
-                        const int tok = (int)fdiv((uint32_t)min(rr, p.R - 1), p.gmul, p.gshift);
-                        if (rr >= p.R || key >= p.Sk || (CAUSAL && key > tok + koff)) x[i] = -__builtin_inff();
+                    for (int j4 = 0; j4 < 4; ++j4) {
+                        const f32x4 l4 = *(const LDS f32x4*)(lt + 32 * mb + 8 * j4 + 4 * half);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) x[4 * j4 + e] = __builtin_fmaf(s[4 * j4 + e], c, l4[e]);
                     }
-                }
-                f32x4 pv[4];
+                    if (need_mask) {
 #pragma unroll
-                for (int i = 0; i < 16; ++i) pv[i >> 2][i & 3] = __builtin_amdgcn_exp2f(x[i]);
+                        for (int i = 0; i < 16; ++i) {
+                            const int rr = r0 + 32 * mb + 8 * (i >> 2) + 4 * half + (i & 3);
+                            const int tok = (int)fdiv((uint32_t)min(rr, p.R - 1), p.gmul, p.gshift);
+                            if (rr >= p.R || key >= p.Sk || (CAUSAL && key > tok + koff)) x[i] = -__builtin_inff();
+                        }
+                    }
 #pragma unroll
-                for (int k4 = 0; k4 < 4; ++k4) *(LDS f32x4*)(ps + k4 * 1024) = pv[k4];
+                    for (int i = 0; i < 16; ++i) a[2 * mb + (i >> 3)][i & 7] = (__bf16)__builtin_amdgcn_exp2f(x[i]);
 #pragma unroll
-                for (int i = 0; i < 16; ++i) a[i >> 3][i & 7] = (__bf16)pv[i >> 2][i & 3];
-            } else {
-                const LDS float* dt = lt + 64;
+                    for (int h = 0; h < 2; ++h) *(LDS bf16x8*)(ps + (2 * mb + h) * 1024) = a[2 * mb + h];
+                } else {
+                    const LDS float* dt = lt + 64 + 32 * mb;
 #pragma unroll
-                for (int k4 = 0; k4 < 4; ++k4) {
-                    const f32x4 pv = *(const LDS f32x4*)(ps + k4 * 1024);
-                    const f32x4 d4 = *(const LDS f32x4*)(dt + 8 * k4 + 4 * half);
+                    for (int h = 0; h < 2; ++h) {
+                        const bf16x8 pv = *(const LDS bf16x8*)(ps + (2 * mb + h) * 1024);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int i = 4 * k4 + e;
-                        a[i >> 3][i & 7] = (__bf16)(pv[e] * (s[i] - d4[e]));
+                        for (int j4 = 0; j4 < 2; ++j4) {
+                            const f32x4 d4 = *(const LDS f32x4*)(dt + 8 * (2 * h + j4) + 4 * half);
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                const int i = 8 * h + 4 * j4 + e;
+                                a[2 * mb + h][i & 7] = (__bf16)((float)pv[i & 7] * (s[i] - d4[e]));
+                            }
+                        }
                     }
                 }
             }
             // dV += P^T dO or dK += dS^T Q, the second factor read transposed
             const LDS char* xt = DK ? qt : ot;
 #pragma unroll
-            for (int kb2 = 0; kb2 < 2; ++kb2) {
+            for (int kb2 = 0; kb2 < 2 * MB; ++kb2) {
 #pragma unroll
                 for (int cb = 0; cb < D / 32; ++cb) {
                     const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS s16x4*)(xt + bofs[cb][0] + kb2 * 16 * D * 2));

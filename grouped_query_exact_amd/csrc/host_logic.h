@@ -27,13 +27,12 @@ constexpr int kDecStagesKV8 = 3;
 
 // Backward pass: the dK/dV kernel takes 128 keys per workgroup of
 // kBwdThreads (32 keys per wavefront, one wavefront for dK and one for dV)
-// against query tiles of 32 packed rows, streamed through a ring of
-// kBwdStages LDS stages (kBwdStages - 2 tiles in flight while one is
-// computed).
+// against query tiles of kBwdRows packed rows, streamed through a ring of
+// kBwdStages LDS stages (tiles j-1 and j in use, kBwdStages - 2 in flight).
 constexpr int kBwdKeys = 128;
-constexpr int kBwdRows = 32;
+constexpr int kBwdRows = 64;
 constexpr int kBwdThreads = 512;
-constexpr int kBwdStages = 4;
+constexpr int kBwdStages = 3;
 
 // Division by a runtime constant through a precomputed multiplier (the
 // batch-sensitivity article, "PackGQA" mechanism 3, precomputes the
