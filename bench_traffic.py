@@ -47,7 +47,7 @@ KERNEL_SRCS = [os.path.join(ROOT, "grouped_query_exact_amd", "csrc", f)
 PROFILES = os.path.join(ROOT, "profiles")
 COPY_BYTES = 1 << 30
 KERNEL_NAMES = ("attn_fwd_kernel", "attn_decode_kernel", "combine_kernel")
-BWD_KERNEL_NAMES = ("bwd_dot_kernel", "bwd_dq_kernel", "bwd_dkdv_kernel")
+BWD_KERNEL_NAMES = ("bwd_dq_kernel", "bwd_dkdv_kernel")
 RUN_LAUNCHES = 4
 
 # name -> (workload factory, pack_gqa, num_splits); -1 / 0 = the library's choice

@@ -11,13 +11,13 @@
 // (batch-sensitivity article, "performance analysis"); the gradients are the
 // chain rule of the forward definition.
 //
-// Three kernels, all on PackGQA rows (row r of a KV group is token r / G,
+// Two kernels, both on PackGQA rows (row r of a KV group is token r / G,
 // query head g*G + r % G):
-//  * bwd_dot_kernel: D and -LSE*log2(e) for every row (memory-bound).
 //  * bwd_dq_kernel: the forward kernel's tiling (128 rows, 64-key tiles
 //    through a double-buffered LDS ring): S^T = K Q^T and dP^T = V dO^T with
 //    Q and dO rows in registers, dS in registers as the B operand of
-//    dQ^T += K^T dS^T, K^T read with the transposing LDS read.
+//    dQ^T += K^T dS^T, K^T read with the transposing LDS read. It also
+//    forms D of its rows and stores D and -LSE*log2(e) for the next kernel.
 //  * bwd_dkdv_kernel: 128 keys per workgroup of eight wavefronts, four for
 //    dK and four for dV, 32 keys each with their K (and V) rows in
 //    registers; the workgroup streams every query tile (32 packed rows of Q
@@ -57,28 +57,6 @@ __device__ __forceinline__ float lse2_of(float lse) {
     return lse == -__builtin_inff() ? __builtin_inff() : lse * kLog2e;
 }
 
-// ---------------------------------------------------------------- D
-template <int D>
-__global__ __launch_bounds__(256) void bwd_dot_kernel(const BwdParams p) {
-    const int64_t row = (int64_t)blockIdx.x * 256 + threadIdx.x;  // (b*Sq + i)*Hq + h
-    const int64_t rows = (int64_t)p.B * p.Sq * p.Hq;
-    if (row >= rows) return;
-    const u32x4* o = (const u32x4*)(p.o + row * D);
-    const u32x4* g = (const u32x4*)(p.dout + row * D);
-    float acc = 0.f;
-#pragma unroll
-    for (int c = 0; c < D / 8; ++c) {
-        const u32x4 a = o[c], b = g[c];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc += bf16_lo(a[j]) * bf16_lo(b[j]) + bf16_hi(a[j]) * bf16_hi(b[j]);
-    }
-    const int64_t h = row % p.Hq, bi = row / p.Hq;
-    const int64_t i = bi % p.Sq, bb = bi / p.Sq;
-    const int64_t lrow = (bb * p.Hq + h) * p.Sq + i;
-    p.drow[lrow] = acc;
-    p.nlse2[lrow] = -lse2_of(p.lse[lrow]);
-}
-
 // ---------------------------------------------------------------- dQ
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dq_kernel(const BwdParams p) {
@@ -108,21 +86,34 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int hh = h0 + (rc - ti * p.G);
     const int koff = p.Sk - p.Sq;
 
-    // Q and dO rows -> registers (B operands of S^T = K Q^T and dP^T = V dO^T)
+    // Q and dO rows -> registers (B operands of S^T = K Q^T and dP^T = V dO^T).
+    // Every packed row belongs to exactly one workgroup, which also forms its
+    // D = sum(dO * O) (lanes l and l+32 hold the two halves of the row) and
+    // stores D and -LSE*log2(e) for the dK/dV kernel that runs next.
     bf16x8 qreg[D / 16], oreg[D / 16];
+    float dpart = 0.f;
     {
         const int64_t grow = ((int64_t)b * p.Sq + ti) * p.Hq + hh;
         const uint16_t* qrow = p.q + grow * D;
-        const uint16_t* orow = p.dout + grow * D;
+        const uint16_t* grow_p = p.dout + grow * D;
+        const uint16_t* orow = p.o + grow * D;
 #pragma unroll
         for (int dc = 0; dc < D / 16; ++dc) {
             qreg[dc] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qrow + dc * 16 + half * 8));
-            oreg[dc] = __builtin_bit_cast(bf16x8, *(const u32x4*)(orow + dc * 16 + half * 8));
+            const u32x4 gv = *(const u32x4*)(grow_p + dc * 16 + half * 8);
+            const u32x4 ov = *(const u32x4*)(orow + dc * 16 + half * 8);
+            oreg[dc] = __builtin_bit_cast(bf16x8, gv);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) dpart += bf16_lo(gv[j]) * bf16_lo(ov[j]) + bf16_hi(gv[j]) * bf16_hi(ov[j]);
         }
     }
+    const float drow = xhalf_sum(dpart);
     const int64_t lrow = ((int64_t)b * p.Hq + hh) * p.Sq + ti;
     const float lse2 = lse2_of(p.lse[lrow]);
-    const float drow = p.drow[lrow];
+    if (row_valid && half == 0) {
+        p.drow[lrow] = drow;
+        p.nlse2[lrow] = -lse2;
+    }
 
     const int r_last = min(r0 + kBlockM, p.R) - 1;
     const int i_max = (int)fdiv((uint32_t)r_last, p.gmul, p.gshift);
@@ -544,13 +535,9 @@ void bwd_dkdv_kernel(const BwdParams p) {
 // no query tile). The caller rejects Sk == 0 with queries.
 template <int D, bool CAUSAL>
 static hipError_t launch_bwd_d(const BwdParams& p, hipStream_t stream) {
-    const int64_t rows = (int64_t)p.B * p.Sq * p.Hq;
-    if (rows > 0) {
-        hipLaunchKernelGGL((bwd_dot_kernel<D>), dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, stream, p);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
+    if ((int64_t)p.B * p.Sq * p.Hq > 0) {
         hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3(p.grid_dq), dim3(kThreads), 0, stream, p);
-        e = hipGetLastError();
+        const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     if (p.grid_dkdv > 0)
