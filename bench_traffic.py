@@ -49,6 +49,7 @@ COPY_BYTES = 1 << 30
 KERNEL_NAMES = ("attn_fwd_kernel", "attn_decode_kernel", "combine_kernel")
 BWD_KERNEL_NAMES = ("bwd_dq_kernel", "bwd_dkdv_kernel")
 RUN_LAUNCHES = 4
+BWD_LAUNCHES = 20  # short kernels: enough calls for the average to be the steady state
 
 # name -> (workload factory, pack_gqa, num_splits); -1 / 0 = the library's choice
 WORKLOADS = {
@@ -93,7 +94,7 @@ def run_workload(name):
 
 
 def run_backward():
-    """Forward once, then RUN_LAUNCHES backward calls at the Llama-2 prefill shape (B=4, causal)."""
+    """Forward once, then BWD_LAUNCHES backward calls at the Llama-2 prefill shape (B=4, causal)."""
     import torch
     import grouped_query_exact_amd as g
     import gqa_inputs as gi
@@ -107,10 +108,10 @@ def run_backward():
     lse = torch.empty((w.B, w.Hq, w.Sq), dtype=torch.float32, device=dev)
     g.gqa_attn_fwd(q, k, v, out, lse, w.causal, w.scale)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    for _ in range(RUN_LAUNCHES):
+    for _ in range(BWD_LAUNCHES):
         g.gqa_attn_bwd(q, k, v, out, lse, do, dq, dk, dv, w.causal, w.scale)
     torch.cuda.synchronize()
-    print(json.dumps({"workload": "backward " + w.name, "launches": RUN_LAUNCHES}), flush=True)
+    print(json.dumps({"workload": "backward " + w.name, "launches": BWD_LAUNCHES}), flush=True)
 
 
 def run_copy():
@@ -203,7 +204,7 @@ def backward_profile(out, prof_out, fetch_scale, write_scale):
     write = attention_only(read_counter(out, "bwd_write", "WRITE_SIZE"), BWD_KERNEL_NAMES)
     flops = {"bwd_dq_kernel": 3 * w.flops / 2, "bwd_dkdv_kernel": 4 * w.flops / 2}  # 3 and 4 products of the band
     md = [f"# backward, {w.name}: B={w.B}, Sq=Sk={w.Sq}, Hq={w.Hq}, Hk={w.Hk}, d={w.d}, causal={w.causal}", "",
-          f"One forward call, then {RUN_LAUNCHES} gqa_attn_bwd calls on seeded bf16 N(0,1) inputs. "
+          f"One forward call, then {BWD_LAUNCHES} gqa_attn_bwd calls on seeded bf16 N(0,1) inputs. "
           f"Kernel source hash (forward files) {kernel_hash()}.", "",
           "Commands (REPO = repository root on the GPU box, run from /tmp with TMPDIR=/tmp):", "",
           "    " + cmd_t.replace(ROOT, "$REPO"), "    " + cmd_f.replace(ROOT, "$REPO"),
