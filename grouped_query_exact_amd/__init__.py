@@ -15,7 +15,7 @@ import os
 from typing import Optional, Tuple
 
 __all__ = ["GqaAttnError", "gqa_attn_fwd", "gqa_attn_func", "gqa_attn_fwd_paged", "gqa_attn_func_paged",
-           "gqa_attn_fwd_kv8", "gqa_attn_fwd_paged_kv8", "gqa_attn_fwd_varlen", "gqa_attn_bwd",
+           "gqa_attn_fwd_kv8", "gqa_attn_fwd_paged_kv8", "gqa_attn_fwd_qk8", "gqa_attn_fwd_varlen", "gqa_attn_bwd",
            "gqa_attn_choose", "gqa_attn_plan",
            "gqa_attn_strerror", "library_path", "load_library",
            "GQA_OK", "GQA_ERR_INVALID_ARG", "GQA_ERR_UNSUPPORTED", "GQA_ERR_NOMEM", "GQA_ERR_HIP"]
@@ -63,6 +63,8 @@ def load_library():
     lib.gqa_attn_fwd_paged.restype = c_int
     lib.gqa_attn_fwd_kv8.argtypes = [vp] * 3 + [c_float, c_float] + [vp, vp] + [c_int] * 7 + [c_float, c_int, c_int, vp]
     lib.gqa_attn_fwd_kv8.restype = c_int
+    lib.gqa_attn_fwd_qk8.argtypes = [vp] * 3 + [c_float, c_float] + [vp, vp] + [c_int] * 7 + [c_float, c_int, c_int, vp]
+    lib.gqa_attn_fwd_qk8.restype = c_int
     lib.gqa_attn_fwd_paged_kv8.argtypes = [vp] * 3 + [c_float, c_float] + [vp] * 4 + [c_int] * 8 + \
         [c_int, c_float, c_int, c_int, vp]
     lib.gqa_attn_fwd_paged_kv8.restype = c_int
@@ -183,6 +185,29 @@ def gqa_attn_fwd_kv8(q, k, v, k_scale: float, v_scale: float, out, lse, causal: 
     stream = _stream(q, stream)
     with torch.cuda.device(q.device):
         st = load_library().gqa_attn_fwd_kv8(_ptr(q), _ptr(k), _ptr(v), float(k_scale), float(v_scale), _ptr(out),
+                                             _ptr(lse), B, Sq, Sk, Hq, Hk, d, int(bool(causal)), float(scale),
+                                             int(pack_gqa), int(num_splits), stream)
+    if st != GQA_OK:
+        raise GqaAttnError(st)
+
+
+def gqa_attn_fwd_qk8(q, k, v, q_scale: float, k_scale: float, out, lse, causal: bool, scale: float,
+                     pack_gqa: int = -1, num_splits: int = 0, stream=None) -> None:
+    """Forward pass with fp8 e4m3 Q ([B, Sq, Hq, d] bytes) and K ([B, Sk, Hk, d] bytes) with per-tensor
+    factors and bf16 V, into ``out``/``lse``: the scores run on the fp8 matrix cores."""
+    import torch
+    _check_kv8(q=q, k=k)
+    _check_bf16(v=v, out=out)
+    B, Sq, Hq, d = q.shape
+    _, Sk, Hk, _ = k.shape
+    if tuple(k.shape) != (B, Sk, Hk, d) or tuple(v.shape) != tuple(k.shape) or tuple(out.shape) != tuple(q.shape):
+        raise ValueError("shape mismatch between q, k, v and out")
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()
+                            or tuple(lse.shape) != (B, Hq, Sq) or not lse.is_cuda):
+        raise ValueError("lse must be a contiguous [B, Hq, Sq] float32 GPU tensor")
+    stream = _stream(q, stream)
+    with torch.cuda.device(q.device):
+        st = load_library().gqa_attn_fwd_qk8(_ptr(q), _ptr(k), _ptr(v), float(q_scale), float(k_scale), _ptr(out),
                                              _ptr(lse), B, Sq, Sk, Hq, Hk, d, int(bool(causal)), float(scale),
                                              int(pack_gqa), int(num_splits), stream)
     if st != GQA_OK:

@@ -16,6 +16,7 @@ typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));  // 32 fp8 values (one 32x32x64 operand)
 
 #define LDS __attribute__((address_space(3)))
 
@@ -46,6 +47,16 @@ template <int D>
 __device__ __forceinline__ int swz(int row) {
     if (D == 128) return ((row & 3) << 2) | ((row >> 2) & 3);
     return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+}
+
+// Chunk swizzle of fp8 rows (d bytes, 16-byte chunks): chunk c of row r is
+// stored at c ^ swz8(r), which spreads the rows a 16-lane read group touches
+// over all 16-byte bank groups (d=128: the rows' parity and (r>>1)&7;
+// d=64: (r&3) and (r>>2)&3).
+template <int D>
+__device__ __forceinline__ int swz8(int row) {
+    if (D == 128) return (row >> 1) & 7;
+    return (row >> 2) & 3;
 }
 
 // Remap a hardware workgroup id (dealt round-robin over the 8 XCDs) to a

@@ -126,6 +126,8 @@ struct Call {
     hipStream_t stream;
     bool kv8 = false;       // fp8 e4m3 K/V with per-tensor factors
     float k_scale = 1.f, v_scale = 1.f;
+    bool qk8 = false;       // fp8 e4m3 Q and K with per-tensor factors (q_scale, k_scale), bf16 V
+    float q_scale = 1.f;
     bool varlen = false;    // packed sequences (s.Sq, s.Sk = max_seqlen_q, max_seqlen_k)
     const int* cu_q = nullptr;
     const int* cu_k = nullptr;
@@ -171,12 +173,16 @@ int run(const Call& c) {
     // A scale so small that |scale|*log2(e) is not a normal fp32 number
     // also gives every visible key exactly the same weight in fp32.
     // fp8 K/V: the scores are (scale * k_scale) * q.k8, the output v_scale * P.v8.
-    const double score_scale = c.kv8 ? (double)c.scale * (double)c.k_scale : (double)c.scale;
+    // fp8 Q/K: the scores are (scale * q_scale * k_scale) * q8.k8 (the sign
+    // bit of every e4m3 byte negates it).
+    double score_scale = (double)c.scale;
+    if (c.kv8) score_scale *= (double)c.k_scale;
+    if (c.qk8) score_scale *= (double)c.q_scale * (double)c.k_scale;
     const double cd = std::fabs(score_scale) * 1.4426950408889634;
     const bool zero_scale = cd < 1.1754943508222875e-38;
     p.c = zero_scale ? 1.0f : (float)cd;
     p.qand = zero_scale ? 0u : 0xFFFFFFFFu;
-    p.qsign = score_scale < 0.0 ? 0x80008000u : 0u;
+    p.qsign = score_scale < 0.0 ? (c.qk8 ? 0x80808080u : 0x80008000u) : 0u;
     p.vscale = c.kv8 ? c.v_scale : 1.f;
     if (c.varlen) {
         p.cu_q = c.cu_q;
@@ -205,7 +211,7 @@ int run(const Call& c) {
 
     auto launch = [&](bool split) {
         return plan.decode ? gqa::launch_decode(p, d, s.causal != 0, split, c.paged, c.kv8, c.varlen, c.stream)
-                           : gqa::launch_attention(p, d, s.causal != 0, split, c.varlen, c.stream);
+                           : gqa::launch_attention(p, d, s.causal != 0, split, c.varlen, c.qk8, c.stream);
     };
     if (plan.ns == 1) {
         hipError_t e = launch(false);
@@ -414,6 +420,28 @@ int gqa_attn_fwd_kv8(const void* q, const void* k, const void* v, float k_scale,
         if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return GQA_ERR_UNSUPPORTED;
         Call c{q, k, v, out, lse, s, scale, pack_gqa, num_splits, false, nullptr, nullptr, 0, 0, 0, stream,
                true, k_scale, v_scale};
+        return run(c);
+    } catch (...) {
+        return GQA_ERR_HIP;
+    }
+}
+
+int gqa_attn_fwd_qk8(const void* q, const void* k, const void* v, float q_scale, float k_scale, void* out,
+                     float* lse, int B, int Sq, int Sk, int Hq, int Hk, int d, int causal, float scale,
+                     int pack_gqa, int num_splits, hipStream_t stream) {
+    try {
+        if (!std::isfinite(q_scale) || !std::isfinite(k_scale)) return GQA_ERR_INVALID_ARG;
+        gqa::Shape s{B, Sq, Sk, Hq, Hk, d, causal ? 1 : 0};
+        s.q_bytes = 1;
+        int st = gqa::check_sizes(s, scale, pack_gqa, num_splits);
+        if (st != GQA_OK) return st;
+        if ((long long)B * Sq == 0) return GQA_OK;
+        if (!q || !k || !v || !out) return GQA_ERR_INVALID_ARG;
+        if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return GQA_ERR_UNSUPPORTED;
+        Call c{q, k, v, out, lse, s, scale, pack_gqa, num_splits, false, nullptr, nullptr, 0, 0, 0, stream};
+        c.qk8 = true;
+        c.q_scale = q_scale;
+        c.k_scale = k_scale;
         return run(c);
     } catch (...) {
         return GQA_ERR_HIP;

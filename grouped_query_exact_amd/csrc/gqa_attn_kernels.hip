@@ -78,12 +78,16 @@ __device__ __forceinline__ int64_t lse_index(const FwdParams& p, int b, int hh, 
     return varlen ? (int64_t)hh * p.total_q + qtok0 + ti : ((int64_t)b * p.Hq + hh) * p.Sq + ti;
 }
 
-template <int D, bool CAUSAL, bool SPLIT, bool VARLEN>
+// QK8: Q and K hold fp8 e4m3 bytes; S^T = K Q^T runs on the fp8 matrix
+// cores (v_mfma_scale_f32_32x32x64_f8f6f4, unit block scales), V stays bf16.
+template <int D, bool CAUSAL, bool SPLIT, bool VARLEN, bool QK8>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_kernel(const FwdParams p) {
     constexpr int TILE = kBlockN * D;                 // elements of one K or V tile
-    constexpr int TILE_B = TILE * 2;                  // bytes
-    constexpr int NCH = D / 8;                        // 16-byte chunks per row
-    constexpr int NLOAD = kBlockN * NCH / kThreads;   // 16-byte loads per thread per tensor
+    constexpr int TILE_B = TILE * 2;                  // bytes (bf16; an fp8 K tile uses the first half)
+    constexpr int NCH = D / 8;                        // 16-byte chunks per bf16 row
+    constexpr int NLOAD = kBlockN * NCH / kThreads;   // 16-byte loads per thread per bf16 tensor
+    constexpr int NCH8 = D / 16;                      // 16-byte chunks per fp8 row
+    constexpr int NLOADK = QK8 ? kBlockN * NCH8 / kThreads : NLOAD;  // ... for the K tile
     __shared__ __attribute__((aligned(16))) uint16_t smem[4 * TILE];
     LDS char* lds = (LDS char*)smem;                  // [buf][K|V] tiles
 
@@ -132,15 +136,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int hh = h0 + (rc - ti * p.Gp);
     const int koff = Sk - Sq;  // bottom-right causal offset
 
-    // ---- Q rows -> registers (B operand of S^T = K Q^T)
-    bf16x8 qreg[D / 16];
-    {
+    // ---- Q rows -> registers (B operand of S^T = K Q^T). fp8: operand t
+    // covers d in [64t, 64t+64), lane half h holds bytes 64t+32h .. +31 (the
+    // 32x32x64 product pairs byte j of a lane half of A with byte j of the
+    // same lane half of B, so K is read with the same split).
+    bf16x8 qreg[QK8 ? 1 : D / 16];
+    i32x8 q8reg[QK8 ? D / 64 : 1];
+    if (!QK8) {
         const uint16_t* qrow = p.q + ((qtok0 + ti) * p.Hq + hh) * D;
 #pragma unroll
         for (int dc = 0; dc < D / 16; ++dc) {
             u32x4 w = *(const u32x4*)(qrow + dc * 16 + half * 8);
             w = (w & p.qand) ^ p.qsign;
             qreg[dc] = __builtin_bit_cast(bf16x8, w);
+        }
+    } else {
+        const uint8_t* qrow = (const uint8_t*)p.q + ((qtok0 + ti) * p.Hq + hh) * D;
+#pragma unroll
+        for (int t = 0; t < D / 64; ++t) {
+            const u32x4 w0 = (*(const u32x4*)(qrow + 64 * t + 32 * half) & p.qand) ^ p.qsign;
+            const u32x4 w1 = (*(const u32x4*)(qrow + 64 * t + 32 * half + 16) & p.qand) ^ p.qsign;
+            q8reg[t] = i32x8{(int)w0[0], (int)w0[1], (int)w0[2], (int)w0[3], (int)w1[0], (int)w1[1], (int)w1[2], (int)w1[3]};
         }
     }
 
@@ -164,9 +180,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
     // ---- K/V tile loads: per-lane byte offsets inside a tile, scalar tile base
     const int64_t kv_stride_b = (int64_t)p.Hk * D * 2;
-    const char* kbase = (const char*)(p.k + (ktok0 * p.Hk + g) * D);
+    const int64_t k_stride_b = QK8 ? (int64_t)p.Hk * D : kv_stride_b;
+    const char* kbase = QK8 ? (const char*)p.k + (ktok0 * p.Hk + g) * D : (const char*)(p.k + (ktok0 * p.Hk + g) * D);
     const char* vbase = (const char*)(p.v + (ktok0 * p.Hk + g) * D);
-    uint32_t goff[NLOAD];
+    // chunk ci of a tile: row ci / (chunks per row), stored at its position
+    // in the row, holding the global chunk that the row's swizzle puts there
+    auto k_chunk = [&](int ci, int& row) {
+        row = ci / (QK8 ? NCH8 : NCH);
+        return QK8 ? (ci % NCH8) ^ swz8<D>(row) : (ci % NCH) ^ swz<D>(row);
+    };
+    uint32_t goff[NLOAD], goffk[NLOADK];
 #pragma unroll
     for (int u = 0; u < NLOAD; ++u) {
         const int ci = (u * 4 + wave) * 64 + lane;
@@ -174,38 +197,56 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const int logical_ch = (ci % NCH) ^ swz<D>(row);
         goff[u] = (uint32_t)(row * kv_stride_b + logical_ch * 16);
     }
+#pragma unroll
+    for (int u = 0; u < NLOADK; ++u) {
+        int row;
+        const int logical_ch = k_chunk((u * 4 + wave) * 64 + lane, row);
+        goffk[u] = (uint32_t)(row * k_stride_b + logical_ch * 16);
+    }
     auto issue = [&](int kv0, int buf) {
         LDS char* kt = lds + buf * 2 * TILE_B;
         LDS char* vt = kt + TILE_B;
-        const char* kg = kbase + kv0 * kv_stride_b;
+        const char* kg = kbase + kv0 * k_stride_b;
         const char* vg = vbase + kv0 * kv_stride_b;
+        // copy u of K (fp8: the first NLOADK) and of V go to the same offset of
+        // their tiles; with bf16 K the two copies of each u are issued together
         if (kv0 + kBlockN <= Sk) {
 #pragma unroll
             for (int u = 0; u < NLOAD; ++u) {
-                const int dst = (u * 4 + wave) * 1024;
-                lds_dma16(kg, goff[u], kt + dst);
-                lds_dma16(vg, goff[u], vt + dst);
+                if (u < NLOADK) lds_dma16(kg, goffk[u < NLOADK ? u : 0], kt + (u * 4 + wave) * 1024);
+                lds_dma16(vg, goff[u], vt + (u * 4 + wave) * 1024);
             }
         } else {  // ragged last tile: rows past the end re-read the last key (masked later)
 #pragma unroll
             for (int u = 0; u < NLOAD; ++u) {
-                const int dst = (u * 4 + wave) * 1024;
+                if (u < NLOADK) {
+                    int row;
+                    const int logical_ch = k_chunk((u * 4 + wave) * 64 + lane, row);
+                    const int key = min(kv0 + row, Sk - 1) - kv0;
+                    lds_dma16(kg, (uint32_t)(key * k_stride_b + logical_ch * 16), kt + (u * 4 + wave) * 1024);
+                }
                 const int ci = (u * 4 + wave) * 64 + lane;
                 const int row = ci / NCH;
                 const int logical_ch = (ci % NCH) ^ swz<D>(row);
                 const int key = min(kv0 + row, Sk - 1) - kv0;
-                const uint32_t o = (uint32_t)(key * kv_stride_b + logical_ch * 16);
-                lds_dma16(kg, o, kt + dst);
-                lds_dma16(vg, o, vt + dst);
+                lds_dma16(vg, (uint32_t)(key * kv_stride_b + logical_ch * 16), vt + (u * 4 + wave) * 1024);
             }
         }
     };
 
     // ---- per-lane LDS operand offsets (bytes, relative to the tile start)
     const int krow0 = pi32(col);
-    uint32_t kofs[D / 16];
+    uint32_t kofs[QK8 ? 1 : D / 16];
+    uint32_t kofs8[QK8 ? D / 64 : 1][2];  // fp8: operand t, 16-byte halves of the lane's 32 bytes
+    if (!QK8) {
 #pragma unroll
-    for (int dc = 0; dc < D / 16; ++dc) kofs[dc] = krow0 * (D * 2) + (((2 * dc + half) ^ swz<D>(krow0)) * 16);
+        for (int dc = 0; dc < D / 16; ++dc) kofs[dc] = krow0 * (D * 2) + (((2 * dc + half) ^ swz<D>(krow0)) * 16);
+    } else {
+#pragma unroll
+        for (int t = 0; t < D / 64; ++t)
+#pragma unroll
+            for (int e = 0; e < 2; ++e) kofs8[t][e] = krow0 * D + (((4 * t + 2 * half + e) ^ swz8<D>(krow0)) * 16);
+    }
     const int u16 = lane & 15, qq = (lane >> 4) & 1;
     const int rho = ((u16 & 1) << 1) | ((u16 >> 1) & 1);  // 0,2,1,3
     uint32_t vofs[D / 32][2];
@@ -237,10 +278,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
             sacc[mb] = f32x16{};
+            if (!QK8) {
 #pragma unroll
-            for (int dc = 0; dc < D / 16; ++dc) {
-                const bf16x8 a = *(const LDS bf16x8*)(kt + kofs[dc] + mb * 32 * D * 2);
-                sacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[dc], sacc[mb], 0, 0, 0);
+                for (int dc = 0; dc < D / 16; ++dc) {
+                    const bf16x8 a = *(const LDS bf16x8*)(kt + kofs[dc] + mb * 32 * D * 2);
+                    sacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[dc], sacc[mb], 0, 0, 0);
+                }
+            } else {
+#pragma unroll
+                for (int t = 0; t < D / 64; ++t) {
+                    const u32x4 a0 = *(const LDS u32x4*)(kt + kofs8[t][0] + mb * 32 * D);
+                    const u32x4 a1 = *(const LDS u32x4*)(kt + kofs8[t][1] + mb * 32 * D);
+                    const i32x8 a = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+                    // e4m3 x e4m3 (format 0 for A and B), block scale exponents 127 = 1.0
+                    sacc[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, q8reg[t], sacc[mb], 0, 0, 0, 127, 0, 127);
+                }
             }
         }
         // keys of this lane's slots: kv0 + 32*mb + 16*(i/8) + 8*half + (i%8)
@@ -746,22 +798,29 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombineParams p) {
 }
 
 // ---------------------------------------------------------------- launchers
-template <int D, bool CAUSAL, bool SPLIT, bool VARLEN>
+template <int D, bool CAUSAL, bool SPLIT, bool VARLEN, bool QK8>
 static hipError_t launch_attn(const FwdParams& p, hipStream_t stream) {
-    hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, SPLIT, VARLEN>), dim3(p.grid), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, SPLIT, VARLEN, QK8>), dim3(p.grid), dim3(kThreads), 0, stream, p);
     return hipGetLastError();
 }
 
-template <int D, bool VARLEN>
+template <int D, bool VARLEN, bool QK8>
 static hipError_t launch_attn_d(const FwdParams& p, bool causal, bool split, hipStream_t stream) {
-    if (causal) return split ? launch_attn<D, true, true, VARLEN>(p, stream) : launch_attn<D, true, false, VARLEN>(p, stream);
-    return split ? launch_attn<D, false, true, VARLEN>(p, stream) : launch_attn<D, false, false, VARLEN>(p, stream);
+    if (causal)
+        return split ? launch_attn<D, true, true, VARLEN, QK8>(p, stream) : launch_attn<D, true, false, VARLEN, QK8>(p, stream);
+    return split ? launch_attn<D, false, true, VARLEN, QK8>(p, stream) : launch_attn<D, false, false, VARLEN, QK8>(p, stream);
 }
 
-hipError_t launch_attention(const FwdParams& p, int d, bool causal, bool split, bool varlen, hipStream_t stream) {
-    if (d == 128)
-        return varlen ? launch_attn_d<128, true>(p, causal, split, stream) : launch_attn_d<128, false>(p, causal, split, stream);
-    return varlen ? launch_attn_d<64, true>(p, causal, split, stream) : launch_attn_d<64, false>(p, causal, split, stream);
+// Instantiated combinations: bf16, variable-length bf16, fp8 Q/K.
+template <int D>
+static hipError_t launch_attn_dd(const FwdParams& p, bool causal, bool split, bool varlen, bool qk8, hipStream_t stream) {
+    if (qk8) return launch_attn_d<D, false, true>(p, causal, split, stream);
+    return varlen ? launch_attn_d<D, true, false>(p, causal, split, stream) : launch_attn_d<D, false, false>(p, causal, split, stream);
+}
+
+hipError_t launch_attention(const FwdParams& p, int d, bool causal, bool split, bool varlen, bool qk8, hipStream_t stream) {
+    return d == 128 ? launch_attn_dd<128>(p, causal, split, varlen, qk8, stream)
+                    : launch_attn_dd<64>(p, causal, split, varlen, qk8, stream);
 }
 
 template <int D, bool CAUSAL, bool SPLIT, bool PAGED, bool KV8, bool VARLEN>

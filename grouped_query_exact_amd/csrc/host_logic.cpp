@@ -65,7 +65,7 @@ void choose(const Shape& s, int num_cus, int* pack_gqa, int* num_splits) {
     // more arithmetic per byte and four per compute unit are best.
     const int Gp = pack ? G : 1;
     const long long R = (long long)s.Sq * Gp;
-    const bool decode = R <= kDecBlockM;
+    const bool decode = R <= kDecBlockM && s.q_bytes == 2;
     const int bm = decode ? kDecBlockM : kBlockM, bn = decode ? kDecBlockN : kBlockN;
     const long long units = (long long)s.B * (pack ? s.Hk : s.Hq) * ceil_div(R, bm);
     const int T = R > 0 ? key_tiles_for(s, Gp, R, bn) : 0;
@@ -94,7 +94,7 @@ int make_plan(const Shape& s, int pack_gqa, int num_splits, int num_cus, Plan* p
     p->units_per_b = pack ? s.Hk : s.Hq;
     p->R = (long long)s.Sq * p->Gp;
     if (p->R > INT_MAX / 2) return GQA_ERR_INVALID_ARG;
-    p->decode = p->R <= kDecBlockM ? 1 : 0;
+    p->decode = p->R <= kDecBlockM && s.q_bytes == 2 ? 1 : 0;
     p->block_m = p->decode ? kDecBlockM : kBlockM;
     p->block_n = p->decode ? kDecBlockN : kBlockN;
     p->row_tiles = (int)ceil_div(p->R, p->block_m);

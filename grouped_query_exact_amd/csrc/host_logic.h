@@ -53,6 +53,7 @@ inline uint32_t fastdiv_host(uint32_t n, const FastDiv& f) {
 struct Shape {
     int B, Sq, Sk, Hq, Hk, d, causal;
     int kv_bytes = 2;  // bytes per stored K/V element: 2 (bf16) or 1 (fp8)
+    int q_bytes = 2;   // bytes per stored Q element: 2 (bf16) or 1 (fp8 Q and K: tiled kernel only)
 };
 
 // Returns 0 or a gqa_status_t error for the sizes alone (no pointers).

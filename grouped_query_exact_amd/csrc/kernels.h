@@ -27,7 +27,7 @@ struct FwdParams {
     int grid;           // workgroups
     float c;            // |scale| * log2(e), or 1 when scale == 0
     uint32_t qand;      // 0 when scale == 0 (Q read as zeros: every visible score is 0), else all ones
-    uint32_t qsign;     // 0x80008000 to negate Q (negative scale), else 0
+    uint32_t qsign;     // sign bits that negate Q (negative score factor): 0x80008000 bf16, 0x80808080 fp8; else 0
     // paged K/V (decode kernel only): k and v point at page pools
     // [num_pages, page_size, Hk, D]; Sk is unused.
     const int* block_table;  // [B, max_pages] pool page of each logical page
@@ -76,7 +76,7 @@ struct BwdParams {
 
 hipError_t launch_backward(const BwdParams& p, int d, bool causal, hipStream_t stream);
 
-hipError_t launch_attention(const FwdParams& p, int d, bool causal, bool split, bool varlen, hipStream_t stream);
+hipError_t launch_attention(const FwdParams& p, int d, bool causal, bool split, bool varlen, bool qk8, hipStream_t stream);
 hipError_t launch_decode(const FwdParams& p, int d, bool causal, bool split, bool paged, bool kv8, bool varlen,
                          hipStream_t stream);
 hipError_t launch_combine(const CombineParams& p, int d, long long grid, hipStream_t stream);

@@ -204,6 +204,25 @@ int gqa_attn_fwd_paged_kv8(const void* q, const void* k_cache, const void* v_cac
                            int causal, float scale, int pack_gqa, int num_splits,
                            hipStream_t stream);
 
+/* Forward pass with Q and K stored as fp8: the scores on the fp8 matrix cores.
+ *
+ * The same FP8 e4m3 format as gqa_attn_fwd_kv8 (rise-and-fall tuning article,
+ * "verification and further directions"; Stable-Diffusion GQA guide, FP8
+ * intermediate precision), applied where it pays in compute-bound prefill:
+ * q holds e4m3 bytes [B, Sq, Hq, d] and k e4m3 bytes [B, Sk, Hk, d]; v, out
+ * and lse are bf16 / fp32 as for gqa_attn_fwd. With per-tensor factors
+ * q_scale and k_scale the operation is gqa_attn_fwd's over Q = q_scale * q8,
+ * K = k_scale * k8 and V, computed as scores (scale * q_scale * k_scale) *
+ * q8.k8 on the 32x32x64 fp8 products, whose e4m3 x e4m3 products are exact
+ * in the fp32 accumulation, and P V on the bf16 products exactly as
+ * gqa_attn_fwd: the same tolerances as the bf16 path apply. Quantising Q and
+ * K to e4m3 is the caller's step. q_scale, k_scale: any finite fp32 values
+ * (INVALID_ARG otherwise). Every shape runs on the tiled kernel (no decode
+ * specialisation); other rules as for gqa_attn_fwd. */
+int gqa_attn_fwd_qk8(const void* q, const void* k, const void* v, float q_scale, float k_scale,
+                     void* out, float* lse, int B, int Sq, int Sk, int Hq, int Hk, int d,
+                     int causal, float scale, int pack_gqa, int num_splits, hipStream_t stream);
+
 /* The host heuristic behind pack_gqa = -1 / num_splits = 0. It follows the
  * pages' rationale (rise-and-fall tuning article, "root cause" and "fix"
  * table; batch-sensitivity article, "performance analysis"): pack when the

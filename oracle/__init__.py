@@ -14,10 +14,10 @@ from .attention import (NEG_INF, attention_fp64, combine_fp64, kv_head_of,
                         split_combine_fp64, split_partials_fp64, split_tiles,
                         visible_keys)
 from .paged import attention_paged_fp64, gather_pages
-from .fp8 import attention_kv8_fp64, attention_paged_kv8_fp64, e4m3_to_float
+from .fp8 import attention_kv8_fp64, attention_paged_kv8_fp64, attention_qk8_fp64, e4m3_to_float
 from .varlen import attention_varlen_fp64
 from .backward import attention_bwd_fp64, row_dot_fp64
 
-__all__ = ["NEG_INF", "attention_bwd_fp64", "attention_fp64", "attention_kv8_fp64", "attention_paged_fp64", "attention_paged_kv8_fp64",
+__all__ = ["NEG_INF", "attention_bwd_fp64", "attention_fp64", "attention_kv8_fp64", "attention_paged_fp64", "attention_paged_kv8_fp64", "attention_qk8_fp64",
            "attention_varlen_fp64", "combine_fp64", "e4m3_to_float", "gather_pages", "row_dot_fp64",
            "kv_head_of", "split_combine_fp64", "split_partials_fp64", "split_tiles", "visible_keys"]

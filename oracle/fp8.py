@@ -14,6 +14,11 @@ follows the OCP 8-bit floating point format: 1 sign bit, 4 exponent bits
 with bias 7, 3 mantissa bits; exponent 0 encodes subnormals m * 2^-9; the
 code S.1111.111 is NaN and there is no infinity, so the largest finite
 magnitude is 1.75 * 2^8 = 448.
+
+The same reading for fp8 queries and keys (the compute-bound prefill case):
+Q and K given as e4m3 bytes with factors q_scale and k_scale, V in bf16; the
+operation is the plain attention over Q = q_scale * decode(q8),
+K = k_scale * decode(k8) and V.
 """
 
 from __future__ import annotations
@@ -49,3 +54,10 @@ def attention_paged_kv8_fp64(q, k8_cache, v8_cache, block_table, seqlens_k, k_sc
     K = e4m3_to_float(k8_cache) * float(k_scale)
     V = e4m3_to_float(v8_cache) * float(v_scale)
     return attention_paged_fp64(q, K, V, block_table, seqlens_k, causal, scale, **select)
+
+
+def attention_qk8_fp64(q8, k8, v, q_scale: float, k_scale: float, causal: bool, scale: float, **select):
+    """Exact GQA forward over Q = q_scale * decode(q8), K = k_scale * decode(k8) and V."""
+    Q = e4m3_to_float(q8) * float(q_scale)
+    K = e4m3_to_float(k8) * float(k_scale)
+    return attention_fp64(Q, K, np.asarray(v, dtype=np.float64), causal, scale, **select)

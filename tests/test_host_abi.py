@@ -34,7 +34,8 @@ def lib():
 def test_header_declares_the_boundary():
     names = declared_functions()
     assert names == ["gqa_attn_bwd", "gqa_attn_choose", "gqa_attn_fwd", "gqa_attn_fwd_kv8", "gqa_attn_fwd_paged",
-                     "gqa_attn_fwd_paged_kv8", "gqa_attn_fwd_varlen", "gqa_attn_plan", "gqa_attn_strerror"]
+                     "gqa_attn_fwd_paged_kv8", "gqa_attn_fwd_qk8", "gqa_attn_fwd_varlen", "gqa_attn_plan",
+                     "gqa_attn_strerror"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -177,6 +178,29 @@ def test_backward_argument_checks(kw, status):
                             P(a["dk"]), P(a["dv"]), a["B"], a["Sq"], a["Sk"], a["Hq"], a["Hk"], a["d"], a["causal"],
                             a["scale"], None)
     assert st == getattr(g, "GQA_ERR_" + status), (kw, st)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(qs=float("nan")), "INVALID_ARG"),
+    (dict(ks=float("inf")), "INVALID_ARG"),
+    (dict(Hq=6, Hk=4), "INVALID_ARG"),
+    (dict(scale=float("nan")), "INVALID_ARG"),
+    (dict(q=None), "INVALID_ARG"),
+    (dict(d=96), "UNSUPPORTED"),
+    (dict(k=1.0005), "UNSUPPORTED"),
+    (dict(q=None, k=None, v=None, out=None, B=0), "OK"),
+])
+def test_qk8_argument_checks(kw, status):
+    import grouped_query_exact_amd as g
+    a = dict(q=1, k=1, v=1, qs=1.0, ks=1.0, out=1, lse=None, B=1, Sq=8, Sk=8, Hq=4, Hk=2, d=64, causal=1,
+             scale=0.125, pack=-1, ns=0)
+    a.update(kw)
+    P = lambda x: None if x is None else ctypes.c_void_p(int(x * 4096))
+    st = lib().gqa_attn_fwd_qk8(P(a["q"]), P(a["k"]), P(a["v"]), a["qs"], a["ks"], P(a["out"]), P(a["lse"]), a["B"],
+                                a["Sq"], a["Sk"], a["Hq"], a["Hk"], a["d"], a["causal"], a["scale"], a["pack"],
+                                a["ns"], None)
+    want = g.GQA_OK if status == "OK" else getattr(g, "GQA_ERR_" + status)
+    assert st == want, (kw, st)
 
 
 def test_paged_misaligned_table_is_unsupported():

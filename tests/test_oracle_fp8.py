@@ -6,9 +6,12 @@
   (smallest subnormal), -0 = 0x80, NaN = 0x7F and 0xFF;
 * the factor identities: attention over k_scale * K equals attention over K
   with scale * k_scale, and v_scale multiplies the output and leaves the LSE;
-* the paged fp8 oracle equals the contiguous one on gathered sequences.
-Planted mistakes (exponent bias 8, a factor applied to the wrong tensor)
-each fail a pin.
+* the paged fp8 oracle equals the contiguous one on gathered sequences;
+* fp8 queries and keys: attention over q_scale * Q and k_scale * K equals
+  attention over the decoded Q and K with scale * q_scale * k_scale (signs
+  included), and unit factors give the plain attention of the decoded values.
+Planted mistakes (exponent bias 8, a factor applied to the wrong tensor,
+q_scale applied to V) each fail a pin.
 """
 
 import math
@@ -98,3 +101,32 @@ def test_planted_factor_on_wrong_tensor():
     except AssertionError:
         return
     raise AssertionError("the planted factor swap passed")
+
+
+def pin_qk_factors(attn_qk8):
+    B, Sq, Sk, Hq, Hk, d = 2, 5, 29, 6, 2, 16
+    q8, k8 = gi.random_fp8(21, (B, Sq, Hq, d)).numpy(), gi.random_fp8(22, (B, Sk, Hk, d)).numpy()
+    v = gi.random_bf16(23, (B, Sk, Hk, d)).to(torch.float64).numpy()
+    Q, K = ofp8.e4m3_to_float(q8), ofp8.e4m3_to_float(k8)
+    for causal in (False, True):
+        O1, L1 = attn_qk8(q8, k8, v, 1.0, 1.0, causal, 0.25)
+        O0, L0 = oracle.attention_fp64(Q, K, v, causal, 0.25)
+        assert np.allclose(O1, O0, rtol=0, atol=1e-13) and np.allclose(L1, L0, rtol=0, atol=1e-13)
+        for qs, ks in ((0.5, -1.25), (-3.0, 0.125)):
+            Of, Lf = attn_qk8(q8, k8, v, qs, ks, causal, 0.25)
+            Os, Ls = oracle.attention_fp64(Q, K, v, causal, 0.25 * qs * ks)
+            assert np.allclose(Of, Os, rtol=0, atol=1e-12) and np.allclose(Lf, Ls, rtol=0, atol=1e-12)
+
+
+def test_qk_factor_pin():
+    pin_qk_factors(oracle.attention_qk8_fp64)
+
+
+def test_planted_q_scale_on_values():
+    def bad(q8, k8, v, q_scale, k_scale, causal, scale, **kw):
+        return oracle.attention_qk8_fp64(q8, k8, np.asarray(v) * q_scale, 1.0, k_scale, causal, scale, **kw)
+    try:
+        pin_qk_factors(bad)
+    except AssertionError:
+        return
+    raise AssertionError("the planted factor on V passed")
