@@ -225,6 +225,18 @@ def main():
             sweep[f"B{B}_auto"] = {"ms": round(msb, 4), "tflops": round(wb.flops / (msb * 1e-3) / 1e12, 1),
                                    "pack": pl["pack_gqa"], "ns": pl["num_splits"]}
         extra["sweep"] = sweep
+        # the headline shape with Q and K in fp8 e4m3 (scores on the fp8 matrix cores, V and P V bf16)
+        q8 = qb[:128].to(torch.float8_e4m3fn).view(torch.uint8)
+        k8 = kb[:128].to(torch.float8_e4m3fn).view(torch.uint8)
+        o8 = torch.empty_like(qb[:128])
+        l8 = torch.empty((128, wb.Hq, wb.Sq), dtype=torch.float32, device=dev)
+        w128 = gi.sweep(128)
+        ms8, _ = time_calls(lambda: g.gqa_attn_fwd_qk8(q8, k8, vb[:128], 1.0, 1.0, o8, l8, w128.causal, w128.scale),
+                            max(5, args.steps // 5), 3)
+        extra["sweep_b128_fp8_qk"] = {"ms": round(ms8, 4), "tflops": round(w128.flops / (ms8 * 1e-3) / 1e12, 1),
+                                      "kernel": "attn_fwd_kernel (fp8 Q/K scores, bf16 P V)"}
+        print(f"[bench] fp8 Q/K sweep B=128: {ms8:.4f} ms", file=sys.stderr, flush=True)
+        del q8, k8, o8, l8
         del qb, kb, vb
         torch.cuda.empty_cache()
         # Llama-2 prefill shape
