@@ -12,8 +12,9 @@ Also measured in the same run and reported in the same JSON line (unless
 --quick): the rest of the sweep (B = 16, 64, 128, 256 with (pack 1, ns 1)
 and (pack 0, ns 4)), the Llama-2 prefill shape (B=4), and split-KV decode
 (B=64, Sq=1, Sk=8192) as HBM GB/s of Q+K+V+O+LSE bytes, the same decode
-over a paged cache and with fp8 K/V, a variable-length prefill batch, and
-the backward pass at the Llama-2 shape; those inputs are drawn on the GPU
+over a paged cache and with fp8 K/V, the headline shape with fp8 Q and K
+(scores on the fp8 matrix cores), a variable-length prefill batch, and the
+backward pass at the Llama-2 shape; those inputs are drawn on the GPU
 from N(0,1) (the timing does not depend on the values' seeds).
 
 cpu_baseline: the fp64 numpy oracle on a bounded sample (the first batch
