@@ -21,7 +21,9 @@ into <out-dir>/profiles/ (to be copied into profiles/):
     default steps and warm-up), whose average kernel time is the one
     bench.py reports;
   * attn_bwd_llama2_prefill_b4_s2048.md: trace and counters of the
-    backward kernels at the Llama-2 prefill shape (``--run-bwd``).
+    backward kernels at the Llama-2 prefill shape (``--run-bwd``);
+  * attn_fwd_qk8_sweep_b128_s2048.md: trace and counters of the forward
+    with fp8 Q and K at the headline shape (``--run-qk8``).
 
 It never touches the GPU itself; the profiled children do.
 """
@@ -50,6 +52,7 @@ KERNEL_NAMES = ("attn_fwd_kernel", "attn_decode_kernel", "combine_kernel")
 BWD_KERNEL_NAMES = ("bwd_dq_kernel", "bwd_dkdv_kernel")
 RUN_LAUNCHES = 4
 BWD_LAUNCHES = 20  # short kernels: enough calls for the average to be the steady state
+QK8_LAUNCHES = 15  # the first launches of a process run slow; these dominate the average
 
 # name -> (workload factory, pack_gqa, num_splits); -1 / 0 = the library's choice
 WORKLOADS = {
@@ -112,6 +115,61 @@ def run_backward():
         g.gqa_attn_bwd(q, k, v, out, lse, do, dq, dk, dv, w.causal, w.scale)
     torch.cuda.synchronize()
     print(json.dumps({"workload": "backward " + w.name, "launches": BWD_LAUNCHES}), flush=True)
+
+
+def run_qk8():
+    """QK8_LAUNCHES fp8 Q/K forward calls at the headline shape (inputs: the bf16 recipe rounded to e4m3)."""
+    import torch
+    import grouped_query_exact_amd as g
+    import gqa_inputs as gi
+    w = gi.sweep(128)
+    dev = torch.device("cuda:0")
+    q, k, v = gi.make_qkv_device(w, dev)
+    q8 = q.to(torch.float8_e4m3fn).view(torch.uint8)
+    del q
+    k8 = k.to(torch.float8_e4m3fn).view(torch.uint8)
+    del k
+    out = torch.empty((w.B, w.Sq, w.Hq, w.d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.B, w.Hq, w.Sq), dtype=torch.float32, device=dev)
+    for _ in range(QK8_LAUNCHES):
+        g.gqa_attn_fwd_qk8(q8, k8, v, 1.0, 1.0, out, lse, w.causal, w.scale)
+    torch.cuda.synchronize()
+    print(json.dumps({"workload": "fp8 Q/K " + w.name, "launches": QK8_LAUNCHES}), flush=True)
+
+
+def qk8_profile(out, prof_out, fetch_scale, write_scale):
+    """Kernel trace and HBM counters of the fp8 Q/K forward at the headline shape."""
+    import gqa_inputs as gi
+    w = gi.sweep(128)
+    cmd_t = rocprof(["--kernel-trace", "--stats"], out, "qk8_trace", ["--run-qk8"])
+    cmd_f = rocprof(["--pmc", "FETCH_SIZE"], out, "qk8_fetch", ["--run-qk8"])
+    cmd_w = rocprof(["--pmc", "WRITE_SIZE"], out, "qk8_write", ["--run-qk8"])
+    stats = [r for r in read_trace(out, "qk8_trace") if "attn_fwd_kernel" in r["Name"]]
+    fetch = attention_only(read_counter(out, "qk8_fetch", "FETCH_SIZE"))
+    write = attention_only(read_counter(out, "qk8_write", "WRITE_SIZE"))
+    qe = w.B * w.Sq * w.Hq * w.d
+    ke = w.B * w.Sk * w.Hk * w.d
+    alg = qe + ke + 2 * ke + 2 * qe + 4 * w.B * w.Hq * w.Sq  # Q, K fp8; V, O bf16; LSE fp32
+    md = [f"# {w.name} with fp8 Q and K: B={w.B}, Sq=Sk={w.Sq}, Hq={w.Hq}, Hk={w.Hk}, d={w.d}, causal={w.causal}", "",
+          f"{QK8_LAUNCHES} gqa_attn_fwd_qk8 calls (unit factors; the bf16 input recipe rounded to e4m3). "
+          f"Kernel source hash {kernel_hash()}.", "",
+          "Commands (REPO = repository root on the GPU box, run from /tmp with TMPDIR=/tmp):", "",
+          "    " + cmd_t.replace(ROOT, "$REPO"), "    " + cmd_f.replace(ROOT, "$REPO"),
+          "    " + cmd_w.replace(ROOT, "$REPO"), "", "Kernel trace (rocprofv3 --stats):", ""] + stats_table(stats)
+    for r in stats:
+        md += ["", f"Rate at the average time: {w.flops / (float(r['AverageNs']) * 1e-9) / 1e12:.1f} TFLOP/s "
+                   f"(the metric's flops, 4*B*Hq*Sq*Sk*d/2)."]
+    md += ["", f"HBM counters per dispatch (FETCH x{fetch_scale:.3f}, WRITE x{write_scale:.3f} from a 1 GiB copy):", "",
+           "| kernel | FETCH_SIZE (KiB) | WRITE_SIZE (KiB) | HBM bytes (scaled) |", "|---|---|---|---|"]
+    for kname in sorted(set(fetch) | set(write)):
+        f_kib = sum(fetch.get(kname, [0])) / max(1, len(fetch.get(kname, [1])))
+        w_kib = sum(write.get(kname, [0])) / max(1, len(write.get(kname, [1])))
+        md.append(f"| `{kname[:90]}` | {f_kib:.0f} | {w_kib:.0f} | "
+                  f"{(f_kib * 1024 * fetch_scale + w_kib * 1024 * write_scale) / 1e9:.4f} GB |")
+    md += ["", f"Algorithmic bytes (Q and K at one byte, V and O at two, LSE at four, each once): {alg / 1e9:.4f} GB.", ""]
+    with open(os.path.join(prof_out, f"attn_fwd_qk8_{w.name}.md"), "w") as f:
+        f.write("\n".join(md))
+    print("[traffic] fp8 Q/K profile written", flush=True)
 
 
 def run_copy():
@@ -238,6 +296,8 @@ def main():
     ap.add_argument("--run", help=argparse.SUPPRESS)
     ap.add_argument("--copy-ref", action="store_true", help=argparse.SUPPRESS)
     ap.add_argument("--run-bwd", action="store_true", help=argparse.SUPPRESS)
+    ap.add_argument("--run-qk8", action="store_true", help=argparse.SUPPRESS)
+    ap.add_argument("--skip-qk8", action="store_true")
     ap.add_argument("--skip-bench-trace", action="store_true")
     ap.add_argument("--skip-backward", action="store_true")
     ap.add_argument("--out-dir", default=os.path.join(ROOT, "gpurun_out", "traffic"))
@@ -249,6 +309,8 @@ def main():
         return run_copy()
     if a.run_bwd:
         return run_backward()
+    if a.run_qk8:
+        return run_qk8()
 
     out = os.path.abspath(a.out_dir)
     os.makedirs(out, exist_ok=True)
@@ -325,6 +387,8 @@ def main():
         json.dump(traffic, f, indent=1, sort_keys=True)
     if not a.skip_backward:
         backward_profile(out, prof_out, fetch_scale, write_scale)
+    if not a.skip_qk8:
+        qk8_profile(out, prof_out, fetch_scale, write_scale)
     if not a.skip_bench_trace:
         bench_trace(out, prof_out)
     print(f"[traffic] wrote {prof_out}", flush=True)
