@@ -1,0 +1,114 @@
+"""Seeded random shapes against the fp64 oracle (GPU): the bf16 forward, the fp8 Q/K forward, the fp8 K/V
+decode path and the backward, each on shapes drawn from one generator (batch 1-3, lengths 1-300 around
+the tile sizes, G in 1..8, Hk in 1..4, d in {64, 128}, causal or not, packing and splits drawn too).
+Every case is small enough for the oracle to finish in well under a second; tolerances as elsewhere.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import gqa_inputs as gi
+import oracle
+from _parity import TOL_LSE, TOL_O_MAX, TOL_O_MEAN, f64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def draw(seed):
+    rs = np.random.RandomState(seed)
+    B = int(rs.randint(1, 4))
+    Hk = int(rs.randint(1, 5))
+    G = int(rs.choice([1, 2, 3, 4, 5, 8]))
+    d = int(rs.choice([64, 128]))
+    Sq = int(rs.choice([1, 2, 7, 31, 32, 33, 63, 64, 65, 127, 128, 129, 200, 300]))
+    Sk = int(rs.choice([1, 5, 32, 63, 64, 65, 128, 129, 257, 300]))
+    causal = bool(rs.randint(0, 2))
+    pack = int(rs.choice([-1, 0, 1]))
+    ns = int(rs.choice([0, 1, 2, 3, 5]))
+    return B, Sq, Sk, G * Hk, Hk, d, causal, pack, ns
+
+
+def check(O, L, Or, Lr, tag):
+    Og = f64(O)
+    assert np.isfinite(Og).all(), f"{tag}: non-finite output"
+    dO = np.abs(Og - Or)
+    assert dO.max() <= TOL_O_MAX and dO.mean() <= TOL_O_MEAN, f"{tag}: max {dO.max()} mean {dO.mean()}"
+    Lg = f64(L)
+    fin = np.isfinite(Lr)
+    assert np.array_equal(fin, np.isfinite(Lg)), f"{tag}: LSE -inf pattern"
+    if fin.any():
+        assert np.abs(Lg[fin] - Lr[fin]).max() <= TOL_LSE, f"{tag}: LSE"
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_forward_bf16_and_fp8_qk(seed):
+    import grouped_query_exact_amd as g
+    B, Sq, Sk, Hq, Hk, d, causal, pack, ns = draw(11000 + seed)
+    tag = f"seed={seed} B={B} Sq={Sq} Sk={Sk} Hq={Hq} Hk={Hk} d={d} causal={causal} pack={pack} ns={ns}"
+    scale = gi.fp32(1 / math.sqrt(d))
+    q, k, v = gi.random_bf16(seed, (B, Sq, Hq, d)), gi.random_bf16(seed + 100, (B, Sk, Hk, d)), gi.random_bf16(seed + 200, (B, Sk, Hk, d))
+    out = torch.empty((B, Sq, Hq, d), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=DEV)
+    g.gqa_attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), out, lse, causal, scale, pack, ns)
+    torch.cuda.synchronize()
+    Or, Lr = oracle.attention_fp64(f64(q), f64(k), f64(v), causal, scale)
+    check(out, lse, Or, Lr, "bf16 " + tag)
+    q8, k8 = gi.to_fp8_bytes(q), gi.to_fp8_bytes(k)
+    qs, ks = 0.75, -1.5
+    g.gqa_attn_fwd_qk8(q8.to(DEV), k8.to(DEV), v.to(DEV), qs, ks, out, lse, causal, scale, pack, ns)
+    torch.cuda.synchronize()
+    Or, Lr = oracle.attention_qk8_fp64(q8.numpy(), k8.numpy(), f64(v), qs, ks, causal, scale)
+    check(out, lse, Or, Lr, "fp8 Q/K " + tag)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_decode_fp8_kv(seed):
+    import grouped_query_exact_amd as g
+    rs = np.random.RandomState(12000 + seed)
+    B, Hk, G = int(rs.randint(1, 5)), int(rs.randint(1, 5)), int(rs.choice([1, 2, 4, 8]))
+    d = int(rs.choice([64, 128]))
+    Sq = int(rs.choice([1, 2, 4])) if G <= 8 else 1
+    Sq = min(Sq, 32 // G)
+    Sk = int(rs.randint(1, 900))
+    causal, ns = bool(rs.randint(0, 2)), int(rs.choice([0, 1, 3]))
+    Hq = G * Hk
+    tag = f"seed={seed} B={B} Sq={Sq} Sk={Sk} Hq={Hq} Hk={Hk} d={d} causal={causal} ns={ns}"
+    q = gi.random_bf16(seed + 300, (B, Sq, Hq, d))
+    k8, v8 = gi.random_fp8(seed + 400, (B, Sk, Hk, d)), gi.random_fp8(seed + 500, (B, Sk, Hk, d))
+    out = torch.empty((B, Sq, Hq, d), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=DEV)
+    g.gqa_attn_fwd_kv8(q.to(DEV), k8.to(DEV), v8.to(DEV), 0.6, 1.7, out, lse, causal, gi.fp32(1 / math.sqrt(d)), -1, ns)
+    torch.cuda.synchronize()
+    Or, Lr = oracle.attention_kv8_fp64(f64(q), k8.numpy(), v8.numpy(), 0.6, 1.7, causal, gi.fp32(1 / math.sqrt(d)))
+    check(out, lse, Or, Lr, tag)
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_random_backward(seed):
+    import grouped_query_exact_amd as g
+    B, Sq, Sk, Hq, Hk, d, causal, _, _ = draw(13000 + seed)
+    tag = f"seed={seed} B={B} Sq={Sq} Sk={Sk} Hq={Hq} Hk={Hk} d={d} causal={causal}"
+    scale = gi.fp32(1 / math.sqrt(d))
+    q, k, v = gi.random_bf16(seed + 600, (B, Sq, Hq, d)), gi.random_bf16(seed + 700, (B, Sk, Hk, d)), gi.random_bf16(seed + 800, (B, Sk, Hk, d))
+    do = gi.random_bf16(seed + 900, (B, Sq, Hq, d))
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    out = torch.empty_like(qd)
+    lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=DEV)
+    g.gqa_attn_fwd(qd, kd, vd, out, lse, causal, scale)
+    grads = [torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)]
+    g.gqa_attn_bwd(qd, kd, vd, out, lse, do.to(DEV), *grads, causal, scale)
+    torch.cuda.synchronize()
+    ref = oracle.attention_bwd_fp64(f64(q), f64(k), f64(v), f64(do), causal, scale)
+    for name, gx, rx in zip(("dq", "dk", "dv"), grads, ref):
+        gx = f64(gx)
+        assert np.isfinite(gx).all(), f"{tag} {name}: non-finite"
+        m = np.abs(rx).max()
+        err = np.abs(gx - rx)
+        if m == 0:
+            assert err.max() == 0, f"{tag} {name}: expected zeros"
+            continue
+        assert err.max() <= 2e-2 * m and err.mean() <= 2e-3 * m, f"{tag} {name}: max {err.max() / m:.3e} mean {err.mean() / m:.3e}"
