@@ -18,15 +18,16 @@
 //    Q and dO rows in registers, dS in registers as the B operand of
 //    dQ^T += K^T dS^T, K^T read with the transposing LDS read. It also
 //    forms D of its rows and stores D and -LSE*log2(e) for the next kernel.
-//  * bwd_dkdv_kernel: 128 keys per workgroup of eight wavefronts, four for
-//    dK and four for dV, 32 keys each with their K (and V) rows in
-//    registers; the workgroup streams every query tile (32 packed rows of Q
-//    and dO) of the KV group through a ring of LDS stages, so dK and dV
-//    collect all G heads without atomics. S = Q K^T and dP = dO V^T come out
-//    of the matrix cores with one key per lane, which is already the
-//    A-operand layout of dV += P^T dO and dK += dS^T Q; dO and Q enter those
-//    products through the transposing LDS read, with their rows read in the
-//    order the score registers hold them.
+//  * bwd_dkdv_kernel: 128 keys per workgroup of eight wavefronts, a pair per
+//    32 keys: the dV wave holds the keys' K rows in registers, forms S and P
+//    and hands P to the dK wave (V rows in registers) through LDS one tile
+//    later. The workgroup streams every query tile (64 packed rows of Q and
+//    dO, last tile first) of the KV group through a ring of LDS stages, so
+//    dK and dV collect all G heads without atomics. S = Q K^T and
+//    dP = dO V^T come out of the matrix cores with one key per lane, which
+//    is already the A-operand layout of dV += P^T dO and dK += dS^T Q; dO
+//    and Q enter those products through the transposing LDS read, with their
+//    rows read in the order the score registers hold them.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
