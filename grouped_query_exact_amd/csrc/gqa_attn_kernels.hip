@@ -43,6 +43,11 @@
 //  * Workgroup ids are remapped so that consecutive work items (all row tiles
 //    of one batch element and KV group, heaviest causal tiles first) land on
 //    the same XCD and share its L2.
+//  * With fp8 e4m3 Q and K (QK8) the scores run on the fp8 matrix cores
+//    (32x32x64 products, 2 per 32 keys at d=128 instead of 8) from an fp8 K
+//    tile; V, P V and everything after the scores are the bf16 path's.
+// The decode kernel further down takes head units of at most 32 rows (one
+// wavefront, a deeper ring, optional paged or fp8 K/V).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
