@@ -1,7 +1,8 @@
 """Seeded random shapes against the fp64 oracle (GPU): the bf16 forward, the fp8 Q/K forward, the fp8 K/V
-decode path and the backward, each on shapes drawn from one generator (batch 1-3, lengths 1-300 around
-the tile sizes, G in 1..8, Hk in 1..4, d in {64, 128}, causal or not, packing and splits drawn too).
-Every case is small enough for the oracle to finish in well under a second; tolerances as elsewhere.
+decode path, the backward, variable-length batches and paged decode, each on shapes drawn from seeded
+generators (batch 1-3, lengths 0-900 around the tile sizes, G in 1..8, Hk in 1..4, d in {64, 128}, causal
+or not, packing, splits, page sizes and factors drawn too). Every case is small enough for the oracle to
+finish in well under a second; tolerances as elsewhere.
 """
 
 import math
@@ -112,3 +113,60 @@ def test_random_backward(seed):
             assert err.max() == 0, f"{tag} {name}: expected zeros"
             continue
         assert err.max() <= 2e-2 * m and err.mean() <= 2e-3 * m, f"{tag} {name}: max {err.max() / m:.3e} mean {err.mean() / m:.3e}"
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_varlen(seed):
+    """Packed sequences with drawn lengths (empty ones included), chunked-prefill lengths (fewer queries
+    than keys) and decode-shaped batches, drawn packing and splits."""
+    import grouped_query_exact_amd as g
+    rs = np.random.RandomState(14000 + seed)
+    nseq = int(rs.randint(1, 7))
+    Hk, G, d = int(rs.randint(1, 4)), int(rs.choice([1, 2, 3, 4, 8])), int(rs.choice([64, 128]))
+    lk = [int(x) for x in rs.choice([0, 1, 17, 64, 65, 130, 300], size=nseq)]
+    if rs.randint(0, 2):
+        lq = [min(x, int(rs.choice([1, 2, 4]))) for x in lk]  # decode-shaped / short chunks
+    else:
+        lq = [int(min(x, rs.randint(0, x + 1))) for x in lk]  # chunked prefill: up to the key count
+    if max(lk) == 0:
+        lk[0] = 5
+    causal, pack, ns = bool(rs.randint(0, 2)), int(rs.choice([-1, 0, 1])), int(rs.choice([0, 1, 3]))
+    Hq = G * Hk
+    q, k, v, cq, ck = gi.varlen_batch(14000 + seed, lq, lk, Hq, Hk, d)
+    tag = f"seed={seed} lq={lq} lk={lk} Hq={Hq} Hk={Hk} d={d} causal={causal} pack={pack} ns={ns}"
+    if sum(lq) == 0:
+        return
+    scale = gi.fp32(1 / math.sqrt(d))
+    out = torch.empty((sum(lq), Hq, d), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((Hq, sum(lq)), dtype=torch.float32, device=DEV)
+    g.gqa_attn_fwd_varlen(q.to(DEV), k.to(DEV), v.to(DEV), out, lse, cq.to(DEV), ck.to(DEV), max(max(lq), 1),
+                          max(max(lk), 1), causal, scale, pack, ns)
+    torch.cuda.synchronize()
+    Or, Lr = oracle.attention_varlen_fp64(f64(q), f64(k), f64(v), cq.tolist(), ck.tolist(), causal, scale)
+    check(out, lse, Or, Lr, tag)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_paged_decode(seed):
+    import grouped_query_exact_amd as g
+    rs = np.random.RandomState(15000 + seed)
+    nseq = int(rs.randint(1, 6))
+    Hk, G, d = int(rs.randint(1, 4)), int(rs.choice([1, 2, 4, 8])), int(rs.choice([64, 128]))
+    Sq = min(int(rs.choice([1, 2, 4])), 32 // G)
+    ps = int(rs.choice([16, 32, 48, 64, 128]))
+    lens = [int(x) for x in rs.randint(0, 700, size=nseq)]
+    causal, ns = bool(rs.randint(0, 2)), int(rs.choice([0, 1, 3]))
+    Hq = G * Hk
+    kv = gi.paged_kv(15000 + seed, lens, ps, Hk, d, spare_pages=int(rs.randint(0, 4)))
+    q = gi.random_bf16(15100 + seed, (nseq, Sq, Hq, d))
+    tag = f"seed={seed} lens={lens} ps={ps} Sq={Sq} Hq={Hq} Hk={Hk} d={d} causal={causal} ns={ns}"
+    kvd = kv.to(DEV)
+    out = torch.empty((nseq, Sq, Hq, d), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((nseq, Hq, Sq), dtype=torch.float32, device=DEV)
+    scale = gi.fp32(1 / math.sqrt(d))
+    g.gqa_attn_fwd_paged(q.to(DEV), kvd.k_cache, kvd.v_cache, kvd.block_table, kvd.seqlens_k, out, lse, causal, scale,
+                         -1, ns)
+    torch.cuda.synchronize()
+    Or, Lr = oracle.attention_paged_fp64(f64(q), f64(kv.k_cache), f64(kv.v_cache), kv.block_table.numpy(),
+                                         kv.seqlens_k.numpy(), causal, scale)
+    check(out, lse, Or, Lr, tag)
