@@ -278,9 +278,12 @@ int gqa_attn_bwd(const void* q, const void* k, const void* v, const void* out, c
         int st = gqa::check_sizes(s, scale, -1, 0);
         if (st != GQA_OK) return st;
         if ((long long)B * Sq == 0 && (long long)B * Sk == 0) return GQA_OK;
-        if (!q || !k || !v || !out || !lse || !dout || !dq || !dk || !dv) return GQA_ERR_INVALID_ARG;
-        if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(dout) || !aligned16(dq) ||
-            !aligned16(dk) || !aligned16(dv) || !aligned4(lse))
+        // without query rows only dK = dV = 0 is written (from k and v's shapes): the
+        // query-side pointers may be null then
+        const bool has_rows = (long long)B * Sq > 0;
+        if (!k || !v || !dk || !dv || (has_rows && (!q || !out || !lse || !dout || !dq))) return GQA_ERR_INVALID_ARG;
+        if (!aligned16(k) || !aligned16(v) || !aligned16(dk) || !aligned16(dv) ||
+            (has_rows && (!aligned16(q) || !aligned16(out) || !aligned16(dout) || !aligned16(dq) || !aligned4(lse))))
             return GQA_ERR_UNSUPPORTED;
         // per-batch byte offsets of the query tiles are 32-bit
         if ((long long)Sq * Hq * d * 2 > 0x7FFFFFFFLL || (long long)Hq * Sq * 4 > 0x7FFFFFFFLL) return GQA_ERR_INVALID_ARG;

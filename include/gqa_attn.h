@@ -102,7 +102,8 @@ int gqa_attn_fwd(const void* q, const void* k, const void* v, void* out, float* 
  * out and lse must come from gqa_attn_fwd on the same inputs. The library
  * allocates a stream-ordered fp32 workspace of 2*B*Hq*Sq values (D and the
  * log-sum-exp in base 2). dq, dk
- * and dv are overwritten (keys no query sees get 0). Same validation,
+ * and dv are overwritten (keys no query sees get 0). With B*Sq == 0 only
+ * dK = dV = 0 is written and q, out, lse, dout and dq may be null. Same validation,
  * alignment and stream rules as gqa_attn_fwd; additionally Sq*Hq*d*2 must
  * be below 2^31. */
 int gqa_attn_bwd(const void* q, const void* k, const void* v, const void* out, const float* lse,

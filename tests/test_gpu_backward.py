@@ -114,3 +114,20 @@ def test_backward_key_gradients_sum_to_zero_full_size():
     colsum = dk.double().sum(dim=1)                # [B, Hk, d]
     scale_ref = dk.double().abs().sum(dim=1)
     assert float((colsum.abs() / scale_ref).max()) < 2e-2
+
+
+def test_backward_without_queries():
+    """Sq = 0: no query sees any key, so dK = dV = 0 (written over NaN-filled outputs); the query-side
+    tensors are empty (null pointers)."""
+    import grouped_query_exact_amd as g
+    B, Sk, Hq, Hk, d = 2, 50, 8, 2, 128
+    q = torch.empty((B, 0, Hq, d), dtype=torch.bfloat16, device=DEV)
+    k, v = gi.random_bf16(6400, (B, Sk, Hk, d)).to(DEV), gi.random_bf16(6401, (B, Sk, Hk, d)).to(DEV)
+    out, do, dq = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    lse = torch.empty((B, Hq, 0), dtype=torch.float32, device=DEV)
+    dk = torch.full_like(k, float("nan"))
+    dv = torch.full_like(v, float("nan"))
+    for causal in (False, True):
+        g.gqa_attn_bwd(q, k, v, out, lse, do, dq, dk, dv, causal, 0.125)
+        torch.cuda.synchronize()
+        assert torch.all(dk == 0) and torch.all(dv == 0), f"causal={causal}"

@@ -167,6 +167,8 @@ def test_varlen_argument_checks(kw, status):
     (dict(d=96), "UNSUPPORTED"),
     (dict(lse=1.0005), "UNSUPPORTED"),
     (dict(dk=1.0005), "UNSUPPORTED"),
+    (dict(Sq=0, q=None, out=None, lse=None, do=None, dq=None, k=None), "INVALID_ARG"),   # no rows: k still needed
+    (dict(Sq=0, q=None, out=None, lse=None, do=None, dq=None, dv=1.0005), "UNSUPPORTED"),
 ])
 def test_backward_argument_checks(kw, status):
     import grouped_query_exact_amd as g
