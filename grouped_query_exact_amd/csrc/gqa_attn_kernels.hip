@@ -370,12 +370,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
     };
 
+    // both stages are free at the start: the first two tiles are copied
+    // together (for short items the second tile's latency is not exposed)
     if (t_begin < t_end) issue(t_begin * kBlockN, 0);
+    if (t_begin + 1 < t_end) issue((t_begin + 1) * kBlockN, 1);
     for (int t = t_begin; t < t_end; ++t) {
         const int buf = (t - t_begin) & 1;
         wait_vmem();
         __syncthreads();
-        if (t + 1 < t_end) issue((t + 1) * kBlockN, buf ^ 1);
+        if (t > t_begin && t + 1 < t_end) issue((t + 1) * kBlockN, buf ^ 1);
         const int kv0 = t * kBlockN;
         // waves whose rows see none of these keys skip the arithmetic
         if (wave_active && !(CAUSAL && kv0 > iw_max + koff)) {
