@@ -201,7 +201,8 @@ def main():
         "wall_s_timed": round(wall, 4),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                     "kernel": "attn_fwd_kernel<d=128,causal,unsplit>" if plan["num_splits"] == 1
+                     "kernel": ("attn_fwd_pingpong_kernel<d=128,causal>" if plan["threads"] == 512
+                                else "attn_fwd_kernel<d=128,causal,unsplit>") if plan["num_splits"] == 1
                      else "attn_fwd_kernel<d=128,causal,split> + combine_kernel",
                      "flops_per_launch": w.flops},
     }

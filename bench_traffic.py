@@ -48,7 +48,7 @@ KERNEL_SRCS = [os.path.join(ROOT, "grouped_query_exact_amd", "csrc", f)
                for f in ("gqa_attn_kernels.hip", "device_common.h", "kernels.h", "host_logic.h")]
 PROFILES = os.path.join(ROOT, "profiles")
 COPY_BYTES = 1 << 30
-KERNEL_NAMES = ("attn_fwd_kernel", "attn_decode_kernel", "combine_kernel")
+KERNEL_NAMES = ("attn_fwd_kernel", "attn_fwd_pingpong_kernel", "attn_decode_kernel", "combine_kernel")
 BWD_KERNEL_NAMES = ("bwd_dq_kernel", "bwd_dkdv_kernel")
 RUN_LAUNCHES = 4
 BWD_LAUNCHES = 20  # short kernels: enough calls for the average to be the steady state

@@ -38,7 +38,7 @@ class _Plan(ctypes.Structure):
     _fields_ = [("pack_gqa", ctypes.c_int), ("num_splits", ctypes.c_int), ("block_m", ctypes.c_int),
                 ("block_n", ctypes.c_int), ("row_tiles", ctypes.c_int), ("key_tiles", ctypes.c_int),
                 ("grid", ctypes.c_longlong), ("combine_grid", ctypes.c_longlong),
-                ("workspace_bytes", ctypes.c_longlong)]
+                ("workspace_bytes", ctypes.c_longlong), ("threads", ctypes.c_int)]
 
 
 class GqaAttnError(RuntimeError):

@@ -91,7 +91,7 @@ int gqa_attn_plan(int B, int Sq, int Sk, int Hq, int Hk, int d, int causal, int 
     const gqa::Shape s{B, Sq, Sk, Hq, Hk, d, causal ? 1 : 0};
     int st = gqa::check_sizes(s, 1.0f, pack_gqa, num_splits);
     if (st != GQA_OK) return st;
-    if (num_cus <= 0 && (pack_gqa < 0 || num_splits == 0)) num_cus = device_cus(current_device());
+    if (num_cus <= 0) num_cus = device_cus(current_device());  // 0 without a device: make_plan assumes 256
     gqa::Plan p;
     st = gqa::make_plan(s, pack_gqa, num_splits, num_cus, &p);
     if (st != GQA_OK) return st;
@@ -104,6 +104,7 @@ int gqa_attn_plan(int B, int Sq, int Sk, int Hq, int Hk, int d, int causal, int 
     plan->grid = p.grid;
     plan->combine_grid = p.combine_grid;
     plan->workspace_bytes = p.workspace_bytes;
+    plan->threads = p.threads;
     return GQA_OK;
 }
 
@@ -139,8 +140,7 @@ int run(const Call& c) {
     const int d = s.d;
     const int dev = current_device();
     if (dev < 0) return GQA_ERR_HIP;
-    int cus = 0;
-    if (c.pack_gqa < 0 || c.num_splits == 0) cus = device_cus(dev);
+    const int cus = device_cus(dev);  // cached per device
     gqa::Plan plan;
     int st = gqa::make_plan(s, c.pack_gqa, c.num_splits, cus, &plan);
     if (st != GQA_OK) return st;
@@ -206,10 +206,11 @@ int run(const Call& c) {
                      "[gqa_attn] B=%d Sq=%d Sk=%d Hq=%d Hk=%d d=%d causal=%d paged=%d kv8=%d -> pack=%d ns=%d "
                      "kernel=%s row_tiles=%d key_tiles=%d grid=%lld combine_grid=%lld ws=%lld\n",
                      s.B, s.Sq, s.Sk, s.Hq, s.Hk, d, s.causal, c.paged ? 1 : 0, c.kv8 ? 1 : 0, plan.pack, plan.ns,
-                     plan.decode ? "decode" : "tiled", plan.row_tiles, plan.key_tiles, plan.grid,
+                     plan.decode ? "decode" : (plan.pingpong ? "tiled8" : "tiled"), plan.row_tiles, plan.key_tiles, plan.grid,
                      plan.combine_grid, plan.workspace_bytes);
 
     auto launch = [&](bool split) {
+        if (plan.pingpong) return gqa::launch_pingpong(p, d, s.causal != 0, c.stream);  // unsplit only
         return plan.decode ? gqa::launch_decode(p, d, s.causal != 0, split, c.paged, c.kv8, c.varlen, c.stream)
                            : gqa::launch_attention(p, d, s.causal != 0, split, c.varlen, c.qk8, c.stream);
     };
@@ -344,7 +345,7 @@ int gqa_attn_fwd_varlen(const void* q, const void* k, const void* v, void* out, 
                         float scale, int pack_gqa, int num_splits, hipStream_t stream) {
     try {
         if (total_q < 0 || total_k < 0) return GQA_ERR_INVALID_ARG;
-        const gqa::Shape s{B, max_seqlen_q, max_seqlen_k, Hq, Hk, d, causal ? 1 : 0};
+        const gqa::Shape s{B, max_seqlen_q, max_seqlen_k, Hq, Hk, d, causal ? 1 : 0, 2, 2, 1};
         int st = gqa::check_sizes(s, scale, pack_gqa, num_splits);
         if (st != GQA_OK) return st;
         if ((long long)B * max_seqlen_q == 0 || total_q == 0) return GQA_OK;

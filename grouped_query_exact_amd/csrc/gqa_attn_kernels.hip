@@ -430,6 +430,312 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
 }
 
+// Large prefill launches (unsplit bf16 calls with enough work items to fill
+// the GPU): the same per-row arithmetic as attn_fwd_kernel, bit for bit, on a
+// workgroup of 8 wavefronts and 256 packed rows that owns its compute unit.
+// The hardware places wavefronts w and w+4 of a workgroup on the same SIMD,
+// so waves 0-3 (group A) and 4-7 (group B) pair up per SIMD. Every key tile t
+// takes two phases separated by workgroup barriers; in each phase one group
+// issues matrix products and the other group runs its softmax, then they swap:
+//
+//   phase 2t  : A: S(t) = K(t) Q^T, then O += V(t-1)^T P(t-1)   B: softmax(t-1)
+//   phase 2t+1: A: softmax(t)                                  B: S(t), O += V(t-1)^T P(t-1)
+//
+// so the SIMD's matrix core always has one wavefront feeding it while the
+// other one works on its exponentials. The wavefront in its product phase
+// raises its issue priority (s_setprio) so the softmax wavefront's VALU work
+// does not delay its products. S(t)'s K operands are read from LDS eight
+// products ahead. K/V tiles stream through a ring of kPPStages LDS stages by
+// global_load_lds: the copies of tile t+2 go into the stage of tile t-2
+// (whose last readers finished in phase 2t-1), issued by each group during
+// its softmax phase of tile t, and a workgroup waits only for tile t's copies
+// at its top. Causal masking, the row/key bookkeeping, the lazy online
+// softmax in base 2 and the epilogue are those of attn_fwd_kernel.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_pingpong_kernel(
+    const FwdParams p) {
+    constexpr int TILE = kBlockN * D;
+    constexpr int TILE_B = TILE * 2;
+    constexpr int NCH = D / 8;
+    constexpr int NLOAD = kBlockN * NCH / kPPThreads;  // 16-byte copies per thread per tensor and tile
+    constexpr int NS = kPPStages;
+    constexpr int COPIES = 2 * NLOAD;
+    static_assert(NS == 4, "the stage reuse and the wait counts below assume 4 stages");
+    static_assert(kPPThreads == 512 && kPPBlockM == 256, "8 wavefronts of 32 rows");
+    __shared__ __attribute__((aligned(16))) uint16_t smem[NS * 2 * TILE];
+    LDS char* lds = (LDS char*)smem;
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = wave >> 2;
+    const int lane = tid & 63;
+    const int col = lane & 31, half = lane >> 5;
+
+    // ---- work item: (batch, head unit, row tile descending), XCD-contiguous
+    const int logical = xcd_remap(blockIdx.x, p.grid);
+    const int rt = p.row_tiles - 1 - (logical % p.row_tiles);
+    const int tmpu = logical / p.row_tiles;
+    const int unit = tmpu % p.units_per_b;
+    const int b = tmpu / p.units_per_b;
+    const int g = p.Gp > 1 ? unit : unit / p.G;
+    const int h0 = p.Gp > 1 ? unit * p.G : unit;
+    const int r0 = rt * kPPBlockM;
+    const int Sq = p.Sq, Sk = p.Sk;
+    const int64_t qtok0 = (int64_t)b * Sq, ktok0 = (int64_t)b * Sk;
+    const int R = p.R;
+
+    // ---- this lane's row: token ti, head hh
+    const int r = r0 + wave * 32 + col;
+    const bool row_valid = r < R;
+    const int rc = min(r, R - 1);
+    const int ti = (int)fdiv((uint32_t)rc, p.gmul, p.gshift);
+    const int hh = h0 + (rc - ti * p.Gp);
+    const int koff = Sk - Sq;  // bottom-right causal offset
+
+    // ---- key tiles of the item and of this wavefront's rows
+    const int r_last = min(r0 + kPPBlockM, R) - 1;
+    const int i_max = (int)fdiv((uint32_t)r_last, p.gmul, p.gshift);
+    int kv_end = Sk;
+    if (CAUSAL) kv_end = min(Sk, i_max + koff + 1);
+    const int nt = kv_end > 0 ? (kv_end + kBlockN - 1) / kBlockN : 0;
+    const int rw0 = r0 + wave * 32;
+    const bool wave_active = rw0 < R;
+    const int iw_min = (int)fdiv((uint32_t)min(rw0, R - 1), p.gmul, p.gshift);
+    const int iw_max = (int)fdiv((uint32_t)(min(rw0 + 32, R) - 1), p.gmul, p.gshift);
+
+    // ---- K/V tile copies: fixed per-thread 16-byte chunks, scalar tile base
+    const int64_t kv_stride_b = (int64_t)p.Hk * D * 2;
+    const char* kbase = (const char*)(p.k + (ktok0 * p.Hk + g) * D);
+    const char* vbase = (const char*)(p.v + (ktok0 * p.Hk + g) * D);
+    uint32_t goff[NLOAD];
+#pragma unroll
+    for (int u = 0; u < NLOAD; ++u) {
+        const int ci = (u * 8 + wave) * 64 + lane;
+        const int row = ci / NCH;
+        const int logical_ch = (ci % NCH) ^ swz<D>(row);
+        goff[u] = (uint32_t)(row * kv_stride_b + logical_ch * 16);
+    }
+    // the LDS destination is uniform; it is passed through a scalar register
+    auto stage_dst = [&](int stage, int tensor, int u) __attribute__((always_inline)) {
+        const uint32_t a = (uint32_t)(size_t)(lds + (stage & (NS - 1)) * 2 * TILE_B + tensor * TILE_B) + (u * 8 + wave) * 1024;
+        return (LDS void*)(size_t)__builtin_amdgcn_readfirstlane(a);
+    };
+    auto issue = [&](int t) __attribute__((always_inline)) {
+        const int kv0 = t * kBlockN;
+        const char* kg = kbase + kv0 * kv_stride_b;
+        const char* vg = vbase + kv0 * kv_stride_b;
+        if (kv0 + kBlockN <= Sk) {
+#pragma unroll
+            for (int u = 0; u < NLOAD; ++u) {
+                lds_dma16(kg, goff[u], stage_dst(t, 0, u));
+                lds_dma16(vg, goff[u], stage_dst(t, 1, u));
+            }
+        } else {  // ragged last tile: rows past the end re-read the last key (masked later)
+#pragma unroll
+            for (int u = 0; u < NLOAD; ++u) {
+                const int ci = (u * 8 + wave) * 64 + lane;
+                const int row = ci / NCH;
+                const int logical_ch = (ci % NCH) ^ swz<D>(row);
+                const int key = min(kv0 + row, Sk - 1) - kv0;
+                const uint32_t off = (uint32_t)(key * kv_stride_b + logical_ch * 16);
+                lds_dma16(kg, off, stage_dst(t, 0, u));
+                lds_dma16(vg, off, stage_dst(t, 1, u));
+            }
+        }
+    };
+
+    // ---- prologue: tile 0, the Q rows (B operand of S^T = K Q^T), tile 1
+    if (nt > 0) issue(0);
+    bf16x8 qreg[D / 16];
+    {
+        const uint16_t* qrow = p.q + ((qtok0 + ti) * p.Hq + hh) * D;
+#pragma unroll
+        for (int dc = 0; dc < D / 16; ++dc) {
+            u32x4 w = *(const u32x4*)(qrow + dc * 16 + half * 8);
+            w = (w & p.qand) ^ p.qsign;
+            qreg[dc] = __builtin_bit_cast(bf16x8, w);
+        }
+    }
+    // wait for Q here, before the tile loop, so that no wait on it lands inside
+#pragma unroll
+    for (int dc = 0; dc < D / 16; ++dc) asm volatile("" ::"v"(qreg[dc]));
+    if (nt > 1) issue(1);
+
+    // ---- per-lane LDS operand offsets (as in attn_fwd_kernel)
+    const int krow0 = pi32(col);
+    uint32_t kofs[D / 16];
+#pragma unroll
+    for (int dc = 0; dc < D / 16; ++dc) kofs[dc] = krow0 * (D * 2) + (((2 * dc + half) ^ swz<D>(krow0)) * 16);
+    const int u16 = lane & 15, qq = (lane >> 4) & 1;
+    const int rho = ((u16 & 1) << 1) | ((u16 >> 1) & 1);
+    uint32_t vofs[D / 32][2];
+#pragma unroll
+    for (int cb = 0; cb < D / 32; ++cb)
+#pragma unroll
+        for (int rr = 0; rr < 2; ++rr) {
+            const int vrow = half * 8 + rr * 4 + (u16 >> 2);
+            const int vcol = cb * 32 + qq * 16 + rho * 4;
+            vofs[cb][rr] = vrow * (D * 2) + (((vcol >> 3) ^ swz<D>(vrow)) * 16) + (vcol & 7) * 2;
+        }
+
+    f32x16 oacc[D / 32];
+#pragma unroll
+    for (int cb = 0; cb < D / 32; ++cb) oacc[cb] = f32x16{};
+    float m_run = -__builtin_inff();  // running max, scaled log2 units
+    float l_part[4] = {0.f, 0.f, 0.f, 0.f};
+    const float c = p.c;
+    const int jlim = CAUSAL ? min(Sk - 1, ti + koff) : Sk - 1;  // last key visible to this row
+    f32x16 sacc[2];  // S(t): from the product phase to the softmax phase
+    bf16x8 pk[4];    // P(t): from the softmax phase to the next product phase
+
+    // waves whose rows see none of tile t's keys skip its arithmetic (monotone in t)
+    auto act = [&](int t) __attribute__((always_inline)) {
+        return wave_active && !(CAUSAL && t * kBlockN > iw_max + koff);
+    };
+    auto s_part = [&](int t) __attribute__((always_inline)) {
+        const LDS char* kt = lds + (t & (NS - 1)) * 2 * TILE_B;
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) sacc[mb] = f32x16{};
+#pragma unroll
+        for (int dc = 0; dc < D / 16; ++dc)
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb) {
+                const bf16x8 a = *(const LDS bf16x8*)(kt + kofs[dc] + mb * 32 * D * 2);
+                sacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[dc], sacc[mb], 0, 0, 0);
+            }
+        // the operand reads run eight ahead of the products
+        constexpr int NR = D / 8, PRE = 8;
+        __builtin_amdgcn_sched_group_barrier(0x100, PRE, 0);
+#pragma unroll
+        for (int i = 0; i < (NR - PRE) / 2; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, PRE, 0);
+    };
+    auto pv_part = [&](int t) __attribute__((always_inline)) {
+        const LDS char* vt = lds + (t & (NS - 1)) * 2 * TILE_B + TILE_B;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+            for (int cb = 0; cb < D / 32; ++cb) {
+                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS s16x4*)(vt + vofs[cb][0] + kk * 16 * D * 2));
+                const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS s16x4*)(vt + vofs[cb][1] + kk * 16 * D * 2));
+                const s16x8 av = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                oacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), pk[kk], oacc[cb], 0, 0, 0);
+            }
+    };
+    auto softmax = [&](int t) __attribute__((always_inline)) {
+        const int kv0 = t * kBlockN;
+        const bool need_mask = (kv0 + kBlockN > Sk) || (CAUSAL && kv0 + kBlockN - 1 > iw_min + koff);
+        // keys of this lane's slots: kv0 + 32*mb + 16*(i/8) + 8*half + (i%8)
+        if (need_mask) {
+            const int lim = jlim - kv0 - half * 8;
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    if (mb * 32 + ((i >> 3) << 4) + (i & 7) > lim) sacc[mb][i] = -__builtin_inff();
+        }
+        float mx;
+        {
+            float t0 = fmaxf(fmaxf(sacc[0][0], sacc[0][1]), sacc[0][2]);
+            float t1 = fmaxf(fmaxf(sacc[0][3], sacc[0][4]), sacc[0][5]);
+            float t2 = fmaxf(fmaxf(sacc[0][6], sacc[0][7]), sacc[0][8]);
+            float t3 = fmaxf(fmaxf(sacc[0][9], sacc[0][10]), sacc[0][11]);
+            t0 = fmaxf(fmaxf(t0, sacc[0][12]), sacc[0][13]);
+            t1 = fmaxf(fmaxf(t1, sacc[0][14]), sacc[0][15]);
+            t2 = fmaxf(fmaxf(t2, sacc[1][0]), sacc[1][1]);
+            t3 = fmaxf(fmaxf(t3, sacc[1][2]), sacc[1][3]);
+            t0 = fmaxf(fmaxf(t0, sacc[1][4]), sacc[1][5]);
+            t1 = fmaxf(fmaxf(t1, sacc[1][6]), sacc[1][7]);
+            t2 = fmaxf(fmaxf(t2, sacc[1][8]), sacc[1][9]);
+            t3 = fmaxf(fmaxf(t3, sacc[1][10]), sacc[1][11]);
+            t0 = fmaxf(fmaxf(t0, sacc[1][12]), sacc[1][13]);
+            t1 = fmaxf(fmaxf(t1, sacc[1][14]), sacc[1][15]);
+            mx = xhalf_max(fmaxf(fmaxf(t0, t1), fmaxf(t2, t3)));
+        }
+        // lazy running-max update; O holds every product up to tile t-1 here
+        const float mxs = (mx == -__builtin_inff()) ? -__builtin_inff() : mx * c;
+        float alpha = 1.f;
+        if (mxs > m_run + kRescaleThreshold) {
+            alpha = __builtin_amdgcn_exp2f(m_run - mxs);  // exp2(-inf) = 0 on the first update
+            m_run = mxs;
+        }
+        if (__ballot(alpha != 1.f)) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) l_part[i] *= alpha;
+#pragma unroll
+            for (int cb = 0; cb < D / 32; ++cb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) oacc[cb][i] *= alpha;
+        }
+        const float moff = (m_run == -__builtin_inff()) ? 0.f : m_run;
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mb][i], c, -moff));
+                l_part[i & 3] += x;
+                pk[mb * 2 + (i >> 3)][i & 7] = (__bf16)x;
+            }
+    };
+    auto product_phase = [&](int t) __attribute__((always_inline)) {
+        __builtin_amdgcn_s_setprio(1);
+        if (t < nt && act(t)) s_part(t);
+        if (t > 0 && act(t - 1)) pv_part(t - 1);
+        __builtin_amdgcn_s_setprio(0);
+    };
+    // softmax phase of tile t (any t in [-1, nt]); the copies of tile t+2 go first
+    auto softmax_phase = [&](int t_copy, int t_soft) __attribute__((always_inline)) {
+        if (t_copy + NS - 2 < nt) issue(t_copy + NS - 2);
+        if (t_soft >= 0 && t_soft < nt && act(t_soft)) softmax(t_soft);
+    };
+    // top of tile t: this thread's copies of tile t have landed (at most tile
+    // t+1's copies are still in flight), then the barrier publishes the tile
+    // and frees the stage of tile t-2
+    auto top = [&](int t) __attribute__((always_inline)) {
+        if (t < nt) {
+            if (t + 1 < nt) wait_vmem_n<COPIES>();
+            else wait_vmem();
+        }
+        __syncthreads();
+    };
+    // the two groups run separate copies of the loop, so the compiler never
+    // merges two versions of the accumulators at a branch join
+    auto run = [&](auto is_b) __attribute__((always_inline)) {
+        for (int t = 0; t <= nt; ++t) {
+            top(t);
+            if (!decltype(is_b)::value) product_phase(t);
+            else softmax_phase(t, t - 1);
+            __syncthreads();
+            if (!decltype(is_b)::value) softmax_phase(t, t);
+            else product_phase(t);
+        }
+    };
+    if (grp == 0) run(std::false_type{});
+    else run(std::true_type{});
+
+    // ---- epilogue
+    const float l_tot = xhalf_sum((l_part[0] + l_part[1]) + (l_part[2] + l_part[3]));
+    const bool live = l_tot > 0.f;
+    const float inv = live ? 1.f / l_tot : 0.f;
+    const float lse_val = live ? (m_run + __log2f(l_tot)) * kLn2 : -__builtin_inff();
+    if (row_valid) {
+        uint16_t* orow = p.o + ((qtok0 + ti) * p.Hq + hh) * D;
+#pragma unroll
+        for (int cb = 0; cb < D / 32; ++cb)
+#pragma unroll
+            for (int run2 = 0; run2 < 2; ++run2) {
+                bf16x8 ov;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) ov[i] = (__bf16)(oacc[cb][run2 * 8 + i] * inv);
+                *(bf16x8*)(orow + cb * 32 + run2 * 16 + half * 8) = ov;
+            }
+        if (half == 0 && p.lse) p.lse[((int64_t)b * p.Hq + hh) * Sq + ti] = lse_val;
+    }
+}
+
 // Decode-shaped work (the pages' decode regime: one or a few new tokens per
 // sequence against a long KV cache, bound by reading K and V from HBM): a
 // head unit has at most 32 query rows (with PackGQA, the G query heads of a
@@ -829,6 +1135,17 @@ static hipError_t launch_attn_dd(const FwdParams& p, bool causal, bool split, bo
 hipError_t launch_attention(const FwdParams& p, int d, bool causal, bool split, bool varlen, bool qk8, hipStream_t stream) {
     return d == 128 ? launch_attn_dd<128>(p, causal, split, varlen, qk8, stream)
                     : launch_attn_dd<64>(p, causal, split, varlen, qk8, stream);
+}
+
+hipError_t launch_pingpong(const FwdParams& p, int d, bool causal, hipStream_t stream) {
+    if (d == 128) {
+        if (causal) hipLaunchKernelGGL((attn_fwd_pingpong_kernel<128, true>), dim3(p.grid), dim3(kPPThreads), 0, stream, p);
+        else hipLaunchKernelGGL((attn_fwd_pingpong_kernel<128, false>), dim3(p.grid), dim3(kPPThreads), 0, stream, p);
+    } else {
+        if (causal) hipLaunchKernelGGL((attn_fwd_pingpong_kernel<64, true>), dim3(p.grid), dim3(kPPThreads), 0, stream, p);
+        else hipLaunchKernelGGL((attn_fwd_pingpong_kernel<64, false>), dim3(p.grid), dim3(kPPThreads), 0, stream, p);
+    }
+    return hipGetLastError();
 }
 
 template <int D, bool CAUSAL, bool SPLIT, bool PAGED, bool KV8, bool VARLEN>

@@ -101,6 +101,18 @@ int make_plan(const Shape& s, int pack_gqa, int num_splits, int num_cus, Plan* p
     p->key_tiles = p->R > 0 ? key_tiles_for(s, p->Gp, p->R, p->block_n) : 0;
     ns = std::max(1, std::min(ns, std::max(1, p->key_tiles)));
     p->ns = ns;
+    // unsplit bf16 calls with enough 256-row items to give every compute
+    // unit kPPMinItemsPerCU of them run on the 8-wavefront kernel
+    p->pingpong = 0;
+    if (!p->decode && ns == 1 && s.q_bytes == 2 && s.kv_bytes == 2 && !s.varlen) {
+        const long long items = (long long)s.B * p->units_per_b * ceil_div(p->R, kPPBlockM);
+        if (items >= (long long)kPPMinItemsPerCU * (num_cus > 0 ? num_cus : 256)) p->pingpong = 1;
+    }
+    if (p->pingpong) {
+        p->block_m = kPPBlockM;
+        p->row_tiles = (int)ceil_div(p->R, kPPBlockM);
+    }
+    p->threads = p->decode ? kDecThreads : (p->pingpong ? kPPThreads : kThreads);
     p->grid = (long long)s.B * p->units_per_b * p->row_tiles * ns;
     if (p->grid > INT_MAX) return GQA_ERR_INVALID_ARG;
     const long long rows = (long long)s.B * s.Sq * s.Hq;

@@ -13,6 +13,16 @@ constexpr int kBlockM = 128;
 constexpr int kBlockN = 64;
 constexpr int kThreads = 256;
 
+// Large unsplit bf16 prefill launches: 8 wavefronts own 256 packed rows and
+// a compute unit, in two groups that alternate between matrix products and
+// softmax, with a ring of kPPStages K/V stages (128 KiB of LDS at d=128).
+// Chosen when the call has at least kPPMinItemsPerCU such work items per
+// compute unit; smaller grids keep the 4-wavefront kernel, two per CU.
+constexpr int kPPBlockM = 256;
+constexpr int kPPThreads = 512;
+constexpr int kPPStages = 4;
+constexpr int kPPMinItemsPerCU = 2;
+
 // Decode-shaped launches (at most kDecBlockM query rows per head unit, e.g.
 // one new token of a KV group): one wavefront per workgroup streaming tiles
 // of kDecBlockN keys through a ring of kDecStages LDS stages.
@@ -54,6 +64,7 @@ struct Shape {
     int B, Sq, Sk, Hq, Hk, d, causal;
     int kv_bytes = 2;  // bytes per stored K/V element: 2 (bf16) or 1 (fp8)
     int q_bytes = 2;   // bytes per stored Q element: 2 (bf16) or 1 (fp8 Q and K: tiled kernel only)
+    int varlen = 0;    // packed sequences of different lengths (4-wavefront tiled or decode kernel)
 };
 
 // Returns 0 or a gqa_status_t error for the sizes alone (no pointers).
@@ -64,6 +75,8 @@ void choose(const Shape& s, int num_cus, int* pack_gqa, int* num_splits);
 
 struct Plan {
     int decode;         // 1: decode kernel (R <= kDecBlockM), 0: tiled kernel
+    int pingpong;       // 1: the 8-wavefront tiled kernel (kPPBlockM rows), 0: 4 wavefronts
+    int threads;        // threads per attention workgroup
     int block_m;        // query rows per tile
     int block_n;        // keys per tile
     int pack;           // resolved pack flag

@@ -249,6 +249,9 @@ typedef struct {
     long long grid;        /* workgroups of the attention kernel */
     long long combine_grid;/* workgroups of the combine kernel (0 if none) */
     long long workspace_bytes; /* split-KV workspace (0 if num_splits == 1) */
+    int threads;           /* threads per attention workgroup: 64 (decode-shaped calls),
+                              256 (tiled, 128-row tiles) or 512 (large unsplit bf16
+                              calls: 256-row tiles, one workgroup per compute unit) */
 } gqa_attn_plan_t;
 
 /* Resolve pack_gqa / num_splits exactly as gqa_attn_fwd would and describe

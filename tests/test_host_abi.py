@@ -252,6 +252,14 @@ def test_plan_grid_and_workspace():
     assert p["block_n"] == 64
     assert p["row_tiles"] * p["block_m"] >= 2048 * 4
     assert p["grid"] == 128 * 8 * p["row_tiles"]
+    # large unsplit bf16 calls: 8 wavefronts, 256-row tiles, one workgroup per compute unit
+    assert (p["block_m"], p["threads"], p["row_tiles"], p["grid"]) == (256, 512, 32, 32768)
+    # ... only with at least two such items per compute unit (212 * 2 = 424 < 512 here)
+    p = g.gqa_attn_plan(212, 77, 77, 6, 2, 64, False, 1, 1, 256)
+    assert (p["block_m"], p["threads"], p["grid"]) == (128, 256, 212 * 2 * 2)
+    assert g.gqa_attn_plan(212, 77, 77, 6, 2, 64, False, 1, 1, 128)["threads"] == 512
+    # split calls stay on the 4-wavefront kernel
+    assert g.gqa_attn_plan(128, 2048, 2048, 32, 8, 128, True, 1, 2, 256)["threads"] == 256
     p = g.gqa_attn_plan(16, 2048, 2048, 32, 8, 128, True, 0, 4, 256)
     assert p["pack_gqa"] == 0 and p["num_splits"] == 4
     assert p["grid"] == 16 * 32 * p["row_tiles"] * 4
@@ -264,7 +272,7 @@ def test_plan_grid_and_workspace():
     assert p["num_splits"] == 2 and p["key_tiles"] == 2 and p["block_m"] == 128
     # decode-shaped work (at most 32 query rows per head unit) uses 32 x 32 tiles
     p = g.gqa_attn_plan(64, 1, 8192, 32, 8, 128, False, -1, 0, 256)
-    assert (p["block_m"], p["block_n"], p["key_tiles"], p["grid"]) == (32, 32, 256, 512)
+    assert (p["block_m"], p["block_n"], p["key_tiles"], p["grid"], p["threads"]) == (32, 32, 256, 512, 64)
     p = g.gqa_attn_plan(2, 9, 300, 32, 8, 128, True, 1, 1, 256)
     assert p["block_m"] == 128 and p["row_tiles"] == 1  # 36 packed rows
     # a single-head group never packs
@@ -307,7 +315,11 @@ int main() {
         if (make_plan(s, pk, ns, 256, &p) != GQA_OK) { std::printf("plan failed\n"); return 1; }
         if (p.ns < 1 || p.ns > (p.key_tiles > 0 ? p.key_tiles : 1)) { std::printf("bad ns\n"); return 1; }
         if ((long long)p.row_tiles * p.block_m < p.R || (long long)(p.row_tiles - 1) * p.block_m >= p.R) { std::printf("bad row tiles\n"); return 1; }
-        if (p.decode != (p.R <= kDecBlockM) || p.block_m != (p.decode ? kDecBlockM : kBlockM)) { std::printf("bad kernel choice\n"); return 1; }
+        if (p.decode != (p.R <= kDecBlockM)) { std::printf("bad kernel choice\n"); return 1; }
+        const long long items8 = (long long)B * p.units_per_b * ((p.R + kPPBlockM - 1) / kPPBlockM);
+        if (p.pingpong != (!p.decode && p.ns == 1 && items8 >= 2LL * 256)) { std::printf("bad 8-wave choice\n"); return 1; }
+        if (p.block_m != (p.decode ? kDecBlockM : (p.pingpong ? kPPBlockM : kBlockM))) { std::printf("bad block_m\n"); return 1; }
+        if (p.threads != (p.decode ? kDecThreads : (p.pingpong ? kPPThreads : kThreads))) { std::printf("bad threads\n"); return 1; }
         if (p.grid != (long long)B * p.units_per_b * p.row_tiles * p.ns) { std::printf("bad grid\n"); return 1; }
     }
     std::printf("ok %lld\n", checked);
