@@ -39,7 +39,11 @@
  * per-device cache of the compute-unit count.
  *
  * Calls are asynchronous with respect to the host and never synchronize the
- * stream. They are thread-safe. No C++ exception crosses this boundary.
+ * stream. They are thread-safe. No C++ exception crosses this boundary. A
+ * forward call whose split count resolves to 1 enqueues exactly one kernel
+ * and nothing else (no allocation, memset or copy), so it can be captured in
+ * a HIP graph and replayed; split calls also enqueue the workspace
+ * allocation, the combine kernel and the release of the workspace.
  */
 #ifndef GQA_ATTN_H
 #define GQA_ATTN_H
