@@ -58,21 +58,26 @@ void choose(const Shape& s, int num_cus, int* pack_gqa, int* num_splits) {
     *pack_gqa = pack;
 
     // Split the keys when the grid is too small to fill the GPU. The tiled
-    // kernel wants two workgroups per compute unit. The decode kernel (at
-    // most 32 rows, memory-bound) also wants two per compute unit, each with
-    // kDecStages-1 tiles in flight: measured on MI355X, more and shorter
-    // workgroups only add tail and merge costs. With fp8 K/V its tiles cost
-    // more arithmetic per byte and four per compute unit are best.
+    // kernel wants two workgroups per compute unit. The bf16 decode kernel
+    // (at most 32 rows, memory-bound, kDecStages-1 tiles in flight per
+    // workgroup) is split only up to one workgroup per compute unit: measured
+    // on MI355X from one sequence against 128K keys to 64 sequences against
+    // 8K, that count is the fastest, and more, shorter workgroups add tail and
+    // merge costs (a single sequence needs up to 32 splits for it). With fp8
+    // K/V its tiles cost more arithmetic per byte and four per compute unit
+    // are best.
     const int Gp = pack ? G : 1;
     const long long R = (long long)s.Sq * Gp;
     const bool decode = R <= kDecBlockM && s.q_bytes == 2;
     const int bm = decode ? kDecBlockM : kBlockM, bn = decode ? kDecBlockN : kBlockN;
     const long long units = (long long)s.B * (pack ? s.Hk : s.Hq) * ceil_div(R, bm);
     const int T = R > 0 ? key_tiles_for(s, Gp, R, bn) : 0;
-    const long long target = (decode && s.kv_bytes == 1 ? 4LL : 2LL) * num_cus;
+    const bool dec16 = decode && s.kv_bytes == 2;
+    const long long target = (decode ? (s.kv_bytes == 1 ? 4LL : 1LL) : 2LL) * num_cus;
+    const int cap = dec16 ? 64 : 16;
     int ns = 1;
     if (units > 0 && units < target && T > 1) {
-        ns = (int)std::min<long long>(ceil_div(target, units), 16);
+        ns = (int)std::min<long long>(ceil_div(target, units), cap);
         ns = std::max(1, std::min(ns, T / 2 > 0 ? T / 2 : 1));
     }
     *num_splits = ns;
@@ -103,10 +108,19 @@ int make_plan(const Shape& s, int pack_gqa, int num_splits, int num_cus, Plan* p
     p->ns = ns;
     // unsplit bf16 calls with enough 256-row items to give every compute
     // unit kPPMinItemsPerCU of them run on the 8-wavefront kernel
+    // (or one per compute unit when the items are long: an estimated average
+    // of at least kPPMinKeyTiles key tiles, from the first and last row tile)
     p->pingpong = 0;
     if (!p->decode && ns == 1 && s.q_bytes == 2 && s.kv_bytes == 2 && !s.varlen) {
         const long long items = (long long)s.B * p->units_per_b * ceil_div(p->R, kPPBlockM);
-        if (items >= (long long)kPPMinItemsPerCU * (num_cus > 0 ? num_cus : 256)) p->pingpong = 1;
+        const long long cus = num_cus > 0 ? num_cus : 256;
+        if (items >= (long long)kPPMinItemsPerCU * cus) {
+            p->pingpong = 1;
+        } else if (items >= cus) {
+            const int first = key_tiles_for(s, p->Gp, std::min<long long>(p->R, kPPBlockM), kBlockN);
+            const int last = key_tiles_for(s, p->Gp, p->R, kBlockN);
+            if ((long long)first + last >= 2LL * kPPMinKeyTiles) p->pingpong = 1;
+        }
     }
     if (p->pingpong) {
         p->block_m = kPPBlockM;

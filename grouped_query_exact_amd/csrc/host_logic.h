@@ -17,11 +17,13 @@ constexpr int kThreads = 256;
 // a compute unit, in two groups that alternate between matrix products and
 // softmax, with a ring of kPPStages K/V stages (128 KiB of LDS at d=128).
 // Chosen when the call has at least kPPMinItemsPerCU such work items per
-// compute unit; smaller grids keep the 4-wavefront kernel, two per CU.
+// compute unit, or one per compute unit with kPPMinKeyTiles key tiles per
+// item on average; smaller grids keep the 4-wavefront kernel, two per CU.
 constexpr int kPPBlockM = 256;
 constexpr int kPPThreads = 512;
 constexpr int kPPStages = 4;
 constexpr int kPPMinItemsPerCU = 2;
+constexpr int kPPMinKeyTiles = 32;
 
 // Decode-shaped launches (at most kDecBlockM query rows per head unit, e.g.
 // one new token of a KV group): one wavefront per workgroup streaming tiles

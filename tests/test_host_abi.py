@@ -234,10 +234,16 @@ def test_choose_heuristic_shapes():
     # short ragged sequences (Sq=77 fills 60% of a 128-row tile, 3 heads packed fill 90%)
     assert g.gqa_attn_choose(212, 77, 77, 6, 2, 64, False, 256)[0] == 1
     # decode: one query row per head -> pack; 64 x 8 groups already give two
-    # workgroups per compute unit, 8 x 8 groups need the keys split
+    # workgroups per compute unit; fewer groups split the keys up to one
+    # workgroup per compute unit (8 x 8 groups: 4 splits), up to 64 splits
     assert g.gqa_attn_choose(64, 1, 8192, 32, 8, 128, False, 256) == (1, 1)
     pk, ns = g.gqa_attn_choose(8, 1, 8192, 32, 8, 128, False, 256)
-    assert pk == 1 and ns == 8
+    assert pk == 1 and ns == 4
+    assert g.gqa_attn_choose(4, 1, 131072, 32, 8, 128, False, 256) == (1, 8)
+    assert g.gqa_attn_choose(1, 1, 131072, 32, 8, 128, False, 256) == (1, 32)
+    assert g.gqa_attn_choose(1, 1, 131072, 4, 4, 128, False, 256) == (0, 64)
+    # ... but at least two 32-key tiles per split
+    assert g.gqa_attn_choose(1, 1, 1024, 32, 8, 128, False, 256) == (1, 16)
     # MHA: nothing to pack
     assert g.gqa_attn_choose(8, 512, 512, 8, 8, 64, True, 256)[0] == 0
     # invalid sizes are reported
@@ -258,6 +264,11 @@ def test_plan_grid_and_workspace():
     p = g.gqa_attn_plan(212, 77, 77, 6, 2, 64, False, 1, 1, 256)
     assert (p["block_m"], p["threads"], p["grid"]) == (128, 256, 212 * 2 * 2)
     assert g.gqa_attn_plan(212, 77, 77, 6, 2, 64, False, 1, 1, 128)["threads"] == 512
+    # one item per compute unit suffices when the items are long (an average of >= 32 key tiles):
+    # a 2048-token chunk against 65536 keys and a non-causal 2048 x 2048 call do, a causal one does not
+    assert g.gqa_attn_plan(1, 2048, 65536, 32, 8, 128, True, 1, 1, 256)["threads"] == 512
+    assert g.gqa_attn_plan(1, 2048, 2048, 32, 8, 128, False, 1, 1, 256)["threads"] == 512
+    assert g.gqa_attn_plan(1, 2048, 2048, 32, 8, 128, True, 1, 1, 256)["threads"] == 256
     # split calls stay on the 4-wavefront kernel
     assert g.gqa_attn_plan(128, 2048, 2048, 32, 8, 128, True, 1, 2, 256)["threads"] == 256
     p = g.gqa_attn_plan(16, 2048, 2048, 32, 8, 128, True, 0, 4, 256)
@@ -282,6 +293,7 @@ def test_plan_grid_and_workspace():
 CPP_TEST = r"""
 #include "host_logic.h"
 #include "../../include/gqa_attn.h"
+#include <algorithm>
 #include <cstdio>
 #include <cstdlib>
 #include <random>
@@ -317,7 +329,14 @@ int main() {
         if ((long long)p.row_tiles * p.block_m < p.R || (long long)(p.row_tiles - 1) * p.block_m >= p.R) { std::printf("bad row tiles\n"); return 1; }
         if (p.decode != (p.R <= kDecBlockM)) { std::printf("bad kernel choice\n"); return 1; }
         const long long items8 = (long long)B * p.units_per_b * ((p.R + kPPBlockM - 1) / kPPBlockM);
-        if (p.pingpong != (!p.decode && p.ns == 1 && items8 >= 2LL * 256)) { std::printf("bad 8-wave choice\n"); return 1; }
+        auto kt = [&](long long r1) -> long long {  // key tiles of a row tile ending at row r1
+            long long kv_end = Sk;
+            if (causal) kv_end = std::min<long long>(Sk, (r1 - 1) / p.Gp + (Sk - Sq) + 1);
+            return kv_end <= 0 ? 0 : (kv_end + kBlockN - 1) / kBlockN;
+        };
+        const bool long_items = kt(std::min<long long>(p.R, kPPBlockM)) + kt(p.R) >= 2LL * kPPMinKeyTiles;
+        const bool want8 = !p.decode && p.ns == 1 && (items8 >= 2LL * 256 || (items8 >= 256 && long_items));
+        if (p.pingpong != want8) { std::printf("bad 8-wave choice\n"); return 1; }
         if (p.block_m != (p.decode ? kDecBlockM : (p.pingpong ? kPPBlockM : kBlockM))) { std::printf("bad block_m\n"); return 1; }
         if (p.threads != (p.decode ? kDecThreads : (p.pingpong ? kPPThreads : kThreads))) { std::printf("bad threads\n"); return 1; }
         if (p.grid != (long long)B * p.units_per_b * p.row_tiles * p.ns) { std::printf("bad grid\n"); return 1; }
