@@ -2,7 +2,9 @@
 decode path, the backward, variable-length batches and paged decode, each on shapes drawn from seeded
 generators (batch 1-3, lengths 0-900 around the tile sizes, G in 1..8, Hk in 1..4, d in {64, 128}, causal
 or not, packing, splits, page sizes and factors drawn too). Every case is small enough for the oracle to
-finish in well under a second; tolerances as elsewhere.
+finish in well under a second; tolerances as elsewhere. A last group draws shapes with enough work items
+for the 8-wavefront prefill kernel (the batch size follows from the drawn lengths and heads) and checks
+it bit for bit against the 4-wavefront kernel and against the oracle on two batch elements.
 """
 
 import math
@@ -170,3 +172,47 @@ def test_random_paged_decode(seed):
     Or, Lr = oracle.attention_paged_fp64(f64(q), f64(kv.k_cache), f64(kv.v_cache), kv.block_table.numpy(),
                                          kv.seqlens_k.numpy(), causal, scale)
     check(out, lse, Or, Lr, tag)
+
+
+def draw8(seed):
+    """A shape with at least 512 items of 256 packed rows (the 8-wavefront prefill kernel)."""
+    rs = np.random.RandomState(seed)
+    Hk = int(rs.choice([1, 2, 4]))
+    G = int(rs.choice([1, 2, 3, 4, 8]))
+    d = int(rs.choice([64, 128]))
+    Sq = int(rs.choice([200, 255, 256, 257, 300, 511, 512, 513, 700, 1025]))
+    Sk = int(rs.choice([63, 64, 65, 199, 300, 511, 513, 1024, 1100]))
+    causal = bool(rs.randint(0, 2))
+    pack = 1 if G > 1 and rs.randint(0, 3) else 0
+    units = Hk if pack else G * Hk
+    rt8 = -(-(Sq * (G if pack else 1)) // 256)
+    B = -(-512 // (units * rt8)) + int(rs.randint(0, 3))
+    return B, Sq, Sk, G * Hk, Hk, d, causal, pack
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_forward_8_wavefront(seed):
+    """The 8-wavefront kernel on seeded shapes: bit for bit the 4-wavefront kernel (reached through the
+    variable-length entry point with equal lengths) on every row, the oracle on two batch elements."""
+    import grouped_query_exact_amd as g
+    B, Sq, Sk, Hq, Hk, d, causal, pack = draw8(12000 + seed)
+    tag = f"seed={seed} B={B} Sq={Sq} Sk={Sk} Hq={Hq} Hk={Hk} d={d} causal={causal} pack={pack}"
+    assert g.gqa_attn_plan(B, Sq, Sk, Hq, Hk, d, causal, pack, 1, 0)["threads"] == 512, tag
+    scale = gi.fp32(1 / math.sqrt(d))
+    q, k, v = gi.random_bf16(seed + 300, (B, Sq, Hq, d)), gi.random_bf16(seed + 400, (B, Sk, Hk, d)), gi.random_bf16(seed + 500, (B, Sk, Hk, d))
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    out = torch.empty((B, Sq, Hq, d), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=DEV)
+    g.gqa_attn_fwd(qd, kd, vd, out, lse, causal, scale, pack, 1)
+    o4 = torch.empty((B * Sq, Hq, d), dtype=torch.bfloat16, device=DEV)
+    l4 = torch.empty((Hq, B * Sq), dtype=torch.float32, device=DEV)
+    cq = torch.arange(0, (B + 1) * Sq, Sq, dtype=torch.int32, device=DEV)
+    ck = torch.arange(0, (B + 1) * Sk, Sk, dtype=torch.int32, device=DEV)
+    g.gqa_attn_fwd_varlen(qd.view(B * Sq, Hq, d), kd.view(B * Sk, Hk, d), vd.view(B * Sk, Hk, d), o4, l4, cq, ck,
+                          Sq, Sk, causal, scale, pack, 1)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(B * Sq, Hq, d), o4), "O " + tag
+    assert torch.equal(lse.permute(1, 0, 2).reshape(Hq, B * Sq), l4), "LSE " + tag
+    sel = sorted({0, B - 1})
+    Or, Lr = oracle.attention_fp64(f64(q[sel]), f64(k[sel]), f64(v[sel]), causal, scale)
+    check(out[sel], lse[sel], Or, Lr, tag)
