@@ -1076,6 +1076,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
 // Merge of split partials: LSE = M + ln sum_s exp(LSE_s - M) with
 // M = max_s LSE_s, O = sum_s exp(LSE_s - LSE) O_s. A row whose splits are all
 // empty gets O = 0 and LSE = -inf. One row per D/4 lanes, 4 columns a lane.
+// The loops over the splits are unrolled so that eight loads are in flight
+// at once (with few rows and many splits, as in single-sequence decode, the
+// kernel is bound by load latency); the sums keep their split order.
 template <int D>
 __global__ __launch_bounds__(256) void combine_kernel(const CombineParams p) {
     constexpr int LPR = D / 4;
@@ -1084,13 +1087,16 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombineParams p) {
     const int c4 = threadIdx.x % LPR;
     if (row >= p.rows) return;
     float M = -__builtin_inff();
+#pragma unroll 8
     for (int s = 0; s < p.ns; ++s) M = fmaxf(M, p.lpart[(int64_t)s * p.rows + row]);
     f32x4 acc = f32x4{};
     float lse = -__builtin_inff();
     if (M != -__builtin_inff()) {
         float tot = 0.f;
+#pragma unroll 8
         for (int s = 0; s < p.ns; ++s) tot += __expf(p.lpart[(int64_t)s * p.rows + row] - M);
         lse = M + __logf(tot);
+#pragma unroll 8
         for (int s = 0; s < p.ns; ++s) {
             const float ls = p.lpart[(int64_t)s * p.rows + row];
             const float w = __expf(ls - lse);  // exp(-inf) = 0 for empty splits
