@@ -430,8 +430,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
 }
 
-// Large prefill launches (unsplit bf16 calls with enough work items to fill
-// the GPU): the same per-row arithmetic as attn_fwd_kernel, bit for bit, on a
+// Large prefill launches (unsplit bf16 calls at d=128 with enough work items
+// to fill the GPU): the same per-row arithmetic as attn_fwd_kernel, bit for bit, on a
 // workgroup of 8 wavefronts and 256 packed rows that owns its compute unit.
 // The hardware places wavefronts w and w+4 of a workgroup on the same SIMD,
 // so waves 0-3 (group A) and 4-7 (group B) pair up per SIMD. Every key tile t
@@ -1143,14 +1143,11 @@ hipError_t launch_attention(const FwdParams& p, int d, bool causal, bool split, 
                     : launch_attn_dd<64>(p, causal, split, varlen, qk8, stream);
 }
 
+// d=128 only (the plan never picks this kernel at d=64)
 hipError_t launch_pingpong(const FwdParams& p, int d, bool causal, hipStream_t stream) {
-    if (d == 128) {
-        if (causal) hipLaunchKernelGGL((attn_fwd_pingpong_kernel<128, true>), dim3(p.grid), dim3(kPPThreads), 0, stream, p);
-        else hipLaunchKernelGGL((attn_fwd_pingpong_kernel<128, false>), dim3(p.grid), dim3(kPPThreads), 0, stream, p);
-    } else {
-        if (causal) hipLaunchKernelGGL((attn_fwd_pingpong_kernel<64, true>), dim3(p.grid), dim3(kPPThreads), 0, stream, p);
-        else hipLaunchKernelGGL((attn_fwd_pingpong_kernel<64, false>), dim3(p.grid), dim3(kPPThreads), 0, stream, p);
-    }
+    if (d != 128) return hipErrorInvalidValue;
+    if (causal) hipLaunchKernelGGL((attn_fwd_pingpong_kernel<128, true>), dim3(p.grid), dim3(kPPThreads), 0, stream, p);
+    else hipLaunchKernelGGL((attn_fwd_pingpong_kernel<128, false>), dim3(p.grid), dim3(kPPThreads), 0, stream, p);
     return hipGetLastError();
 }
 

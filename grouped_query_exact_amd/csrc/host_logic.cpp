@@ -106,12 +106,12 @@ int make_plan(const Shape& s, int pack_gqa, int num_splits, int num_cus, Plan* p
     p->key_tiles = p->R > 0 ? key_tiles_for(s, p->Gp, p->R, p->block_n) : 0;
     ns = std::max(1, std::min(ns, std::max(1, p->key_tiles)));
     p->ns = ns;
-    // unsplit bf16 calls with enough 256-row items to give every compute
-    // unit kPPMinItemsPerCU of them run on the 8-wavefront kernel
+    // unsplit bf16 calls at d=128 with enough 256-row items to give every
+    // compute unit kPPMinItemsPerCU of them run on the 8-wavefront kernel
     // (or one per compute unit when the items are long: an estimated average
     // of at least kPPMinKeyTiles key tiles, from the first and last row tile)
     p->pingpong = 0;
-    if (!p->decode && ns == 1 && s.q_bytes == 2 && s.kv_bytes == 2 && !s.varlen) {
+    if (!p->decode && ns == 1 && s.d == 128 && s.q_bytes == 2 && s.kv_bytes == 2 && !s.varlen) {
         const long long items = (long long)s.B * p->units_per_b * ceil_div(p->R, kPPBlockM);
         const long long cus = num_cus > 0 ? num_cus : 256;
         if (items >= (long long)kPPMinItemsPerCU * cus) {

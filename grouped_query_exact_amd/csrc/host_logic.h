@@ -13,7 +13,9 @@ constexpr int kBlockM = 128;
 constexpr int kBlockN = 64;
 constexpr int kThreads = 256;
 
-// Large unsplit bf16 prefill launches: 8 wavefronts own 256 packed rows and
+// Large unsplit bf16 prefill launches at d=128 (at d=64 the 4-wavefront
+// kernel fits four wavefronts per SIMD and is as fast or faster, measured):
+// 8 wavefronts own 256 packed rows and
 // a compute unit, in two groups that alternate between matrix products and
 // softmax, with a ring of kPPStages K/V stages (128 KiB of LDS at d=128).
 // Chosen when the call has at least kPPMinItemsPerCU such work items per

@@ -1,8 +1,8 @@
 """The 8-wavefront prefill kernel against the fp64 oracle and, bit for bit,
 against the 4-wavefront tiled kernel (GPU).
 
-Unsplit bf16 calls with at least two 256-row work items per compute unit run
-on the 8-wavefront kernel. The shapes below sit just past that threshold (512
+Unsplit bf16 calls at d=128 with at least two 256-row work items per compute
+unit run on the 8-wavefront kernel. The shapes below sit just past that threshold (512
 or more items on 256 compute units), so the oracle compares every element.
 Variable-length calls always use the 4-wavefront kernel: a batch of
 equal-length sequences through gqa_attn_fwd_varlen gives that kernel's result
@@ -25,7 +25,7 @@ DEV = "cuda:0"
 SHAPES = [
     (64, 256, 256, 8, 2, 128, 1),  # 4 full row tiles per group, 4 full key tiles
     (64, 200, 333, 8, 2, 128, 1),  # ragged rows (800 = 3 tiles + 32) and keys (5 tiles + 13), Sq != Sk
-    (64, 300, 300, 6, 2, 64, 1),   # G = 3, d = 64
+    (64, 300, 300, 6, 2, 128, 1),  # G = 3
     (32, 512, 448, 8, 2, 128, 0),  # unpacked: 2 row tiles per head
     (64, 300, 100, 8, 2, 128, 1),  # causal: tokens 0..199 see no key (bottom-right alignment)
 ]

@@ -263,7 +263,10 @@ def test_plan_grid_and_workspace():
     # ... only with at least two such items per compute unit (212 * 2 = 424 < 512 here)
     p = g.gqa_attn_plan(212, 77, 77, 6, 2, 64, False, 1, 1, 256)
     assert (p["block_m"], p["threads"], p["grid"]) == (128, 256, 212 * 2 * 2)
-    assert g.gqa_attn_plan(212, 77, 77, 6, 2, 64, False, 1, 1, 128)["threads"] == 512
+    assert g.gqa_attn_plan(212, 77, 77, 6, 2, 128, False, 1, 1, 128)["threads"] == 512
+    # d=64 keeps the 4-wavefront kernel
+    assert g.gqa_attn_plan(212, 77, 77, 6, 2, 64, False, 1, 1, 128)["threads"] == 256
+    assert g.gqa_attn_plan(64, 2048, 2048, 32, 8, 64, True, 1, 1, 256)["threads"] == 256
     # one item per compute unit suffices when the items are long (an average of >= 32 key tiles):
     # a 2048-token chunk against 65536 keys and a non-causal 2048 x 2048 call do, a causal one does not
     assert g.gqa_attn_plan(1, 2048, 65536, 32, 8, 128, True, 1, 1, 256)["threads"] == 512
@@ -335,7 +338,7 @@ int main() {
             return kv_end <= 0 ? 0 : (kv_end + kBlockN - 1) / kBlockN;
         };
         const bool long_items = kt(std::min<long long>(p.R, kPPBlockM)) + kt(p.R) >= 2LL * kPPMinKeyTiles;
-        const bool want8 = !p.decode && p.ns == 1 && (items8 >= 2LL * 256 || (items8 >= 256 && long_items));
+        const bool want8 = !p.decode && p.ns == 1 && s.d == 128 && (items8 >= 2LL * 256 || (items8 >= 256 && long_items));
         if (p.pingpong != want8) { std::printf("bad 8-wave choice\n"); return 1; }
         if (p.block_m != (p.decode ? kDecBlockM : (p.pingpong ? kPPBlockM : kBlockM))) { std::printf("bad block_m\n"); return 1; }
         if (p.threads != (p.decode ? kDecThreads : (p.pingpong ? kPPThreads : kThreads))) { std::printf("bad threads\n"); return 1; }
