@@ -1117,6 +1117,68 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombineParams p) {
     }
 }
 
+// Many splits (single-sequence decode against a long context takes up to
+// 128): one workgroup of 256 threads per row. Thread t takes columns
+// 4*(t % (D/4)) .. +3 of the splits s = t / (D/4) + k*SG (SG split groups),
+// so a row's ns partials are read SG at a time instead of one after the
+// other; the groups' maxima, sums and weighted sums are merged through LDS:
+// LSE = M + ln T and O = A / T with M = max_s LSE_s, T = sum_s exp(LSE_s - M),
+// A = sum_s exp(LSE_s - M) O_s. A row whose keys all lie in one split gets
+// that split's O and LSE exactly, as from combine_kernel.
+template <int D>
+__global__ __launch_bounds__(256) void combine_wide_kernel(const CombineParams p) {
+    constexpr int LPR = D / 4;    // lanes per split group (4 columns each)
+    constexpr int SG = 256 / LPR; // split groups
+    __shared__ float sm_max[SG];
+    __shared__ float sm_tot[SG];
+    __shared__ f32x4 sm_acc[SG][LPR];
+    const int64_t row = blockIdx.x;
+    if (row >= p.rows) return;  // uniform over the workgroup
+    const int c4 = threadIdx.x % LPR, sg = threadIdx.x / LPR;
+    float m = -__builtin_inff();
+#pragma unroll 4
+    for (int s = sg; s < p.ns; s += SG) m = fmaxf(m, p.lpart[(int64_t)s * p.rows + row]);
+    if (c4 == 0) sm_max[sg] = m;
+    __syncthreads();
+    float M = -__builtin_inff();
+#pragma unroll
+    for (int k = 0; k < SG; ++k) M = fmaxf(M, sm_max[k]);
+    float tot = 0.f;
+    f32x4 acc = f32x4{};
+    if (M != -__builtin_inff()) {
+#pragma unroll 4
+        for (int s = sg; s < p.ns; s += SG) {
+            const float w = __expf(p.lpart[(int64_t)s * p.rows + row] - M);  // 0 for empty splits
+            const f32x4 v = *(const f32x4*)(p.opart + ((int64_t)s * p.rows + row) * D + c4 * 4);
+            tot += w;
+            acc += w * v;
+        }
+    }
+    if (c4 == 0) sm_tot[sg] = tot;
+    sm_acc[sg][c4] = acc;
+    __syncthreads();
+    if (sg != 0) return;
+    float T = 0.f;
+    f32x4 A = f32x4{};
+#pragma unroll
+    for (int k = 0; k < SG; ++k) {
+        T += sm_tot[k];
+        A += sm_acc[k][c4];
+    }
+    const bool live = M != -__builtin_inff();
+    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+    bf16x4 ov;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ov[i] = (__bf16)(live ? A[i] / T : 0.f);
+    *(bf16x4*)(p.o + row * D + c4 * 4) = ov;
+    if (c4 == 0 && p.lse) {
+        const int64_t hq = row % p.Hq;
+        const int64_t bt = row / p.Hq;
+        const int64_t i = bt % p.Sq, bb = bt / p.Sq;
+        p.lse[(bb * p.Hq + hq) * p.Sq + i] = live ? M + __logf(T) : -__builtin_inff();
+    }
+}
+
 // ---------------------------------------------------------------- launchers
 template <int D, bool CAUSAL, bool SPLIT, bool VARLEN, bool QK8>
 static hipError_t launch_attn(const FwdParams& p, hipStream_t stream) {
@@ -1186,6 +1248,13 @@ hipError_t launch_decode(const FwdParams& p, int d, bool causal, bool split, boo
 }
 
 hipError_t launch_combine(const CombineParams& p, int d, long long grid, hipStream_t stream) {
+    if (p.ns >= kCombineWideSplits) {  // one workgroup per row (grid == rows)
+        if (d == 128)
+            hipLaunchKernelGGL((combine_wide_kernel<128>), dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
+        else
+            hipLaunchKernelGGL((combine_wide_kernel<64>), dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
+        return hipGetLastError();
+    }
     if (d == 128)
         hipLaunchKernelGGL((combine_kernel<128>), dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
     else

@@ -132,7 +132,7 @@ int make_plan(const Shape& s, int pack_gqa, int num_splits, int num_cus, Plan* p
     if (p->grid > INT_MAX) return GQA_ERR_INVALID_ARG;
     const long long rows = (long long)s.B * s.Sq * s.Hq;
     if (ns > 1) {
-        p->combine_grid = ceil_div(rows, combine_rows_per_block(s.d));
+        p->combine_grid = ns >= kCombineWideSplits ? rows : ceil_div(rows, combine_rows_per_block(s.d));
         p->workspace_bytes = (long long)ns * rows * ((long long)s.d * 4 + 4);
         if (p->combine_grid > INT_MAX) return GQA_ERR_INVALID_ARG;
     } else {

@@ -99,7 +99,10 @@ struct Plan {
 // Resolves the plan; returns 0 or a status (sizes too large for the grid).
 int make_plan(const Shape& s, int pack_gqa, int num_splits, int num_cus, Plan* p);
 
-// Rows of the combine kernel handled by one 256-thread workgroup.
+// Rows of the combine kernel handled by one 256-thread workgroup. From
+// kCombineWideSplits splits on, the merge takes one workgroup per row, whose
+// threads share out the splits.
 inline int combine_rows_per_block(int d) { return kThreads / (d / 4); }
+constexpr int kCombineWideSplits = 16;
 
 }  // namespace gqa

@@ -102,3 +102,42 @@ def test_one_tile_per_split():
         assert plan["num_splits"] == 16
         O, L = gpu_run(q, k, v, False, scale, 1, ns)
         compare_to_oracle(O, L, q, k, v, False, scale, tag=f"ns={ns}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_many_splits(d):
+    """Split counts on both sides of the switch to the one-workgroup-per-row merge
+    (16 splits): 15, 16, 64, one 32-key tile per split (129) and more splits than
+    tiles (200, clamped to 129); one and four new tokens, causal and not."""
+    import grouped_query_exact_amd as g
+    B, Hq, Hk, Sk = 2, 8, 2, 4096 + 7
+    scale = gi.fp32(1 / math.sqrt(d))
+    for Sq in (1, 4):
+        q, k, v = _qkv(9600 + d + Sq, B, Sq, Sk, Hq, Hk, d)
+        for causal in (False, True):
+            for ns in (15, 16, 64, 129, 200):
+                plan = _plan(q, k, causal, 1, ns)
+                assert plan["block_m"] == 32 and plan["num_splits"] == min(ns, 129), plan
+                O, L = gpu_run(q, k, v, causal, scale, 1, ns)
+                compare_to_oracle(O, L, q, k, v, causal, scale, tag=f"d={d} Sq={Sq} causal={causal} ns={ns}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_many_splits_tiled_empty_rows(d):
+    """The tiled kernel split 16 and 33 ways (one 64-key tile per split) with causal
+    rows for which the last splits hold no visible key, and -- with more query
+    tokens than keys -- rows that see no key in any split (O = 0, LSE = -inf)."""
+    B, Hq, Hk = 1, 4, 1
+    scale = gi.fp32(1 / math.sqrt(d))
+    for Sq, Sk in ((300, 2048 + 13), (2100, 2061)):
+        q, k, v = _qkv(9650 + d + Sq, B, Sq, Sk, Hq, Hk, d)
+        for ns in (16, 33):
+            plan = _plan(q, k, True, 0, ns)
+            assert plan["block_m"] != 32 and plan["num_splits"] == ns, plan
+            O, L = gpu_run(q, k, v, True, scale, 0, ns)
+            compare_to_oracle(O, L, q, k, v, True, scale, tag=f"d={d} Sq={Sq} Sk={Sk} ns={ns}")
+            if Sq > Sk:
+                dead = Sq - Sk
+                assert torch.all(O[:, :dead].float() == 0)
+                assert torch.all(torch.isneginf(L[:, :, :dead]))
+                assert torch.all(torch.isfinite(L[:, :, dead:]))

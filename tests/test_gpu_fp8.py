@@ -129,3 +129,17 @@ def test_kv8_rejects_prefill_shapes():
     with pytest.raises(g.GqaAttnError) as e:
         g.gqa_attn_fwd_kv8(q, k8, k8, 1.0, 1.0, out, None, True, 0.125)
     assert e.value.status == g.GQA_ERR_UNSUPPORTED
+
+
+def test_kv8_one_sequence_long():
+    """One sequence of 32 query heads over 8 fp8 KV heads against 16389 keys with the
+    automatic split count (128 on 256 compute units: the one-workgroup-per-row merge)
+    and with 128 splits asked for explicitly."""
+    B, Sq, Sk, Hq, Hk, d = 1, 1, 16384 + 5, 32, 8, 128
+    k8, v8 = gi.random_fp8(8700, (B, Sk, Hk, d)), gi.random_fp8(8701, (B, Sk, Hk, d))
+    q = gi.random_bf16(8702, (B, Sq, Hq, d))
+    scale = gi.fp32(1 / math.sqrt(d))
+    for ks, vs, ns in ((1.0, 1.0, 0), (0.37, 2.5, 0), (1.0, 1.0, 128)):
+        O, L = run_kv8(q, k8, v8, ks, vs, False, scale, -1, ns)
+        Or, Lr = oracle.attention_kv8_fp64(f64(q), k8.numpy(), v8.numpy(), ks, vs, False, scale)
+        check(O, L, Or, Lr, f"ks={ks} vs={vs} ns={ns}")
