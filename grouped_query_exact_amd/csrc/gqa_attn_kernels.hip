@@ -760,10 +760,13 @@ __global__ __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2
 // bandwidth pressure, rise-and-fall tuning article, "verification and
 // further directions") with per-tensor factors: the scores use
 // scale * k_scale, the output is multiplied by v_scale. The ring holds the
-// raw fp8 tiles (half the bytes per key); before a tile is used, the wave
-// converts it into a bf16 staging tile laid out exactly like a bf16 ring
-// tile, so the products are the same as for bf16 K/V holding the fp8 values
-// (every e4m3 value is exact in bf16).
+// raw fp8 tiles (half the bytes per key). Each matrix operand is read from
+// them and converted in registers: for K, 8 consecutive bytes of one key;
+// for V, 8 keys of one column through the transposing byte read. Every e4m3
+// value is exact in bf16 and the operands hold the same values in the same
+// order (the accumulator rows of V's columns aside, which only change where
+// the epilogue stores them), so the products are those of bf16 K/V holding
+// the fp8 values.
 template <int D, bool CAUSAL, bool SPLIT, bool PAGED, bool KV8, bool VARLEN, int STAGES>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void attn_decode_kernel(const FwdParams p) {
     constexpr int BN = kDecBlockN;                 // keys per tile
@@ -771,12 +774,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
     constexpr int TILE_B = BN * D * EB;            // ring bytes of one K or V tile
     constexpr int NCH = D * EB / 16;               // 16-byte chunks per stored row
     constexpr int NLOAD = BN * NCH / 64;           // 16-byte copies per lane per tensor and tile
-    constexpr int BF_TILE = BN * D * 2;            // bytes of a bf16 tile
     constexpr int RING_B = STAGES * 2 * TILE_B;
-    constexpr int SMEM_B = RING_B + (KV8 ? 2 * BF_TILE : 0);
     static_assert(BN == 32, "one 32-key MFMA block per tile");
-    __shared__ u32x4 smem[SMEM_B / 16];
-    LDS char* lds = (LDS char*)smem;               // ring stage s: K tile, then V tile; then (KV8) bf16 K, V
+    __shared__ u32x4 smem[RING_B / 16];
+    LDS char* lds = (LDS char*)smem;               // ring stage s: K tile, then V tile
 
     const int lane = threadIdx.x;
     const int col = lane & 31, half = lane >> 5;
@@ -828,14 +829,18 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
     }
     const int n = t_end - t_begin;
 
-    // ---- tile copies: per-lane byte offsets inside a tile. bf16 tiles are
-    // stored swizzled (chunk c of row r at c ^ swz(r)); fp8 tiles in order.
+    // ---- tile copies: per-lane byte offsets inside a tile. Tiles are stored
+    // swizzled: 16-byte chunk c of row r at c ^ swz(r) (bf16) or c ^ swz8(r)
+    // (fp8; the 256-byte bank window holds 256/D rows of D bytes, and rows of
+    // one window pair with distinct chunk masks, so 16 consecutive keys
+    // reading the same logical chunk hit 16 distinct 16-byte bank slots).
     const int64_t kv_stride_b = (int64_t)p.Hk * D * EB;
     // contiguous: this sequence's rows of head g; paged: head g of page 0
     const int64_t seq_off = PAGED ? (int64_t)g * D : (ktok0 * p.Hk + g) * D;
     const char* kbase = (const char*)p.k + seq_off * EB;
     const char* vbase = (const char*)p.v + seq_off * EB;
-    auto ring_chunk = [&](int ci, int row) { return KV8 ? (ci % NCH) : ((ci % NCH) ^ swz<D>(row)); };
+    auto swz8 = [](int row) { return (row / (256 / D)) % (D / 16); };
+    auto ring_chunk = [&](int ci, int row) { return KV8 ? ((ci % NCH) ^ swz8(row)) : ((ci % NCH) ^ swz<D>(row)); };
     uint32_t goff[NLOAD];
 #pragma unroll
     for (int u = 0; u < NLOAD; ++u) {
@@ -898,38 +903,14 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
         }
     };
 
-    // fp8 ring tile -> bf16 staging tile (swizzled like a bf16 ring tile):
-    // each lane converts 16-byte fp8 chunks (16 keys' worth of one row) into
-    // two 16-byte bf16 chunks. The wave's LDS operations run in order, so
-    // the reads that follow see these writes.
-    auto convert = [&](const LDS char* src, LDS char* dst) {
-        constexpr int C8 = D / 16;  // fp8 chunks per row
-#pragma unroll
-        for (int u = 0; u < BN * C8 / 64; ++u) {
-            const int ci = u * 64 + lane;
-            const int row = ci / C8, c8 = ci % C8;
-            const u32x4 w = *(const LDS u32x4*)(src + ci * 16);
-            u32x4 lo, hi;
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                lo[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, false));
-                lo[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, true));
-                hi[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[2 + i], 1.0f, false));
-                hi[2 * i + 1] =
-                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[2 + i], 1.0f, true));
-            }
-            LDS char* drow = dst + row * (D * 2);
-            *(LDS u32x4*)(drow + (((2 * c8) ^ swz<D>(row)) * 16)) = lo;
-            *(LDS u32x4*)(drow + (((2 * c8 + 1) ^ swz<D>(row)) * 16)) = hi;
-        }
-        asm volatile("" ::: "memory");
-    };
-
-    // ---- per-lane LDS operand offsets (as in the tiled kernel, one key block)
+    // ---- per-lane LDS operand offsets (as in the tiled kernel, one key block;
+    // fp8 K: the 8 bytes of values 16*dc + 8*half .. +7 of key krow0)
     const int krow0 = pi32(col);
     uint32_t kofs[D / 16];
 #pragma unroll
-    for (int dc = 0; dc < D / 16; ++dc) kofs[dc] = krow0 * (D * 2) + (((2 * dc + half) ^ swz<D>(krow0)) * 16);
+    for (int dc = 0; dc < D / 16; ++dc)
+        kofs[dc] = KV8 ? krow0 * D + ((dc ^ swz8(krow0)) * 16) + half * 8
+                       : krow0 * (D * 2) + (((2 * dc + half) ^ swz<D>(krow0)) * 16);
     const int u16 = lane & 15, qq = (lane >> 4) & 1;
     const int rho = ((u16 & 1) << 1) | ((u16 >> 1) & 1);
     uint32_t vofs[D / 32][2];
@@ -941,6 +922,22 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
             const int vcol = cb * 32 + qq * 16 + rho * 4;
             vofs[cb][rr] = vrow * (D * 2) + (((vcol >> 3) ^ swz<D>(vrow)) * 16) + (vcol & 7) * 2;
         }
+    // fp8 V: one transposing byte read per product. In each group of 16
+    // lanes, lane 2k+b names 8 bytes of key row k (of the group's 8 keys)
+    // starting at column 16*(group % 2) + 8*b of the 32-column block; lane j
+    // (j < 8) of the group receives byte j of the rows named by the even
+    // lanes, lane 8+j byte j of the rows named by the odd lanes, i.e. the 8
+    // keys of one column in key order: the A operand of the output product.
+    uint32_t v8ofs[D / 32];
+    {
+        const int grp16 = lane >> 4, w16 = lane & 15;
+        const int vkey = 8 * (grp16 >> 1) + (w16 >> 1);
+#pragma unroll
+        for (int cb = 0; cb < D / 32; ++cb) {
+            const int dofs = cb * 32 + 16 * (grp16 & 1) + 8 * (w16 & 1);
+            v8ofs[cb] = vkey * D + (((dofs >> 4) ^ swz8(vkey)) * 16) + (dofs & 15);
+        }
+    }
 
     f32x16 oacc[D / 32];
 #pragma unroll
@@ -953,18 +950,22 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
     auto compute = [&](int stage, int kv0) {
         const LDS char* kt = lds + stage * 2 * TILE_B;
         const LDS char* vt = kt + TILE_B;
-        if (KV8) {
-            LDS char* kbf = lds + RING_B;
-            LDS char* vbf = kbf + BF_TILE;
-            convert(kt, kbf);
-            convert(vt, vbf);
-            kt = kbf;
-            vt = vbf;
-        }
         f32x16 sacc = f32x16{};
 #pragma unroll
         for (int dc = 0; dc < D / 16; ++dc) {
-            const bf16x8 a = *(const LDS bf16x8*)(kt + kofs[dc]);
+            bf16x8 a;
+            if (KV8) {  // exact e4m3 -> bf16 of 8 values, two per conversion
+                const u32x2 w = *(const LDS u32x2*)(kt + kofs[dc]);
+                u32x4 cv;
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    cv[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, false));
+                    cv[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, true));
+                }
+                a = __builtin_bit_cast(bf16x8, cv);
+            } else {
+                a = *(const LDS bf16x8*)(kt + kofs[dc]);
+            }
             sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[dc], sacc, 0, 0, 0);
         }
         // slot i of this lane holds key kv0 + 16*(i/8) + 8*half + (i%8)
@@ -1007,11 +1008,22 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
         for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
             for (int cb = 0; cb < D / 32; ++cb) {
-                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS s16x4*)(vt + vofs[cb][0] + kk * 16 * D * 2));
-                const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS s16x4*)(vt + vofs[cb][1] + kk * 16 * D * 2));
-                const s16x8 av = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-                oacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), pk[kk],
-                                                                     oacc[cb], 0, 0, 0);
+                bf16x8 av;
+                if (KV8) {  // keys 16*kk + .. lie 16 rows further; the row swizzle repeats every 16 rows
+                    const i32x2 w = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS i32x2*)(vt + v8ofs[cb] + kk * 16 * D));
+                    u32x4 cv;
+#pragma unroll
+                    for (int i = 0; i < 2; ++i) {
+                        cv[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, false));
+                        cv[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, true));
+                    }
+                    av = __builtin_bit_cast(bf16x8, cv);
+                } else {
+                    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS s16x4*)(vt + vofs[cb][0] + kk * 16 * D * 2));
+                    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS s16x4*)(vt + vofs[cb][1] + kk * 16 * D * 2));
+                    av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                }
+                oacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pk[kk], oacc[cb], 0, 0, 0);
             }
         }
     };
@@ -1040,17 +1052,32 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
     const float lse_val = live ? (m_run + __log2f(l_tot)) * kLn2 : -__builtin_inff();
     const int64_t grow = (qtok0 + ti) * p.Hq + hh;
     if (!row_valid) return;
+    // output slots 4q .. 4q+3 of block cb hold columns 32*cb + col4(q) + 0..3:
+    // the bf16 transposing reads give A row m the column with bits 2 and 3
+    // of m exchanged, the fp8 transposing reads column m itself
+    auto col4 = [&](int q) { return KV8 ? 8 * q + 4 * half : 16 * (q >> 1) + 8 * half + 4 * (q & 1); };
     if (!SPLIT) {
         uint16_t* orow = p.o + grow * D;
 #pragma unroll
-        for (int cb = 0; cb < D / 32; ++cb)
+        for (int cb = 0; cb < D / 32; ++cb) {
+            if (KV8) {
 #pragma unroll
-            for (int run = 0; run < 2; ++run) {
-                bf16x8 ov;
+                for (int q = 0; q < 4; ++q) {
+                    bf16x4 ov;
 #pragma unroll
-                for (int i = 0; i < 8; ++i) ov[i] = (__bf16)(oacc[cb][run * 8 + i] * inv);
-                *(bf16x8*)(orow + cb * 32 + run * 16 + half * 8) = ov;
+                    for (int i = 0; i < 4; ++i) ov[i] = (__bf16)(oacc[cb][q * 4 + i] * inv);
+                    *(bf16x4*)(orow + cb * 32 + col4(q)) = ov;
+                }
+            } else {  // two adjacent runs per 16-byte store
+#pragma unroll
+                for (int run = 0; run < 2; ++run) {
+                    bf16x8 ov;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) ov[i] = (__bf16)(oacc[cb][run * 8 + i] * inv);
+                    *(bf16x8*)(orow + cb * 32 + col4(2 * run)) = ov;
+                }
             }
+        }
         if (half == 0 && p.lse) p.lse[lse_index(p, b, hh, qtok0, ti, VARLEN)] = lse_val;
     } else {
         const int64_t rows = VARLEN ? (int64_t)p.total_q * p.Hq : (int64_t)p.B * p.Sq * p.Hq;
@@ -1058,16 +1085,11 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
 #pragma unroll
         for (int cb = 0; cb < D / 32; ++cb)
 #pragma unroll
-            for (int run = 0; run < 2; ++run) {
-                f32x4 v0, v1;
+            for (int q = 0; q < 4; ++q) {
+                f32x4 v;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    v0[i] = oacc[cb][run * 8 + i] * inv;
-                    v1[i] = oacc[cb][run * 8 + 4 + i] * inv;
-                }
-                float* dst = orow + cb * 32 + run * 16 + half * 8;
-                *(f32x4*)dst = v0;
-                *(f32x4*)(dst + 4) = v1;
+                for (int i = 0; i < 4; ++i) v[i] = oacc[cb][q * 4 + i] * inv;
+                *(f32x4*)(orow + cb * 32 + col4(q)) = v;
             }
         if (half == 0) p.lpart[(int64_t)s * rows + grow] = lse_val;
     }
@@ -1104,7 +1126,6 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombineParams p) {
             acc += w * v;
         }
     }
-    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
     bf16x4 ov;
 #pragma unroll
     for (int i = 0; i < 4; ++i) ov[i] = (__bf16)acc[i];
@@ -1166,7 +1187,6 @@ __global__ __launch_bounds__(256) void combine_wide_kernel(const CombineParams p
         A += sm_acc[k][c4];
     }
     const bool live = M != -__builtin_inff();
-    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
     bf16x4 ov;
 #pragma unroll
     for (int i = 0; i < 4; ++i) ov[i] = (__bf16)(live ? A[i] / T : 0.f);

@@ -64,9 +64,13 @@ void choose(const Shape& s, int num_cus, int* pack_gqa, int* num_splits) {
     // on MI355X from one sequence against 128K keys to 64 sequences against
     // 8K, that count is the fastest, and more, shorter workgroups add tail and
     // merge costs (a single sequence needs up to 32 splits for it). With fp8
-    // K/V its tiles cost more arithmetic per byte and four per compute unit
-    // are best (up to 128 splits: one sequence against 128K keys takes 77 us
-    // at 128 splits, 307 us at 16).
+    // K/V a tile costs more arithmetic per byte (the conversion to bf16):
+    // two workgroups per compute unit are fastest when each unit has at
+    // least 256 key tiles to stream and there are at least 32 head units
+    // (64 x 8K, 8 x 32K, 4 x 64K keys: 9-13% faster than four), four
+    // otherwise (one sequence against 128K keys: 52 us at 128 splits, 57 at
+    // 64; against 256K keys 108 us at 128, 117 at 64; 32 x 4K keys), up to
+    // 128 splits.
     const int Gp = pack ? G : 1;
     const long long R = (long long)s.Sq * Gp;
     const bool decode = R <= kDecBlockM && s.q_bytes == 2;
@@ -74,7 +78,8 @@ void choose(const Shape& s, int num_cus, int* pack_gqa, int* num_splits) {
     const long long units = (long long)s.B * (pack ? s.Hk : s.Hq) * ceil_div(R, bm);
     const int T = R > 0 ? key_tiles_for(s, Gp, R, bn) : 0;
     const bool dec16 = decode && s.kv_bytes == 2;
-    const long long target = (decode ? (s.kv_bytes == 1 ? 4LL : 1LL) : 2LL) * num_cus;
+    const long long per_cu = !decode ? 2 : dec16 ? 1 : (units >= 32 && units * T >= 256LL * num_cus ? 2 : 4);
+    const long long target = per_cu * num_cus;
     const int cap = decode ? (dec16 ? 64 : 128) : 16;
     int ns = 1;
     if (units > 0 && units < target && T > 1) {

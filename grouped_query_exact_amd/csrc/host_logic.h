@@ -34,10 +34,9 @@ constexpr int kDecBlockM = 32;
 constexpr int kDecBlockN = 32;
 constexpr int kDecThreads = 64;
 constexpr int kDecStages = 4;
-// fp8 K/V: each tile is also converted to bf16 in LDS, which makes a
-// wavefront's tile slower than its copy; a shorter ring (40 KiB per
-// workgroup) lets four workgroups share a compute unit instead.
-constexpr int kDecStagesKV8 = 3;
+// fp8 K/V: half the bytes per stage (32 KiB per workgroup at d=128); 6 and
+// 8 stages measured no faster.
+constexpr int kDecStagesKV8 = 4;
 
 // Backward pass: the dK/dV kernel takes 128 keys per workgroup of
 // kBwdThreads (32 keys per wavefront, one wavefront for dK and one for dV)

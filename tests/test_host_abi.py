@@ -344,8 +344,9 @@ int main() {
         if (p.threads != (p.decode ? kDecThreads : (p.pingpong ? kPPThreads : kThreads))) { std::printf("bad threads\n"); return 1; }
         if (p.grid != (long long)B * p.units_per_b * p.row_tiles * p.ns) { std::printf("bad grid\n"); return 1; }
     }
-    // fp8 K/V decode splits up to four workgroups per compute unit, at most 128 splits,
-    // at least two 32-key tiles per split; bf16 decode up to one per compute unit
+    // fp8 K/V decode splits up to two workgroups per compute unit when each unit has at
+    // least 256 key tiles and there are at least 32 head units, else up to four; at most
+    // 128 splits, at least two 32-key tiles per split; bf16 decode up to one per compute unit
     {
         int pk = -1, ns = 0;
         Shape k8{1, 1, 131072, 32, 8, 128, 0, 1};
@@ -353,7 +354,13 @@ int main() {
         if (pk != 1 || ns != 128) { std::printf("bad fp8 decode split %d %d\n", pk, ns); return 1; }
         Shape k8b{8, 1, 65536, 32, 8, 128, 0, 1};
         choose(k8b, 256, &pk, &ns);
-        if (ns != 16) { std::printf("bad fp8 decode split B=8 %d\n", ns); return 1; }
+        if (ns != 8) { std::printf("bad fp8 decode split B=8 %d\n", ns); return 1; }
+        Shape k8d{64, 1, 8192, 32, 8, 128, 0, 1};  // 512 key tiles per compute unit: two workgroups each
+        choose(k8d, 256, &pk, &ns);
+        if (ns != 1) { std::printf("bad fp8 decode split B=64 %d\n", ns); return 1; }
+        Shape k8e{1, 1, 262144, 32, 8, 128, 0, 1};  // 256 tiles per unit but 8 head units: four each
+        choose(k8e, 256, &pk, &ns);
+        if (ns != 128) { std::printf("bad fp8 decode split 1 x 256K %d\n", ns); return 1; }
         Shape k8c{1, 1, 2048, 32, 8, 128, 0, 1};
         choose(k8c, 256, &pk, &ns);
         if (ns != 32) { std::printf("bad fp8 decode split short %d\n", ns); return 1; }
