@@ -144,7 +144,7 @@ int run(const Call& c) {
     gqa::Plan plan;
     int st = gqa::make_plan(s, c.pack_gqa, c.num_splits, cus, &plan);
     if (st != GQA_OK) return st;
-    if ((c.paged || c.kv8) && !plan.decode) return GQA_ERR_UNSUPPORTED;
+    if (c.kv8 && !plan.decode) return GQA_ERR_UNSUPPORTED;  // fp8 K/V: decode kernel only
 
     gqa::FwdParams p{};
     p.q = (const uint16_t*)c.q;
@@ -210,9 +210,9 @@ int run(const Call& c) {
                      plan.combine_grid, plan.workspace_bytes);
 
     auto launch = [&](bool split) {
-        if (plan.pingpong) return gqa::launch_pingpong(p, d, s.causal != 0, c.stream);  // unsplit only
+        if (plan.pingpong) return gqa::launch_pingpong(p, d, s.causal != 0, c.paged, c.stream);  // unsplit only
         return plan.decode ? gqa::launch_decode(p, d, s.causal != 0, split, c.paged, c.kv8, c.varlen, c.stream)
-                           : gqa::launch_attention(p, d, s.causal != 0, split, c.varlen, c.qk8, c.stream);
+                           : gqa::launch_attention(p, d, s.causal != 0, split, c.varlen, c.qk8, c.paged, c.stream);
     };
     if (plan.ns == 1) {
         hipError_t e = launch(false);
@@ -373,12 +373,13 @@ static int fwd_paged(const void* q, const void* k_cache, const void* v_cache, co
         if (page_size <= 0 || max_pages <= 0 || num_pages <= 0) return GQA_ERR_INVALID_ARG;
         if ((long long)max_pages * page_size > INT_MAX / 2) return GQA_ERR_INVALID_ARG;
         if (kv8 && (!std::isfinite(k_scale) || !std::isfinite(v_scale))) return GQA_ERR_INVALID_ARG;
-        const gqa::Shape s{B, Sq, max_pages * page_size, Hq, Hk, d, causal ? 1 : 0, kv8 ? 1 : 2};
+        gqa::Shape s{B, Sq, max_pages * page_size, Hq, Hk, d, causal ? 1 : 0, kv8 ? 1 : 2};
+        s.paged = 1;
         int st = gqa::check_sizes(s, scale, pack_gqa, num_splits);
         if (st != GQA_OK) return st;
         if (page_size % 16 != 0) return GQA_ERR_UNSUPPORTED;
         if ((long long)page_size * Hk * d * (kv8 ? 1 : 2) > INT_MAX) return GQA_ERR_INVALID_ARG;  // 32-bit in-page offsets
-        {  // decode-shaped calls only (the pack decision does not depend on the CU count)
+        if (kv8) {  // fp8 pools: decode-shaped calls only (the pack decision does not depend on the CU count)
             gqa::Plan probe;
             st = gqa::make_plan(s, pack_gqa, num_splits, 256, &probe);
             if (st != GQA_OK) return st;

@@ -85,7 +85,7 @@ __device__ __forceinline__ int64_t lse_index(const FwdParams& p, int b, int hh, 
 
 // QK8: Q and K hold fp8 e4m3 bytes; S^T = K Q^T runs on the fp8 matrix
 // cores (v_mfma_scale_f32_32x32x64_f8f6f4, unit block scales), V stays bf16.
-template <int D, bool CAUSAL, bool SPLIT, bool VARLEN, bool QK8>
+template <int D, bool CAUSAL, bool SPLIT, bool VARLEN, bool QK8, bool PAGED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_kernel(const FwdParams p) {
     constexpr int TILE = kBlockN * D;                 // elements of one K or V tile
     constexpr int TILE_B = TILE * 2;                  // bytes (bf16; an fp8 K tile uses the first half)
@@ -130,6 +130,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     int Sq = p.Sq, Sk = p.Sk;
     int64_t qtok0 = (int64_t)b * p.Sq, ktok0 = (int64_t)b * p.Sk;
     if (VARLEN) seq_extent(p, b, qtok0, Sq, ktok0, Sk);
+    if (PAGED) Sk = __builtin_amdgcn_readfirstlane(min(max(p.seqlens_k[b], 0), p.max_pages * p.page_size));
     const int R = VARLEN ? Sq * p.Gp : p.R;  // rows of this head unit
     if (VARLEN && r0 >= R) return;            // row tile past the end of this sequence
 
@@ -186,8 +187,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // ---- K/V tile loads: per-lane byte offsets inside a tile, scalar tile base
     const int64_t kv_stride_b = (int64_t)p.Hk * D * 2;
     const int64_t k_stride_b = QK8 ? (int64_t)p.Hk * D : kv_stride_b;
-    const char* kbase = QK8 ? (const char*)p.k + (ktok0 * p.Hk + g) * D : (const char*)(p.k + (ktok0 * p.Hk + g) * D);
-    const char* vbase = (const char*)(p.v + (ktok0 * p.Hk + g) * D);
+    // contiguous: this sequence's rows of head g; paged: head g of pool page 0
+    const char* kbase = QK8 ? (const char*)p.k + (ktok0 * p.Hk + g) * D
+                            : (const char*)(p.k + (PAGED ? (int64_t)g * D : (ktok0 * p.Hk + g) * D));
+    const char* vbase = (const char*)(p.v + (PAGED ? (int64_t)g * D : (ktok0 * p.Hk + g) * D));
     // chunk ci of a tile: row ci / (chunks per row), stored at its position
     // in the row, holding the global chunk that the row's swizzle puts there
     auto k_chunk = [&](int ci, int& row) {
@@ -211,6 +214,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     auto issue = [&](int kv0, int buf) {
         LDS char* kt = lds + buf * 2 * TILE_B;
         LDS char* vt = kt + TILE_B;
+        if (PAGED) {
+            // copy u covers key rows 64*(4u + wave)/NCH .. +64/NCH-1 of the tile
+            // (4 at d=128, 8 at d=64), inside one group of 16 keys and so inside
+            // one page: the page of its first row (or of the last key, past the
+            // end, where every row re-reads the last key). A scalar load (constant
+            // address space), so that it never waits for the copies in flight.
+            const __attribute__((address_space(4))) int* table =
+                (const __attribute__((address_space(4))) int*)p.block_table;
+#pragma unroll
+            for (int u = 0; u < NLOAD; ++u) {
+                const int key_first = min(kv0 + (u * 4 + wave) * 64 / NCH, Sk - 1);
+                const int pidx = (int)fdiv((uint32_t)key_first, p.pmul, p.pshift);
+                const int page = __builtin_amdgcn_readfirstlane(
+                    min(max(table[(int64_t)b * p.max_pages + pidx], 0), p.num_pages - 1));
+                const int64_t page_off = (int64_t)page * p.page_size * kv_stride_b;
+                const int ci = (u * 4 + wave) * 64 + lane;
+                const int row = ci / NCH;
+                const int logical_ch = (ci % NCH) ^ swz<D>(row);
+                const int key = min(kv0 + row, Sk - 1) - pidx * p.page_size;
+                const uint32_t off = (uint32_t)(key * kv_stride_b + logical_ch * 16);
+                lds_dma16(kbase + page_off, off, kt + (u * 4 + wave) * 1024);
+                lds_dma16(vbase + page_off, off, vt + (u * 4 + wave) * 1024);
+            }
+            return;
+        }
         const char* kg = kbase + kv0 * k_stride_b;
         const char* vg = vbase + kv0 * kv_stride_b;
         // copy u of K (fp8: the first NLOADK) and of V go to the same offset of
@@ -451,7 +479,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // its softmax phase of tile t, and a workgroup waits only for tile t's copies
 // at its top. Causal masking, the row/key bookkeeping, the lazy online
 // softmax in base 2 and the epilogue are those of attn_fwd_kernel.
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool PAGED>
 __global__ __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_pingpong_kernel(
     const FwdParams p) {
     constexpr int TILE = kBlockN * D;
@@ -480,8 +508,9 @@ __global__ __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2
     const int g = p.Gp > 1 ? unit : unit / p.G;
     const int h0 = p.Gp > 1 ? unit * p.G : unit;
     const int r0 = rt * kPPBlockM;
-    const int Sq = p.Sq, Sk = p.Sk;
-    const int64_t qtok0 = (int64_t)b * Sq, ktok0 = (int64_t)b * Sk;
+    const int Sq = p.Sq;
+    const int Sk = PAGED ? __builtin_amdgcn_readfirstlane(min(max(p.seqlens_k[b], 0), p.max_pages * p.page_size)) : p.Sk;
+    const int64_t qtok0 = (int64_t)b * Sq, ktok0 = (int64_t)b * p.Sk;
     const int R = p.R;
 
     // ---- this lane's row: token ti, head hh
@@ -505,8 +534,9 @@ __global__ __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2
 
     // ---- K/V tile copies: fixed per-thread 16-byte chunks, scalar tile base
     const int64_t kv_stride_b = (int64_t)p.Hk * D * 2;
-    const char* kbase = (const char*)(p.k + (ktok0 * p.Hk + g) * D);
-    const char* vbase = (const char*)(p.v + (ktok0 * p.Hk + g) * D);
+    // contiguous: this sequence's rows of head g; paged: head g of pool page 0
+    const char* kbase = (const char*)(p.k + (PAGED ? (int64_t)g * D : (ktok0 * p.Hk + g) * D));
+    const char* vbase = (const char*)(p.v + (PAGED ? (int64_t)g * D : (ktok0 * p.Hk + g) * D));
     uint32_t goff[NLOAD];
 #pragma unroll
     for (int u = 0; u < NLOAD; ++u) {
@@ -522,6 +552,26 @@ __global__ __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2
     };
     auto issue = [&](int t) __attribute__((always_inline)) {
         const int kv0 = t * kBlockN;
+        if (PAGED) {  // as in attn_fwd_kernel: each copy's 4 key rows lie in one page
+            const __attribute__((address_space(4))) int* table =
+                (const __attribute__((address_space(4))) int*)p.block_table;
+#pragma unroll
+            for (int u = 0; u < NLOAD; ++u) {
+                const int key_first = min(kv0 + (u * 8 + wave) * 64 / NCH, Sk - 1);
+                const int pidx = (int)fdiv((uint32_t)key_first, p.pmul, p.pshift);
+                const int page = __builtin_amdgcn_readfirstlane(
+                    min(max(table[(int64_t)b * p.max_pages + pidx], 0), p.num_pages - 1));
+                const int64_t page_off = (int64_t)page * p.page_size * kv_stride_b;
+                const int ci = (u * 8 + wave) * 64 + lane;
+                const int row = ci / NCH;
+                const int logical_ch = (ci % NCH) ^ swz<D>(row);
+                const int key = min(kv0 + row, Sk - 1) - pidx * p.page_size;
+                const uint32_t off = (uint32_t)(key * kv_stride_b + logical_ch * 16);
+                lds_dma16(kbase + page_off, off, stage_dst(t, 0, u));
+                lds_dma16(vbase + page_off, off, stage_dst(t, 1, u));
+            }
+            return;
+        }
         const char* kg = kbase + kv0 * kv_stride_b;
         const char* vg = vbase + kv0 * kv_stride_b;
         if (kv0 + kBlockN <= Sk) {
@@ -1200,36 +1250,47 @@ __global__ __launch_bounds__(256) void combine_wide_kernel(const CombineParams p
 }
 
 // ---------------------------------------------------------------- launchers
-template <int D, bool CAUSAL, bool SPLIT, bool VARLEN, bool QK8>
+template <int D, bool CAUSAL, bool SPLIT, bool VARLEN, bool QK8, bool PAGED>
 static hipError_t launch_attn(const FwdParams& p, hipStream_t stream) {
-    hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, SPLIT, VARLEN, QK8>), dim3(p.grid), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, SPLIT, VARLEN, QK8, PAGED>), dim3(p.grid), dim3(kThreads), 0, stream, p);
     return hipGetLastError();
 }
 
-template <int D, bool VARLEN, bool QK8>
+template <int D, bool VARLEN, bool QK8, bool PAGED>
 static hipError_t launch_attn_d(const FwdParams& p, bool causal, bool split, hipStream_t stream) {
     if (causal)
-        return split ? launch_attn<D, true, true, VARLEN, QK8>(p, stream) : launch_attn<D, true, false, VARLEN, QK8>(p, stream);
-    return split ? launch_attn<D, false, true, VARLEN, QK8>(p, stream) : launch_attn<D, false, false, VARLEN, QK8>(p, stream);
+        return split ? launch_attn<D, true, true, VARLEN, QK8, PAGED>(p, stream)
+                     : launch_attn<D, true, false, VARLEN, QK8, PAGED>(p, stream);
+    return split ? launch_attn<D, false, true, VARLEN, QK8, PAGED>(p, stream)
+                 : launch_attn<D, false, false, VARLEN, QK8, PAGED>(p, stream);
 }
 
-// Instantiated combinations: bf16, variable-length bf16, fp8 Q/K.
+// Instantiated combinations: bf16, variable-length bf16, fp8 Q/K, paged bf16.
 template <int D>
-static hipError_t launch_attn_dd(const FwdParams& p, bool causal, bool split, bool varlen, bool qk8, hipStream_t stream) {
-    if (qk8) return launch_attn_d<D, false, true>(p, causal, split, stream);
-    return varlen ? launch_attn_d<D, true, false>(p, causal, split, stream) : launch_attn_d<D, false, false>(p, causal, split, stream);
+static hipError_t launch_attn_dd(const FwdParams& p, bool causal, bool split, bool varlen, bool qk8, bool paged,
+                                 hipStream_t stream) {
+    if (qk8) return launch_attn_d<D, false, true, false>(p, causal, split, stream);
+    if (paged) return launch_attn_d<D, false, false, true>(p, causal, split, stream);
+    return varlen ? launch_attn_d<D, true, false, false>(p, causal, split, stream)
+                  : launch_attn_d<D, false, false, false>(p, causal, split, stream);
 }
 
-hipError_t launch_attention(const FwdParams& p, int d, bool causal, bool split, bool varlen, bool qk8, hipStream_t stream) {
-    return d == 128 ? launch_attn_dd<128>(p, causal, split, varlen, qk8, stream)
-                    : launch_attn_dd<64>(p, causal, split, varlen, qk8, stream);
+hipError_t launch_attention(const FwdParams& p, int d, bool causal, bool split, bool varlen, bool qk8, bool paged,
+                            hipStream_t stream) {
+    return d == 128 ? launch_attn_dd<128>(p, causal, split, varlen, qk8, paged, stream)
+                    : launch_attn_dd<64>(p, causal, split, varlen, qk8, paged, stream);
 }
 
 // d=128 only (the plan never picks this kernel at d=64)
-hipError_t launch_pingpong(const FwdParams& p, int d, bool causal, hipStream_t stream) {
+hipError_t launch_pingpong(const FwdParams& p, int d, bool causal, bool paged, hipStream_t stream) {
     if (d != 128) return hipErrorInvalidValue;
-    if (causal) hipLaunchKernelGGL((attn_fwd_pingpong_kernel<128, true>), dim3(p.grid), dim3(kPPThreads), 0, stream, p);
-    else hipLaunchKernelGGL((attn_fwd_pingpong_kernel<128, false>), dim3(p.grid), dim3(kPPThreads), 0, stream, p);
+    if (paged) {
+        if (causal) hipLaunchKernelGGL((attn_fwd_pingpong_kernel<128, true, true>), dim3(p.grid), dim3(kPPThreads), 0, stream, p);
+        else hipLaunchKernelGGL((attn_fwd_pingpong_kernel<128, false, true>), dim3(p.grid), dim3(kPPThreads), 0, stream, p);
+    } else {
+        if (causal) hipLaunchKernelGGL((attn_fwd_pingpong_kernel<128, true, false>), dim3(p.grid), dim3(kPPThreads), 0, stream, p);
+        else hipLaunchKernelGGL((attn_fwd_pingpong_kernel<128, false, false>), dim3(p.grid), dim3(kPPThreads), 0, stream, p);
+    }
     return hipGetLastError();
 }
 

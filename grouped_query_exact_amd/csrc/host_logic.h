@@ -68,6 +68,7 @@ struct Shape {
     int kv_bytes = 2;  // bytes per stored K/V element: 2 (bf16) or 1 (fp8)
     int q_bytes = 2;   // bytes per stored Q element: 2 (bf16) or 1 (fp8 Q and K: tiled kernel only)
     int varlen = 0;    // packed sequences of different lengths (4-wavefront tiled or decode kernel)
+    int paged = 0;     // K/V in a pool of pages
 };
 
 // Returns 0 or a gqa_status_t error for the sizes alone (no pointers).

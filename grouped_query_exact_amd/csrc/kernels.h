@@ -76,9 +76,10 @@ struct BwdParams {
 
 hipError_t launch_backward(const BwdParams& p, int d, bool causal, hipStream_t stream);
 
-hipError_t launch_attention(const FwdParams& p, int d, bool causal, bool split, bool varlen, bool qk8, hipStream_t stream);
+hipError_t launch_attention(const FwdParams& p, int d, bool causal, bool split, bool varlen, bool qk8, bool paged,
+                            hipStream_t stream);
 // unsplit bf16 prefill on the 8-wavefront kernel (p.row_tiles of kPPBlockM rows)
-hipError_t launch_pingpong(const FwdParams& p, int d, bool causal, hipStream_t stream);
+hipError_t launch_pingpong(const FwdParams& p, int d, bool causal, bool paged, hipStream_t stream);
 hipError_t launch_decode(const FwdParams& p, int d, bool causal, bool split, bool paged, bool kv8, bool varlen,
                          hipStream_t stream);
 hipError_t launch_combine(const CombineParams& p, int d, long long grid, hipStream_t stream);

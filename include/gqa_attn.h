@@ -65,9 +65,9 @@ typedef enum {
                                  paged: page_size, max_pages or num_pages <= 0;
                                  fp8: non-finite k_scale or v_scale */
     GQA_ERR_UNSUPPORTED = -2, /* d not in {64,128}, pointer not 16-byte aligned;
-                                 paged and fp8: more than 32 query rows per head
-                                 unit; paged: page_size % 16 != 0, table
-                                 pointers not 4-byte aligned */
+                                 fp8 K/V (contiguous or paged): more than 32
+                                 query rows per head unit; paged: page_size %
+                                 16 != 0, table pointers not 4-byte aligned */
     GQA_ERR_NOMEM = -3,       /* the split-KV workspace could not be allocated */
     GQA_ERR_HIP = -4          /* a HIP call or kernel launch failed */
 } gqa_status_t;
@@ -144,7 +144,8 @@ int gqa_attn_fwd_varlen(const void* q, const void* k, const void* v, void* out, 
                         int Hq, int Hk, int d, int causal, float scale, int pack_gqa, int num_splits,
                         hipStream_t stream);
 
-/* Forward pass over a paged KV cache, for decode-shaped calls.
+/* Forward pass over a paged KV cache: decode, and prefill of a chunk of new
+ * tokens against cached keys.
  *
  * The pages serve dynamic-length sequences (and caches of sequences longer
  * than 8192 tokens) with FlashAttention's paged KV cache (Stable-Diffusion
@@ -164,10 +165,12 @@ int gqa_attn_fwd_varlen(const void* q, const void* k, const void* v, void* out, 
  * j <= i + seqlens_k[b] - Sq). Table entries past a sequence's last page
  * and page rows past its last key are never read.
  *
- * Limits: page_size a positive multiple of 16; a head unit may hold at most
- * 32 query rows (G * Sq with PackGQA, Sq without: decode and a few
- * speculative tokens), else GQA_ERR_UNSUPPORTED. num_splits and pack_gqa
- * are resolved as for a contiguous call with Sk = max_pages * page_size.
+ * Head units of at most 32 query rows (G * Sq with PackGQA, Sq without:
+ * decode and a few speculative tokens) run on the decode kernel, larger ones
+ * on the 4-wavefront tiled kernel, whose tile copies look up each group of
+ * key rows' page in the table. Limits: page_size a positive multiple of 16.
+ * num_splits and pack_gqa are resolved as for a contiguous call with
+ * Sk = max_pages * page_size.
  * seqlens_k and block_table live on the device and are not validated on the
  * host: the kernel clamps a length to [0, max_pages * page_size] and a page
  * number to [0, num_pages - 1], so bad values give wrong results, never an

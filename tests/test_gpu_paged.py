@@ -1,13 +1,15 @@
-"""Decode over a paged KV cache (gqa_attn_fwd_paged) against the paged fp64 oracle (GPU).
+"""Decode and chunked prefill over a paged KV cache (gqa_attn_fwd_paged) against the paged
+fp64 oracle (GPU).
 
 The cache is a pool of pages handed out in a seeded random order; sequences
 have their own key lengths (empty ones included) and the unused page rows,
 unused pages and unused table entries hold NaN / -1, so any read outside the
 sequences shows up as a non-finite output. Cases: page sizes 16 to 256 around
 the 32-key tile, lengths around page and tile boundaries, causal and not, one
-and four new tokens, both head dimensions and several split counts; the
-paged path against the contiguous path (bitwise, same tile order); and the
-full-size decode workload on sampled sequences.
+and four new tokens (decode kernel) and chunks of 40 and 200 tokens (tiled
+kernel), both head dimensions and several split counts; the paged path
+against the contiguous path (bitwise, same tile order, decode and prefill);
+and the full-size decode workload on sampled sequences.
 """
 
 import math
@@ -77,6 +79,87 @@ def test_paged_unpacked_and_auto():
     for pack, ns in ((0, 1), (0, 2), (-1, 0)):
         O, L = run_paged(q, kv, True, 0.0883883461356163, pack, ns)
         compare_paged(O, L, q, kv, True, 0.0883883461356163, tag=f"pack={pack} ns={ns}")
+
+
+PREFILL_LENGTHS = [0, 1, 63, 64, 65, 200, 517, 1000]
+
+
+@pytest.mark.parametrize("page_size", [16, 48, 64, 256])
+@pytest.mark.parametrize("d", [64, 128])
+def test_paged_prefill_parity(page_size, d):
+    """Chunks of 40 and 200 new tokens (more than 32 rows per head unit: the tiled kernel)
+    against ragged and empty cached sequences; causal (with rows that see no key where the
+    chunk is longer than the cache) and not; packed with 1 split, unpacked with 3, and the
+    library's choice."""
+    import grouped_query_exact_amd as g
+    Hq, Hk = 8, 2
+    kv = gi.paged_kv(7500 + page_size + d, PREFILL_LENGTHS, page_size, Hk, d, spare_pages=3)
+    scale = gi.fp32(1 / math.sqrt(d))
+    for Sq in (40, 200):
+        q = gi.random_bf16(7600 + page_size + d + Sq, (len(PREFILL_LENGTHS), Sq, Hq, d))
+        for causal in (False, True):
+            for pack, ns in ((1, 1), (0, 3), (-1, 0)):
+                plan = g.gqa_attn_plan(len(PREFILL_LENGTHS), Sq, kv.block_table.shape[1] * page_size, Hq, Hk, d,
+                                       causal, pack, ns, 256)
+                assert plan["block_m"] != 32, plan
+                O, L = run_paged(q, kv, causal, scale, pack, ns)
+                compare_paged(O, L, q, kv, causal, scale,
+                              tag=f"prefill ps={page_size} d={d} Sq={Sq} causal={causal} pack={pack} ns={ns}")
+
+
+def test_paged_prefill_equals_contiguous_bitwise():
+    """A 300-token chunk against 1000 cached keys per sequence, pages in order: the tiled
+    kernel reads the same keys in the same tile order as the contiguous call."""
+    import grouped_query_exact_amd as g
+    B, Sq, Sk, Hq, Hk, d, ps = 3, 300, 1000, 32, 8, 128, 64
+    P = -(-Sk // ps)
+    q, k, v = gi.random_bf16(7700, (B, Sq, Hq, d)), gi.random_bf16(7701, (B, Sk, Hk, d)), gi.random_bf16(7702, (B, Sk, Hk, d))
+    kc = torch.zeros((B * P, ps, Hk, d), dtype=torch.bfloat16)
+    vc = torch.zeros_like(kc)
+    kc.view(B, P * ps, Hk, d)[:, :Sk] = k
+    vc.view(B, P * ps, Hk, d)[:, :Sk] = v
+    kv = gi.PagedKV(kc, vc, torch.arange(B * P, dtype=torch.int32).view(B, P), torch.full((B,), Sk, dtype=torch.int32))
+    for causal in (False, True):
+        for pack, ns in ((1, 1), (0, 1), (1, 3)):
+            Op, Lp = run_paged(q, kv, causal, 0.0883883461356163, pack, ns)
+            out = torch.empty((B, Sq, Hq, d), dtype=torch.bfloat16, device=DEV)
+            lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=DEV)
+            g.gqa_attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), out, lse, causal, 0.0883883461356163, pack, ns)
+            torch.cuda.synchronize()
+            assert torch.equal(Op, out) and torch.equal(Lp, lse), f"causal={causal} pack={pack} ns={ns}"
+
+
+def test_paged_prefill_8_wavefront():
+    """16 sequences, 512-token chunks, 32 query heads over 8 KV heads (1024 items of 256 packed
+    rows: the 8-wavefront kernel), ragged cached lengths (one shorter than the chunk, so causal
+    rows that see no key), pages of 64 in random pool order: oracle on sampled sequences. With
+    equal lengths and pages in order: bitwise equal to the contiguous call."""
+    import grouped_query_exact_amd as g
+    B, Sq, Hq, Hk, d, ps = 16, 512, 32, 8, 128, 64
+    rs = np.random.RandomState(7800)
+    lens = [int(x) for x in rs.randint(300, 2000, size=B)]
+    lens[0], lens[1] = 100, 2048
+    kv = gi.paged_kv(7800, lens, ps, Hk, d, spare_pages=3)
+    q = gi.random_bf16(7801, (B, Sq, Hq, d))
+    scale = gi.fp32(1 / math.sqrt(d))
+    for causal in (True, False):
+        plan = g.gqa_attn_plan(B, Sq, kv.block_table.shape[1] * ps, Hq, Hk, d, causal, -1, 1, 256)
+        assert plan["threads"] == 512, plan
+        O, L = run_paged(q, kv, causal, scale, -1, 1)
+        assert torch.isfinite(O.float()).all()
+        compare_paged(O, L, q, kv, causal, scale, batches=[0, 1, 9], tag=f"8-wavefront causal={causal}")
+    Sk = 1024
+    P = Sk // ps
+    k, v = gi.random_bf16(7802, (B, Sk, Hk, d)), gi.random_bf16(7803, (B, Sk, Hk, d))
+    kvc = gi.PagedKV(k.reshape(B * P, ps, Hk, d).contiguous(), v.reshape(B * P, ps, Hk, d).contiguous(),
+                     torch.arange(B * P, dtype=torch.int32).view(B, P), torch.full((B,), Sk, dtype=torch.int32))
+    for causal in (True, False):
+        Op, Lp = run_paged(q, kvc, causal, scale, -1, 1)
+        out = torch.empty((B, Sq, Hq, d), dtype=torch.bfloat16, device=DEV)
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=DEV)
+        g.gqa_attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), out, lse, causal, scale, -1, 1)
+        torch.cuda.synchronize()
+        assert torch.equal(Op, out) and torch.equal(Lp, lse), f"causal={causal}"
 
 
 def test_paged_equals_contiguous_bitwise():

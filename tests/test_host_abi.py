@@ -109,6 +109,15 @@ def _paged(q=1, kc=1, vc=1, bt=1, sl=1, out=1, lse=None, B=2, Sq=1, Hq=8, Hk=2, 
                                 num_pages, page_size, max_pages, causal, scale, pack, ns, None)
 
 
+def _paged8(q=1, kc=1, vc=1, bt=1, sl=1, out=1, lse=None, B=2, Sq=1, Hq=8, Hk=2, d=128, num_pages=10,
+            page_size=32, max_pages=4, causal=0, scale=0.125, pack=-1, ns=0):
+    """gqa_attn_fwd_paged_kv8 with fake pointers and unit factors; only invalid calls are allowed."""
+    L = lib()
+    P = lambda x: None if x is None else ctypes.c_void_p(x * 4096)
+    return L.gqa_attn_fwd_paged_kv8(P(q), P(kc), P(vc), 1.0, 1.0, P(bt), P(sl), P(out), P(lse), B, Sq, Hq, Hk, d,
+                                    num_pages, page_size, max_pages, causal, scale, pack, ns, None)
+
+
 @pytest.mark.parametrize("kw,status", [
     (dict(page_size=0), "INVALID_ARG"),
     (dict(page_size=-16), "INVALID_ARG"),
@@ -123,8 +132,6 @@ def _paged(q=1, kc=1, vc=1, bt=1, sl=1, out=1, lse=None, B=2, Sq=1, Hq=8, Hk=2, 
     (dict(page_size=24), "UNSUPPORTED"),            # not a multiple of 16
     (dict(page_size=8), "UNSUPPORTED"),
     (dict(d=96), "UNSUPPORTED"),
-    (dict(Sq=9, Hq=8, Hk=2), "UNSUPPORTED"),        # 36 packed rows: not decode-shaped
-    (dict(Sq=33, Hq=2, Hk=2), "UNSUPPORTED"),       # 33 rows of one head
     (dict(Sq=9, pack=0), "OK_OR_DEVICE"),           # 9 unpacked rows per head: accepted up to the launch
 ])
 def test_paged_argument_checks(kw, status):
@@ -134,6 +141,17 @@ def test_paged_argument_checks(kw, status):
         assert st in (g.GQA_OK, g.GQA_ERR_HIP)  # no GPU here: the first HIP call fails
     else:
         assert st == getattr(g, "GQA_ERR_" + status), (kw, st)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(page_size=24), "UNSUPPORTED"),            # not a multiple of 16
+    (dict(Sq=9, Hq=8, Hk=2), "UNSUPPORTED"),        # 36 packed rows: fp8 pools take decode shapes only
+    (dict(Sq=33, Hq=2, Hk=2), "UNSUPPORTED"),       # 33 rows of one head
+    (dict(max_pages=0), "INVALID_ARG"),
+])
+def test_paged_kv8_argument_checks(kw, status):
+    import grouped_query_exact_amd as g
+    assert _paged8(**kw) == getattr(g, "GQA_ERR_" + status), kw
 
 
 @pytest.mark.parametrize("kw,status", [
