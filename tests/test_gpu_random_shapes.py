@@ -1,5 +1,5 @@
 """Seeded random shapes against the fp64 oracle (GPU): the bf16 forward, the fp8 Q/K forward, the fp8 K/V
-decode path, the backward, variable-length batches and paged decode, each on shapes drawn from seeded
+decode path, the backward, variable-length batches and paged decode and prefill, each on shapes drawn from seeded
 generators (batch 1-3, lengths 0-900 around the tile sizes, G in 1..8, Hk in 1..4, d in {64, 128}, causal
 or not, packing, splits, page sizes and factors drawn too). Every case is small enough for the oracle to
 finish in well under a second; tolerances as elsewhere. A last group draws shapes with enough work items
@@ -168,6 +168,33 @@ def test_random_paged_decode(seed):
     scale = gi.fp32(1 / math.sqrt(d))
     g.gqa_attn_fwd_paged(q.to(DEV), kvd.k_cache, kvd.v_cache, kvd.block_table, kvd.seqlens_k, out, lse, causal, scale,
                          -1, ns)
+    torch.cuda.synchronize()
+    Or, Lr = oracle.attention_paged_fp64(f64(q), f64(kv.k_cache), f64(kv.v_cache), kv.block_table.numpy(),
+                                         kv.seqlens_k.numpy(), causal, scale)
+    check(out, lse, Or, Lr, tag)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_paged_prefill(seed):
+    """Chunks of 33-200 new tokens over a paged cache (the prefill kernels' page lookups)."""
+    import grouped_query_exact_amd as g
+    rs = np.random.RandomState(15500 + seed)
+    nseq = int(rs.randint(1, 5))
+    Hk, G, d = int(rs.randint(1, 4)), int(rs.choice([1, 2, 3, 4])), int(rs.choice([64, 128]))
+    Sq = int(rs.choice([33, 40, 77, 130, 200]))
+    ps = int(rs.choice([16, 32, 48, 64, 128]))
+    lens = [int(x) for x in rs.randint(0, 700, size=nseq)]
+    causal, pack, ns = bool(rs.randint(0, 2)), int(rs.choice([-1, 0, 1])), int(rs.choice([0, 1, 3]))
+    Hq = G * Hk
+    kv = gi.paged_kv(15500 + seed, lens, ps, Hk, d, spare_pages=int(rs.randint(0, 4)))
+    q = gi.random_bf16(15600 + seed, (nseq, Sq, Hq, d))
+    tag = f"seed={seed} lens={lens} ps={ps} Sq={Sq} Hq={Hq} Hk={Hk} d={d} causal={causal} pack={pack} ns={ns}"
+    kvd = kv.to(DEV)
+    out = torch.empty((nseq, Sq, Hq, d), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((nseq, Hq, Sq), dtype=torch.float32, device=DEV)
+    scale = gi.fp32(1 / math.sqrt(d))
+    g.gqa_attn_fwd_paged(q.to(DEV), kvd.k_cache, kvd.v_cache, kvd.block_table, kvd.seqlens_k, out, lse, causal, scale,
+                         pack, ns)
     torch.cuda.synchronize()
     Or, Lr = oracle.attention_paged_fp64(f64(q), f64(kv.k_cache), f64(kv.v_cache), kv.block_table.numpy(),
                                          kv.seqlens_k.numpy(), causal, scale)
