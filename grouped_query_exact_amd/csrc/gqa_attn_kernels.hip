@@ -229,11 +229,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 const int page = __builtin_amdgcn_readfirstlane(
                     min(max(table[(int64_t)b * p.max_pages + pidx], 0), p.num_pages - 1));
                 const int64_t page_off = (int64_t)page * p.page_size * kv_stride_b;
-                const int ci = (u * 4 + wave) * 64 + lane;
-                const int row = ci / NCH;
-                const int logical_ch = (ci % NCH) ^ swz<D>(row);
-                const int key = min(kv0 + row, Sk - 1) - pidx * p.page_size;
-                const uint32_t off = (uint32_t)(key * kv_stride_b + logical_ch * 16);
+                uint32_t off;
+                if (kv0 + kBlockN <= Sk) {  // full tile: the copy's rows start at or after the page's first key
+                    off = goff[u] - (uint32_t)((pidx * p.page_size - kv0) * kv_stride_b);
+                } else {
+                    const int ci = (u * 4 + wave) * 64 + lane;
+                    const int row = ci / NCH;
+                    const int logical_ch = (ci % NCH) ^ swz<D>(row);
+                    const int key = min(kv0 + row, Sk - 1) - pidx * p.page_size;
+                    off = (uint32_t)(key * kv_stride_b + logical_ch * 16);
+                }
                 lds_dma16(kbase + page_off, off, kt + (u * 4 + wave) * 1024);
                 lds_dma16(vbase + page_off, off, vt + (u * 4 + wave) * 1024);
             }
@@ -562,11 +567,16 @@ __global__ __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2
                 const int page = __builtin_amdgcn_readfirstlane(
                     min(max(table[(int64_t)b * p.max_pages + pidx], 0), p.num_pages - 1));
                 const int64_t page_off = (int64_t)page * p.page_size * kv_stride_b;
-                const int ci = (u * 8 + wave) * 64 + lane;
-                const int row = ci / NCH;
-                const int logical_ch = (ci % NCH) ^ swz<D>(row);
-                const int key = min(kv0 + row, Sk - 1) - pidx * p.page_size;
-                const uint32_t off = (uint32_t)(key * kv_stride_b + logical_ch * 16);
+                uint32_t off;
+                if (kv0 + kBlockN <= Sk) {  // full tile: the copy's rows start at or after the page's first key
+                    off = goff[u] - (uint32_t)((pidx * p.page_size - kv0) * kv_stride_b);
+                } else {
+                    const int ci = (u * 8 + wave) * 64 + lane;
+                    const int row = ci / NCH;
+                    const int logical_ch = (ci % NCH) ^ swz<D>(row);
+                    const int key = min(kv0 + row, Sk - 1) - pidx * p.page_size;
+                    off = (uint32_t)(key * kv_stride_b + logical_ch * 16);
+                }
                 lds_dma16(kbase + page_off, off, stage_dst(t, 0, u));
                 lds_dma16(vbase + page_off, off, stage_dst(t, 1, u));
             }
