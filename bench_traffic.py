@@ -22,6 +22,8 @@ into <out-dir>/profiles/ (to be copied into profiles/):
     bench.py reports;
   * attn_bwd_llama2_prefill_b4_s2048.md: trace and counters of the
     backward kernels at the Llama-2 prefill shape (``--run-bwd``);
+  * attn_fwd_kv8_decode_b64_sk8192.md: trace and counters of the fp8 K/V
+    decode at the decode workload's shape (``--run-kv8``);
   * attn_fwd_qk8_sweep_b128_s2048.md: trace and counters of the forward
     with fp8 Q and K at the headline shape (``--run-qk8``).
 
@@ -53,6 +55,7 @@ BWD_KERNEL_NAMES = ("bwd_dq_kernel", "bwd_dkdv_kernel")
 RUN_LAUNCHES = 4
 BWD_LAUNCHES = 20  # short kernels: enough calls for the average to be the steady state
 QK8_LAUNCHES = 15  # the first launches of a process run slow; these dominate the average
+KV8_LAUNCHES = 20
 
 # name -> (workload factory, pack_gqa, num_splits); -1 / 0 = the library's choice
 WORKLOADS = {
@@ -170,6 +173,61 @@ def qk8_profile(out, prof_out, fetch_scale, write_scale):
     with open(os.path.join(prof_out, f"attn_fwd_qk8_{w.name}.md"), "w") as f:
         f.write("\n".join(md))
     print("[traffic] fp8 Q/K profile written", flush=True)
+
+
+def run_kv8():
+    """KV8_LAUNCHES fp8 K/V decode calls at the decode workload's shape (K/V: the bf16 recipe rounded to e4m3)."""
+    import torch
+    import grouped_query_exact_amd as g
+    import gqa_inputs as gi
+    w = gi.DECODE
+    dev = torch.device("cuda:0")
+    q, k, v = gi.make_qkv_device(w, dev)
+    k8 = k.to(torch.float8_e4m3fn).view(torch.uint8)
+    v8 = v.to(torch.float8_e4m3fn).view(torch.uint8)
+    del k, v
+    out = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.Sq), dtype=torch.float32, device=dev)
+    for _ in range(KV8_LAUNCHES):
+        g.gqa_attn_fwd_kv8(q, k8, v8, 1.0, 1.0, out, lse, w.causal, w.scale)
+    torch.cuda.synchronize()
+    print(json.dumps({"workload": "fp8 K/V " + w.name, "launches": KV8_LAUNCHES}), flush=True)
+
+
+def kv8_profile(out, prof_out, fetch_scale, write_scale):
+    """Kernel trace and HBM counters of the fp8 K/V decode at the decode workload's shape."""
+    import gqa_inputs as gi
+    w = gi.DECODE
+    cmd_t = rocprof(["--kernel-trace", "--stats"], out, "kv8_trace", ["--run-kv8"])
+    cmd_f = rocprof(["--pmc", "FETCH_SIZE"], out, "kv8_fetch", ["--run-kv8"])
+    cmd_w = rocprof(["--pmc", "WRITE_SIZE"], out, "kv8_write", ["--run-kv8"])
+    stats = [r for r in read_trace(out, "kv8_trace") if any(n in r["Name"] for n in KERNEL_NAMES)]
+    fetch = attention_only(read_counter(out, "kv8_fetch", "FETCH_SIZE"))
+    write = attention_only(read_counter(out, "kv8_write", "WRITE_SIZE"))
+    qe = w.B * w.Sq * w.Hq * w.d
+    ke = w.B * w.Sk * w.Hk * w.d
+    alg = 2 * qe + 2 * ke + 2 * qe + 4 * w.B * w.Hq * w.Sq  # Q bf16; K, V fp8; O bf16; LSE fp32
+    md = [f"# {w.name} with fp8 K/V: B={w.B}, Sq={w.Sq}, Sk={w.Sk}, Hq={w.Hq}, Hk={w.Hk}, d={w.d}, causal={w.causal}", "",
+          f"{KV8_LAUNCHES} gqa_attn_fwd_kv8 calls (unit factors; the bf16 input recipe rounded to e4m3, "
+          f"library's choice of packing and splits). Kernel source hash {kernel_hash()}.", "",
+          "Commands (REPO = repository root on the GPU box, run from /tmp with TMPDIR=/tmp):", "",
+          "    " + cmd_t.replace(ROOT, "$REPO"), "    " + cmd_f.replace(ROOT, "$REPO"),
+          "    " + cmd_w.replace(ROOT, "$REPO"), "", "Kernel trace (rocprofv3 --stats):", ""] + stats_table(stats)
+    for r in stats:
+        if "attn_decode_kernel" in r["Name"]:
+            md += ["", f"Rate at the average time: {alg / (float(r['AverageNs']) * 1e-9) / 1e9:.1f} GB/s of "
+                       f"algorithmic bytes ({alg / (float(r['AverageNs']) * 1e-9) / 1e9 / 8000:.3f} of 8 TB/s)."]
+    md += ["", f"HBM counters per dispatch (FETCH x{fetch_scale:.3f}, WRITE x{write_scale:.3f} from a 1 GiB copy):", "",
+           "| kernel | FETCH_SIZE (KiB) | WRITE_SIZE (KiB) | HBM bytes (scaled) |", "|---|---|---|---|"]
+    for kname in sorted(set(fetch) | set(write)):
+        f_kib = sum(fetch.get(kname, [0])) / max(1, len(fetch.get(kname, [1])))
+        w_kib = sum(write.get(kname, [0])) / max(1, len(write.get(kname, [1])))
+        md.append(f"| `{kname[:90]}` | {f_kib:.0f} | {w_kib:.0f} | "
+                  f"{(f_kib * 1024 * fetch_scale + w_kib * 1024 * write_scale) / 1e9:.4f} GB |")
+    md += ["", f"Algorithmic bytes (Q and O at two bytes, K and V at one, LSE at four, each once): {alg / 1e9:.4f} GB.", ""]
+    with open(os.path.join(prof_out, f"attn_fwd_kv8_{w.name}.md"), "w") as f:
+        f.write("\n".join(md))
+    print("[traffic] fp8 K/V decode profile written", flush=True)
 
 
 def run_copy():
@@ -297,6 +355,8 @@ def main():
     ap.add_argument("--copy-ref", action="store_true", help=argparse.SUPPRESS)
     ap.add_argument("--run-bwd", action="store_true", help=argparse.SUPPRESS)
     ap.add_argument("--run-qk8", action="store_true", help=argparse.SUPPRESS)
+    ap.add_argument("--run-kv8", action="store_true", help=argparse.SUPPRESS)
+    ap.add_argument("--skip-kv8", action="store_true")
     ap.add_argument("--skip-qk8", action="store_true")
     ap.add_argument("--skip-bench-trace", action="store_true")
     ap.add_argument("--skip-backward", action="store_true")
@@ -311,6 +371,8 @@ def main():
         return run_backward()
     if a.run_qk8:
         return run_qk8()
+    if a.run_kv8:
+        return run_kv8()
 
     out = os.path.abspath(a.out_dir)
     os.makedirs(out, exist_ok=True)
@@ -389,6 +451,8 @@ def main():
         backward_profile(out, prof_out, fetch_scale, write_scale)
     if not a.skip_qk8:
         qk8_profile(out, prof_out, fetch_scale, write_scale)
+    if not a.skip_kv8:
+        kv8_profile(out, prof_out, fetch_scale, write_scale)
     if not a.skip_bench_trace:
         bench_trace(out, prof_out)
     print(f"[traffic] wrote {prof_out}", flush=True)
