@@ -31,6 +31,39 @@ __device__ __forceinline__ uint32_t fdiv(uint32_t n, uint32_t mul, uint32_t shif
     return (__umulhi(n, mul) + n) >> shift;
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Adds the 8 bf16 probabilities of v, exactly as the P V product uses them,
+// to four fp32 partial sums (one v_dot2c_f32_bf16 per pair). Dividing the
+// output by this sum makes O a convex combination of the values with
+// exactly the weights the product applied: a row that sees one key returns
+// that key's value unchanged.
+__device__ __forceinline__ void add_bf16x8(const bf16x8 v, float (&s)[4]) {
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    s[0] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 0, 1), one, s[0], false);
+    s[1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 2, 3), one, s[1], false);
+    s[2] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 4, 5), one, s[2], false);
+    s[3] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 6, 7), one, s[3], false);
+}
+
+// Lazy running maximum of the online softmax, in scaled log2 units. The
+// maximum is raised only when a tile's row maximum mxs exceeds it by more
+// than 2^kRescaleThreshold, and then to the integer ceil(mxs). Returns the
+// factor alpha by which the row's accumulated sum and output are to be
+// multiplied: 1 (no change), 0 (first visible key), or an exact power of
+// two. Because every maximum is an integer, the probabilities exp2(s*c - m)
+// that two tilings of the same row compute (unsplit and split, 64- and
+// 32-key tiles) differ by exact powers of two, so their bf16 roundings
+// agree; only the last-bit rounding of the exponent argument can differ.
+__device__ __forceinline__ float raise_max(float& m_run, float mxs) {
+    if (!(mxs > m_run + kRescaleThreshold)) return 1.f;
+    const float m_new = __builtin_ceilf(mxs);
+    const float alpha = m_run == -__builtin_inff() ? 0.f
+                                                   : __builtin_amdgcn_ldexpf(1.f, (int)fmaxf(m_run - m_new, -256.f));
+    m_run = m_new;
+    return alpha;
+}
+
 // Position (within a block of 32) of the key stored in LDS row m, chosen so
 // that MFMA result slot i of lane half h holds key 16*(i/8) + 8*h + (i%8).
 __device__ __forceinline__ int pi32(int m) {

@@ -36,17 +36,40 @@ int device_cus(int dev) {
     return v;
 }
 
-// Keep freed workspace in the device's default pool so that steady-state
-// calls do not return memory to the driver and allocate it again.
-void keep_pool(int dev) {
-    if (dev < 0 || dev >= kMaxDevices) return;
+// Split and backward workspaces come from a stream-ordered memory pool the
+// library owns, one per device. It keeps up to kPoolKeepBytes reserved
+// between calls, so steady-state calls (decode splits need a few MB) take
+// nothing from the driver, and returns anything above that to the device at
+// the next synchronisation (a 35 GB split workspace is not held for good).
+// The device's default pool, which other code uses, is left as it is. If the
+// pool cannot be created, the default pool serves the allocations.
+constexpr uint64_t kPoolKeepBytes = 256ull << 20;
+hipMemPool_t g_pool[kMaxDevices];
+
+hipMemPool_t lib_pool(int dev) {
+    if (dev < 0 || dev >= kMaxDevices) return nullptr;
     std::call_once(g_pool_once[dev], [dev] {
-        hipMemPool_t pool;
-        if (hipDeviceGetDefaultMemPool(&pool, dev) == hipSuccess) {
-            uint64_t thr = UINT64_MAX;
-            (void)hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &thr);
+        hipMemPoolProps props = {};
+        props.allocType = hipMemAllocationTypePinned;
+        props.handleTypes = hipMemHandleTypeNone;
+        props.location.type = hipMemLocationTypeDevice;
+        props.location.id = dev;
+        hipMemPool_t pool = nullptr;
+        if (hipMemPoolCreate(&pool, &props) != hipSuccess || !pool) {
+            (void)hipGetLastError();
+            return;
         }
+        uint64_t thr = kPoolKeepBytes;
+        (void)hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &thr);
+        g_pool[dev] = pool;
     });
+    return g_pool[dev];
+}
+
+// Stream-ordered workspace allocation from the library's pool (see lib_pool).
+hipError_t ws_alloc(void** ptr, size_t bytes, int dev, hipStream_t stream) {
+    hipMemPool_t pool = lib_pool(dev);
+    return pool ? hipMallocFromPoolAsync(ptr, bytes, pool, stream) : hipMallocAsync(ptr, bytes, stream);
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -219,29 +242,42 @@ int run(const Call& c) {
         return e == hipSuccess ? GQA_OK : GQA_ERR_HIP;
     }
 
-    keep_pool(dev);
     void* ws = nullptr;
-    const size_t ws_bytes = c.varlen ? (size_t)plan.ns * (size_t)c.total_q * s.Hq * ((size_t)d * 4 + 4)
+    const size_t ws_bytes = c.varlen ? (size_t)plan.ns * (size_t)c.total_q * s.Hq * ((size_t)d * 4 + 8)
                                      : (size_t)plan.workspace_bytes;
-    if (hipMallocAsync(&ws, ws_bytes, c.stream) != hipSuccess || !ws) {
+    if (ws_alloc(&ws, ws_bytes, dev, c.stream) != hipSuccess || !ws) {
         (void)hipGetLastError();
         return GQA_ERR_NOMEM;
     }
     const int64_t rows = c.varlen ? (int64_t)c.total_q * s.Hq : (int64_t)s.B * s.Sq * s.Hq;
     p.opart = (float*)ws;
     p.lpart = (float*)ws + (int64_t)plan.ns * rows * d;
+    p.wpart = p.lpart + (int64_t)plan.ns * rows;
     hipError_t e = launch(true);
     if (e == hipSuccess) {
         gqa::CombineParams cp{};
         cp.opart = p.opart;
         cp.lpart = p.lpart;
+        cp.wpart = p.wpart;
         cp.o = (uint16_t*)c.out;
         cp.lse = c.lse;
         cp.rows = rows;
         cp.ns = plan.ns;
         cp.Sq = c.varlen ? c.total_q : s.Sq;  // varlen: lse [Hq, total_q] = one batch of total_q tokens
         cp.Hq = s.Hq;
-        e = gqa::launch_combine(cp, d, plan.combine_grid, c.stream);
+        if (c.varlen) {
+            cp.cu_q = c.cu_q;
+            cp.B = s.B;
+            cp.total_q = c.total_q;
+            cp.max_sq = s.Sq;
+        }
+        // variable-length calls: the workspace has total_q * Hq rows (the plan counts B * max_seqlen_q * Hq)
+        const long long cgrid = !c.varlen ? plan.combine_grid
+                                : plan.ns >= gqa::kCombineWideSplits ? (long long)rows
+                                                                     : ((long long)rows + gqa::combine_rows_per_block(d) - 1) /
+                                                                           gqa::combine_rows_per_block(d);
+        if (cgrid > INT_MAX) e = hipErrorInvalidValue;
+        else e = gqa::launch_combine(cp, d, cgrid, c.stream);
     }
     const hipError_t ef = hipFreeAsync(ws, c.stream);
     if (e != hipSuccess || ef != hipSuccess) return GQA_ERR_HIP;
@@ -320,11 +356,10 @@ int gqa_attn_bwd(const void* q, const void* k, const void* v, const void* out, c
         p.scale = scale;
         if (current_device() < 0) return GQA_ERR_HIP;
         const int dev = current_device();
-        keep_pool(dev);
         void* ws = nullptr;
         const size_t rows = (size_t)B * Hq * (size_t)(Sq > 0 ? Sq : 1);
         const size_t ws_bytes = 2 * rows * 4;  // D, then -LSE*log2(e)
-        if (hipMallocAsync(&ws, ws_bytes, stream) != hipSuccess || !ws) {
+        if (ws_alloc(&ws, ws_bytes, dev, stream) != hipSuccess || !ws) {
             (void)hipGetLastError();
             return GQA_ERR_NOMEM;
         }

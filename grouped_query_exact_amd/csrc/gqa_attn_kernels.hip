@@ -33,10 +33,12 @@
 //    registers of a lane hold runs of 8 consecutive keys and the output
 //    registers hold runs of 8 consecutive head-dimension columns.
 //  * Online softmax in base 2 with scale*log2(e) folded into one FMA, and a
-//    lazily updated row maximum: the running maximum is only raised (and the
-//    accumulator rescaled) when a row's new maximum exceeds it by more than
-//    2^8. Every row's final O = acc / l uses the same maximum for numerator
-//    and denominator, so the result is the same exact softmax.
+//    lazily updated integral row maximum: the running maximum is only raised
+//    (and the accumulator rescaled by an exact power of two) when a row's new
+//    maximum exceeds it by more than 2^8, and then to an integer. Every row's
+//    final O = acc / l uses the same maximum for numerator and denominator,
+//    so the result is the same exact softmax, and tilings that meet other
+//    maxima round the same probabilities to bf16 (see raise_max).
 //  * Causal tiles above the diagonal are never loaded; waves whose rows see
 //    none of a tile's keys skip its arithmetic; only boundary tiles evaluate
 //    the mask.
@@ -81,6 +83,34 @@ __device__ __forceinline__ void seq_extent(const FwdParams& p, int b, int64_t& q
 // for variable-length calls (token qtok0 + ti of the packed axis).
 __device__ __forceinline__ int64_t lse_index(const FwdParams& p, int b, int hh, int64_t qtok0, int ti, bool varlen) {
     return varlen ? (int64_t)hh * p.total_q + qtok0 + ti : ((int64_t)b * p.Hq + hh) * p.Sq + ti;
+}
+
+// Row `row` of the split workspace ([B*Sq or total_q, Hq]) -> its LSE element.
+__device__ __forceinline__ int64_t lse_row(const CombineParams& p, int64_t row) {
+    const int64_t hq = row % p.Hq;
+    const int64_t bt = row / p.Hq;
+    return ((bt / p.Sq) * p.Hq + hq) * p.Sq + bt % p.Sq;
+}
+
+// Whether the attention kernel wrote the partials of workspace row `row`.
+// Variable-length calls: token t = row / Hq belongs to the last sequence whose
+// first token is <= t and was written iff it is among that sequence's first
+// min(length, max_seqlen_q) tokens (offsets clamped as in seq_extent); tokens
+// past the last sequence belong to none. Other calls write every row.
+__device__ __forceinline__ bool row_written(const CombineParams& p, int64_t row) {
+    if (!p.cu_q) return true;
+    typedef const __attribute__((address_space(1))) int* gint_p;
+    const gint_p cu = (gint_p)p.cu_q;
+    const int t = (int)(row / p.Hq);
+    int lo = 0, hi = p.B - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (min(max(cu[mid], 0), p.total_q) <= t) lo = mid;
+        else hi = mid - 1;
+    }
+    const int q0 = min(max(cu[lo], 0), p.total_q);
+    const int q1 = min(max(cu[lo + 1], q0), p.total_q);
+    return t >= q0 && t - q0 < min(q1 - q0, p.max_sq);
 }
 
 // QK8: Q and K hold fp8 e4m3 bytes; S^T = K Q^T runs on the fp8 matrix
@@ -301,7 +331,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
     for (int cb = 0; cb < D / 32; ++cb) oacc[cb] = f32x16{};
     float m_run = -__builtin_inff();  // running max, scaled log2 units
-    float l_part[4] = {0.f, 0.f, 0.f, 0.f};  // this lane's partial row sums
+    float l_part[4] = {0.f, 0.f, 0.f, 0.f};  // this lane's partial row sums (fp32 P: the LSE)
+    float w_part[4] = {0.f, 0.f, 0.f, 0.f};  // ... of the bf16 P the output product uses (its normaliser)
     const float c = p.c;
     const int jlim = CAUSAL ? min(Sk - 1, ti + koff) : Sk - 1;  // last key visible to this row
 
@@ -362,14 +393,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
         // lazy running-max update (per row; both lanes of a row agree)
         const float mxs = (mx == -__builtin_inff()) ? -__builtin_inff() : mx * c;
-        float alpha = 1.f;
-        if (mxs > m_run + kRescaleThreshold) {
-            alpha = __builtin_amdgcn_exp2f(m_run - mxs);  // exp2(-inf) = 0 on the first update
-            m_run = mxs;
-        }
+        const float alpha = raise_max(m_run, mxs);
         if (__ballot(alpha != 1.f)) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) l_part[i] *= alpha;
+            for (int i = 0; i < 4; ++i) {
+                l_part[i] *= alpha;
+                w_part[i] *= alpha;
+            }
 #pragma unroll
             for (int cb = 0; cb < D / 32; ++cb)
 #pragma unroll
@@ -388,6 +418,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 l_part[i & 3] += x;
                 pk[mb * 2 + (i >> 3)][i & 7] = (__bf16)x;
             }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) add_bf16x8(pk[r], w_part);
 
         // O^T += V^T P^T
 #pragma unroll
@@ -421,9 +453,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
 
     // ---- epilogue
+    // O is normalised by the sum of the bf16 probabilities its product used;
+    // the LSE comes from the fp32 probabilities. A split writes both log-sums:
+    // the combine weights its outputs by the first and merges the LSE from the
+    // second, which reproduces the unsplit arithmetic.
     const float l_tot = xhalf_sum((l_part[0] + l_part[1]) + (l_part[2] + l_part[3]));
-    const bool live = l_tot > 0.f;
-    const float inv = live ? 1.f / l_tot : 0.f;
+    const float w_tot = xhalf_sum((w_part[0] + w_part[1]) + (w_part[2] + w_part[3]));
+    const bool live = l_tot > 0.f;  // the largest probability is >= 1/2, so w_tot > 0 too
+    const float inv = live ? 1.f / w_tot : 0.f;
     const float lse_val = live ? (m_run + __log2f(l_tot)) * kLn2 : -__builtin_inff();
     const int64_t grow = (qtok0 + ti) * p.Hq + hh;  // row of [B*Sq or total_q, Hq]
     if (!SPLIT) {
@@ -458,7 +495,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                     *(f32x4*)dst = v0;
                     *(f32x4*)(dst + 4) = v1;
                 }
-            if (half == 0) p.lpart[(int64_t)s * rows + grow] = lse_val;
+            if (half == 0) {
+                p.lpart[(int64_t)s * rows + grow] = lse_val;
+                p.wpart[(int64_t)s * rows + grow] = live ? (m_run + __log2f(w_tot)) * kLn2 : -__builtin_inff();
+            }
         }
     }
 }
@@ -642,7 +682,8 @@ __global__ __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2
 #pragma unroll
     for (int cb = 0; cb < D / 32; ++cb) oacc[cb] = f32x16{};
     float m_run = -__builtin_inff();  // running max, scaled log2 units
-    float l_part[4] = {0.f, 0.f, 0.f, 0.f};
+    float l_part[4] = {0.f, 0.f, 0.f, 0.f};  // fp32 P: the LSE
+    float w_part[4] = {0.f, 0.f, 0.f, 0.f};  // bf16 P: the output's normaliser
     const float c = p.c;
     const int jlim = CAUSAL ? min(Sk - 1, ti + koff) : Sk - 1;  // last key visible to this row
     f32x16 sacc[2];  // S(t): from the product phase to the softmax phase
@@ -717,14 +758,13 @@ __global__ __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2
         }
         // lazy running-max update; O holds every product up to tile t-1 here
         const float mxs = (mx == -__builtin_inff()) ? -__builtin_inff() : mx * c;
-        float alpha = 1.f;
-        if (mxs > m_run + kRescaleThreshold) {
-            alpha = __builtin_amdgcn_exp2f(m_run - mxs);  // exp2(-inf) = 0 on the first update
-            m_run = mxs;
-        }
+        const float alpha = raise_max(m_run, mxs);
         if (__ballot(alpha != 1.f)) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) l_part[i] *= alpha;
+            for (int i = 0; i < 4; ++i) {
+                l_part[i] *= alpha;
+                w_part[i] *= alpha;
+            }
 #pragma unroll
             for (int cb = 0; cb < D / 32; ++cb)
 #pragma unroll
@@ -739,6 +779,8 @@ __global__ __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2
                 l_part[i & 3] += x;
                 pk[mb * 2 + (i >> 3)][i & 7] = (__bf16)x;
             }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) add_bf16x8(pk[r], w_part);
     };
     auto product_phase = [&](int t) __attribute__((always_inline)) {
         __builtin_amdgcn_s_setprio(1);
@@ -778,8 +820,9 @@ __global__ __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2
 
     // ---- epilogue
     const float l_tot = xhalf_sum((l_part[0] + l_part[1]) + (l_part[2] + l_part[3]));
+    const float w_tot = xhalf_sum((w_part[0] + w_part[1]) + (w_part[2] + w_part[3]));
     const bool live = l_tot > 0.f;
-    const float inv = live ? 1.f / l_tot : 0.f;
+    const float inv = live ? 1.f / w_tot : 0.f;
     const float lse_val = live ? (m_run + __log2f(l_tot)) * kLn2 : -__builtin_inff();
     if (row_valid) {
         uint16_t* orow = p.o + ((qtok0 + ti) * p.Hq + hh) * D;
@@ -1003,7 +1046,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
 #pragma unroll
     for (int cb = 0; cb < D / 32; ++cb) oacc[cb] = f32x16{};
     float m_run = -__builtin_inff();
-    float l_part[4] = {0.f, 0.f, 0.f, 0.f};
+    float l_part[4] = {0.f, 0.f, 0.f, 0.f};  // fp32 P: the LSE
+    float w_part[4] = {0.f, 0.f, 0.f, 0.f};  // bf16 P: the output's normaliser
     const float c = p.c;
     const int jlim = CAUSAL ? min(Sk - 1, ti + koff) : Sk - 1;
 
@@ -1043,14 +1087,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
         t1 = fmaxf(fmaxf(t1, sacc[14]), sacc[15]);
         const float mx = xhalf_max(fmaxf(fmaxf(t0, t1), fmaxf(t2, t3)));
         const float mxs = (mx == -__builtin_inff()) ? -__builtin_inff() : mx * c;
-        float alpha = 1.f;
-        if (mxs > m_run + kRescaleThreshold) {
-            alpha = __builtin_amdgcn_exp2f(m_run - mxs);
-            m_run = mxs;
-        }
+        const float alpha = raise_max(m_run, mxs);
         if (__ballot(alpha != 1.f)) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) l_part[i] *= alpha;
+            for (int i = 0; i < 4; ++i) {
+                l_part[i] *= alpha;
+                w_part[i] *= alpha;
+            }
 #pragma unroll
             for (int cb = 0; cb < D / 32; ++cb)
 #pragma unroll
@@ -1064,6 +1107,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
             l_part[i & 3] += x;
             pk[i >> 3][i & 7] = (__bf16)x;
         }
+        add_bf16x8(pk[0], w_part);
+        add_bf16x8(pk[1], w_part);
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
@@ -1107,8 +1152,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
 
     // ---- epilogue
     const float l_tot = xhalf_sum((l_part[0] + l_part[1]) + (l_part[2] + l_part[3]));
+    const float w_tot = xhalf_sum((w_part[0] + w_part[1]) + (w_part[2] + w_part[3]));
     const bool live = l_tot > 0.f;
-    const float inv = live ? (KV8 ? p.vscale : 1.f) / l_tot : 0.f;
+    const float inv = live ? (KV8 ? p.vscale : 1.f) / w_tot : 0.f;
     const float lse_val = live ? (m_run + __log2f(l_tot)) * kLn2 : -__builtin_inff();
     const int64_t grow = (qtok0 + ti) * p.Hq + hh;
     if (!row_valid) return;
@@ -1151,112 +1197,127 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
                 for (int i = 0; i < 4; ++i) v[i] = oacc[cb][q * 4 + i] * inv;
                 *(f32x4*)(orow + cb * 32 + col4(q)) = v;
             }
-        if (half == 0) p.lpart[(int64_t)s * rows + grow] = lse_val;
+        if (half == 0) {
+            p.lpart[(int64_t)s * rows + grow] = lse_val;
+            p.wpart[(int64_t)s * rows + grow] = live ? (m_run + __log2f(w_tot)) * kLn2 : -__builtin_inff();
+        }
     }
 }
 
-// Merge of split partials: LSE = M + ln sum_s exp(LSE_s - M) with
-// M = max_s LSE_s, O = sum_s exp(LSE_s - LSE) O_s. A row whose splits are all
-// empty gets O = 0 and LSE = -inf. One row per D/4 lanes, 4 columns a lane.
-// The loops over the splits are unrolled so that eight loads are in flight
-// at once (with few rows and many splits, as in single-sequence decode, the
-// kernel is bound by load latency); the sums keep their split order.
+// Merge of split partials. Split s wrote its output O_s, normalised by the
+// sum of the bf16 probabilities it applied, the log-sum W_s of those
+// probabilities and the log-sum-exp LSE_s of its fp32 probabilities. Then
+//   O = sum_s exp(W_s - Mw) O_s / sum_s exp(W_s - Mw),   Mw = max_s W_s,
+//   LSE = M + ln sum_s exp(LSE_s - M),                   M = max_s LSE_s,
+// which is the unsplit normalisation of O and the unsplit LSE. A row whose
+// splits are all empty gets O = 0 and LSE = -inf; a row whose keys all lie in
+// one split gets that split's O and LSE unchanged. One row per D/4 lanes, 4
+// columns a lane. The loops over the splits are unrolled so that eight loads
+// are in flight at once (with few rows and many splits, as in single-sequence
+// decode, the kernel is bound by load latency); the sums keep their split
+// order.
 template <int D>
 __global__ __launch_bounds__(256) void combine_kernel(const CombineParams p) {
     constexpr int LPR = D / 4;
     constexpr int RPB = 256 / LPR;
     const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
     const int c4 = threadIdx.x % LPR;
-    if (row >= p.rows) return;
-    float M = -__builtin_inff();
+    if (row >= p.rows || !row_written(p, row)) return;
+    float M = -__builtin_inff(), Mw = -__builtin_inff();
 #pragma unroll 8
-    for (int s = 0; s < p.ns; ++s) M = fmaxf(M, p.lpart[(int64_t)s * p.rows + row]);
+    for (int s = 0; s < p.ns; ++s) {
+        M = fmaxf(M, p.lpart[(int64_t)s * p.rows + row]);
+        Mw = fmaxf(Mw, p.wpart[(int64_t)s * p.rows + row]);
+    }
     f32x4 acc = f32x4{};
     float lse = -__builtin_inff();
     if (M != -__builtin_inff()) {
-        float tot = 0.f;
-#pragma unroll 8
-        for (int s = 0; s < p.ns; ++s) tot += __expf(p.lpart[(int64_t)s * p.rows + row] - M);
-        lse = M + __logf(tot);
+        float tot = 0.f, totw = 0.f;
 #pragma unroll 8
         for (int s = 0; s < p.ns; ++s) {
-            const float ls = p.lpart[(int64_t)s * p.rows + row];
-            const float w = __expf(ls - lse);  // exp(-inf) = 0 for empty splits
+            tot += __expf(p.lpart[(int64_t)s * p.rows + row] - M);
+            const float w = __expf(p.wpart[(int64_t)s * p.rows + row] - Mw);  // 0 for empty splits
             const f32x4 v = *(const f32x4*)(p.opart + ((int64_t)s * p.rows + row) * D + c4 * 4);
+            totw += w;
             acc += w * v;
         }
+        lse = M + __logf(tot);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] = acc[i] / totw;
     }
     bf16x4 ov;
 #pragma unroll
     for (int i = 0; i < 4; ++i) ov[i] = (__bf16)acc[i];
     *(bf16x4*)(p.o + row * D + c4 * 4) = ov;
-    if (c4 == 0 && p.lse) {
-        const int64_t hq = row % p.Hq;
-        const int64_t bt = row / p.Hq;
-        const int64_t i = bt % p.Sq, bb = bt / p.Sq;
-        p.lse[(bb * p.Hq + hq) * p.Sq + i] = lse;
-    }
+    if (c4 == 0 && p.lse) p.lse[lse_row(p, row)] = lse;
 }
 
 // Many splits (single-sequence decode against a long context takes up to
 // 128): one workgroup of 256 threads per row. Thread t takes columns
 // 4*(t % (D/4)) .. +3 of the splits s = t / (D/4) + k*SG (SG split groups),
 // so a row's ns partials are read SG at a time instead of one after the
-// other; the groups' maxima, sums and weighted sums are merged through LDS:
-// LSE = M + ln T and O = A / T with M = max_s LSE_s, T = sum_s exp(LSE_s - M),
-// A = sum_s exp(LSE_s - M) O_s. A row whose keys all lie in one split gets
-// that split's O and LSE exactly, as from combine_kernel.
+// other; the groups' maxima, sums and weighted sums are merged through LDS.
+// Same merge as combine_kernel (the sums run in another order).
 template <int D>
 __global__ __launch_bounds__(256) void combine_wide_kernel(const CombineParams p) {
     constexpr int LPR = D / 4;    // lanes per split group (4 columns each)
     constexpr int SG = 256 / LPR; // split groups
-    __shared__ float sm_max[SG];
-    __shared__ float sm_tot[SG];
+    __shared__ float sm_max[SG], sm_maxw[SG];
+    __shared__ float sm_tot[SG], sm_totw[SG];
     __shared__ f32x4 sm_acc[SG][LPR];
     const int64_t row = blockIdx.x;
-    if (row >= p.rows) return;  // uniform over the workgroup
+    if (row >= p.rows || !row_written(p, row)) return;  // uniform over the workgroup
     const int c4 = threadIdx.x % LPR, sg = threadIdx.x / LPR;
-    float m = -__builtin_inff();
+    float m = -__builtin_inff(), mw = -__builtin_inff();
 #pragma unroll 4
-    for (int s = sg; s < p.ns; s += SG) m = fmaxf(m, p.lpart[(int64_t)s * p.rows + row]);
-    if (c4 == 0) sm_max[sg] = m;
+    for (int s = sg; s < p.ns; s += SG) {
+        m = fmaxf(m, p.lpart[(int64_t)s * p.rows + row]);
+        mw = fmaxf(mw, p.wpart[(int64_t)s * p.rows + row]);
+    }
+    if (c4 == 0) {
+        sm_max[sg] = m;
+        sm_maxw[sg] = mw;
+    }
     __syncthreads();
-    float M = -__builtin_inff();
+    float M = -__builtin_inff(), Mw = -__builtin_inff();
 #pragma unroll
-    for (int k = 0; k < SG; ++k) M = fmaxf(M, sm_max[k]);
-    float tot = 0.f;
+    for (int k = 0; k < SG; ++k) {
+        M = fmaxf(M, sm_max[k]);
+        Mw = fmaxf(Mw, sm_maxw[k]);
+    }
+    float tot = 0.f, totw = 0.f;
     f32x4 acc = f32x4{};
     if (M != -__builtin_inff()) {
 #pragma unroll 4
         for (int s = sg; s < p.ns; s += SG) {
-            const float w = __expf(p.lpart[(int64_t)s * p.rows + row] - M);  // 0 for empty splits
+            tot += __expf(p.lpart[(int64_t)s * p.rows + row] - M);
+            const float w = __expf(p.wpart[(int64_t)s * p.rows + row] - Mw);  // 0 for empty splits
             const f32x4 v = *(const f32x4*)(p.opart + ((int64_t)s * p.rows + row) * D + c4 * 4);
-            tot += w;
+            totw += w;
             acc += w * v;
         }
     }
-    if (c4 == 0) sm_tot[sg] = tot;
+    if (c4 == 0) {
+        sm_tot[sg] = tot;
+        sm_totw[sg] = totw;
+    }
     sm_acc[sg][c4] = acc;
     __syncthreads();
     if (sg != 0) return;
-    float T = 0.f;
+    float T = 0.f, Tw = 0.f;
     f32x4 A = f32x4{};
 #pragma unroll
     for (int k = 0; k < SG; ++k) {
         T += sm_tot[k];
+        Tw += sm_totw[k];
         A += sm_acc[k][c4];
     }
     const bool live = M != -__builtin_inff();
     bf16x4 ov;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) ov[i] = (__bf16)(live ? A[i] / T : 0.f);
+    for (int i = 0; i < 4; ++i) ov[i] = (__bf16)(live ? A[i] / Tw : 0.f);
     *(bf16x4*)(p.o + row * D + c4 * 4) = ov;
-    if (c4 == 0 && p.lse) {
-        const int64_t hq = row % p.Hq;
-        const int64_t bt = row / p.Hq;
-        const int64_t i = bt % p.Sq, bb = bt / p.Sq;
-        p.lse[(bb * p.Hq + hq) * p.Sq + i] = live ? M + __logf(T) : -__builtin_inff();
-    }
+    if (c4 == 0 && p.lse) p.lse[lse_row(p, row)] = live ? M + __logf(T) : -__builtin_inff();
 }
 
 // ---------------------------------------------------------------- launchers

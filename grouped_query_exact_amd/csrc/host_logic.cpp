@@ -116,6 +116,10 @@ int make_plan(const Shape& s, int pack_gqa, int num_splits, int num_cus, Plan* p
     // compute unit kPPMinItemsPerCU of them run on the 8-wavefront kernel
     // (or one per compute unit when the items are long: an estimated average
     // of at least kPPMinKeyTiles key tiles, from the first and last row tile)
+    // (variable-length calls stay on the 4-wavefront kernel: their grid holds
+    // an item for every row tile of the longest sequence in every sequence,
+    // and the empty ones cost the 8-wavefront kernel more: 16 sequences of
+    // 128..2048 tokens ran at 683 TFLOP/s on it against 730 on the 4-wavefront kernel)
     p->pingpong = 0;
     if (!p->decode && ns == 1 && s.d == 128 && s.q_bytes == 2 && s.kv_bytes == 2 && !s.varlen) {
         const long long items = (long long)s.B * p->units_per_b * ceil_div(p->R, kPPBlockM);
@@ -138,7 +142,7 @@ int make_plan(const Shape& s, int pack_gqa, int num_splits, int num_cus, Plan* p
     const long long rows = (long long)s.B * s.Sq * s.Hq;
     if (ns > 1) {
         p->combine_grid = ns >= kCombineWideSplits ? rows : ceil_div(rows, combine_rows_per_block(s.d));
-        p->workspace_bytes = (long long)ns * rows * ((long long)s.d * 4 + 4);
+        p->workspace_bytes = (long long)ns * rows * ((long long)s.d * 4 + 8);  // O_s, LSE_s, W_s (fp32)
         if (p->combine_grid > INT_MAX) return GQA_ERR_INVALID_ARG;
     } else {
         p->combine_grid = 0;

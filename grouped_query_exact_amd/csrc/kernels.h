@@ -14,8 +14,9 @@ struct FwdParams {
     const uint16_t* v;  // [B, Sk, Hk, D] bf16
     uint16_t* o;        // [B, Sq, Hq, D] bf16 (unsplit launches)
     float* lse;         // [B, Hq, Sq] fp32 or null (unsplit launches)
-    float* opart;       // [ns, B*Sq*Hq, D] fp32 (split launches)
-    float* lpart;       // [ns, B*Sq*Hq] fp32 (split launches)
+    float* opart;       // [ns, B*Sq*Hq, D] fp32 (split launches): O_s, normalised by its bf16 weights
+    float* lpart;       // [ns, B*Sq*Hq] fp32 (split launches): LSE_s of the fp32 probabilities
+    float* wpart;       // [ns, B*Sq*Hq] fp32 (split launches): log-sum of the bf16 probabilities
     int B, Sq, Sk, Hq, Hk;
     int G;              // Hq / Hk
     int Gp;             // rows per token in a tile: G when packed, 1 otherwise
@@ -45,10 +46,15 @@ struct FwdParams {
 struct CombineParams {
     const float* opart;
     const float* lpart;
+    const float* wpart;
     uint16_t* o;
     float* lse;
-    int64_t rows;       // B * Sq * Hq
-    int ns, Sq, Hq;
+    int64_t rows;       // B * Sq * Hq (variable-length calls: total_q * Hq)
+    int ns, Sq, Hq;     // variable-length calls: Sq = total_q (LSE [Hq, total_q])
+    // variable-length calls: the rows the attention kernel wrote are the first
+    // min(length, max_sq) tokens of each sequence; the combine skips the others
+    const int* cu_q;    // [B+1] cumulative query lengths, or null (every row written)
+    int B, total_q, max_sq;
 };
 
 // Backward pass (always PackGQA rows: the G query heads of a KV group).

@@ -33,10 +33,13 @@
  * be 16-byte aligned. d must be 64 or 128.
  *
  * Ownership: the caller owns every tensor. The library allocates only the
- * split-KV workspace (fp32 partial outputs and log-sum-exps), stream-ordered
- * with hipMallocAsync/hipFreeAsync on the caller's stream, so calls on
- * different streams never share it. The library keeps no other state than a
- * per-device cache of the compute-unit count.
+ * split-KV workspace (fp32 partial outputs and log-sums), stream-ordered on
+ * the caller's stream (hipMallocFromPoolAsync/hipFreeAsync) from a memory
+ * pool the library creates per device, so calls on different streams never
+ * share it. That pool keeps up to 256 MiB of freed workspace reserved for
+ * later calls and returns anything above that to the device at the next
+ * synchronisation; the device's default pool is not modified. Other state:
+ * a per-device cache of the compute-unit count.
  *
  * Calls are asynchronous with respect to the host and never synchronize the
  * stream. They are thread-safe. No C++ exception crosses this boundary. A

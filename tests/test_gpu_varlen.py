@@ -117,3 +117,34 @@ def test_varlen_llama_mix_sampled():
     O, L = run_varlen(q, k, v, cq, ck, True, scale)
     assert torch.isfinite(O.float()).all()
     check(O, L, q, k, v, cq, ck, True, scale, sequences=[1, 4, 6, 7], tag="llama mix")
+
+
+@pytest.mark.parametrize("lq,lk,max_sq", [([40, 100, 7], [1100, 1200, 50], 64),   # tiled kernel
+                                          ([1, 3, 2], [700, 1500, 90], 2)])        # decode kernel
+def test_varlen_split_leaves_unwritten_tokens_untouched(lq, lk, max_sq):
+    """Tokens past max_seqlen_q of a longer sequence and padding tokens after the last
+    sequence are written by no path: unsplit, split with the per-row combine, or split
+    with the one-workgroup-per-row combine (>= 16 splits). NaN guard values stay."""
+    import grouped_query_exact_amd as g
+    Hq, Hk, d, pad = 8, 2, 64, 13
+    q, k, v, cq, ck = gi.varlen_batch(9500 + max_sq, lq, lk, Hq, Hk, d)
+    total_q = int(cq[-1]) + pad
+    qp = torch.cat([q, gi.random_bf16(9599, (pad, Hq, d))]).to(DEV)
+    written = torch.zeros(total_q, dtype=torch.bool)
+    for b, n in enumerate(lq):
+        written[int(cq[b]):int(cq[b]) + min(n, max_sq)] = True
+    scale = gi.fp32(1 / math.sqrt(d))
+    for causal in (False, True):
+        for ns in (1, 3, 17):
+            out = torch.full((total_q, Hq, d), float("nan"), dtype=torch.bfloat16, device=DEV)
+            lse = torch.full((Hq, total_q), float("nan"), dtype=torch.float32, device=DEV)
+            g.gqa_attn_fwd_varlen(qp, k.to(DEV), v.to(DEV), out, lse, cq.to(DEV), ck.to(DEV), max_sq, max(lk), causal,
+                                  scale, 1, ns)
+            torch.cuda.synchronize()
+            tag = f"lq={lq} causal={causal} ns={ns}"
+            assert torch.isnan(out[~written.to(DEV)].float()).all(), f"{tag}: unwritten tokens were written"
+            assert torch.isnan(lse[:, ~written.to(DEV)]).all(), f"{tag}: unwritten LSE entries were written"
+            assert torch.isfinite(out[written.to(DEV)].float()).all(), f"{tag}: written tokens not finite"
+            ok = [b for b, n in enumerate(lq) if n <= max_sq]  # sequences within max_seqlen_q: exact results
+            check(out, lse, q, k, v, cq, ck, causal, scale, sequences=ok, tag=tag)
+

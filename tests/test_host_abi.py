@@ -295,7 +295,7 @@ def test_plan_grid_and_workspace():
     p = g.gqa_attn_plan(16, 2048, 2048, 32, 8, 128, True, 0, 4, 256)
     assert p["pack_gqa"] == 0 and p["num_splits"] == 4
     assert p["grid"] == 16 * 32 * p["row_tiles"] * 4
-    assert p["workspace_bytes"] == 4 * 16 * 2048 * 32 * (128 * 4 + 4)
+    assert p["workspace_bytes"] == 4 * 16 * 2048 * 32 * (128 * 4 + 8)  # O_s, LSE_s, W_s
     # the split count is clamped to the number of key tiles (decode tiles: 32 keys)
     p = g.gqa_attn_plan(1, 1, 100, 4, 4, 64, False, 0, 16, 256)
     assert p["num_splits"] == 4 and p["key_tiles"] == 4
