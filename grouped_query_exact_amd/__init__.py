@@ -14,17 +14,20 @@ import math
 import os
 from typing import Optional, Tuple
 
-__all__ = ["GqaAttnError", "gqa_attn_fwd", "gqa_attn_func", "gqa_attn_fwd_paged", "gqa_attn_func_paged",
+__all__ = ["GqaAttnError", "gqa_attn_fwd", "gqa_attn_fwd_noalloc", "gqa_attn_func", "gqa_attn_fwd_paged", "gqa_attn_func_paged",
            "gqa_attn_fwd_kv8", "gqa_attn_fwd_paged_kv8", "gqa_attn_fwd_qk8", "gqa_attn_fwd_varlen", "gqa_attn_bwd",
            "gqa_attn_choose", "gqa_attn_plan",
            "gqa_attn_strerror", "library_path", "load_library",
-           "GQA_OK", "GQA_ERR_INVALID_ARG", "GQA_ERR_UNSUPPORTED", "GQA_ERR_NOMEM", "GQA_ERR_HIP"]
+           "GQA_OK", "GQA_ERR_INVALID_ARG", "GQA_ERR_UNSUPPORTED", "GQA_ERR_NOMEM", "GQA_ERR_HIP",
+           "GQA_ERR_SCRATCH", "GQA_NOALLOC_SCRATCH_BYTES"]
 
 GQA_OK = 0
 GQA_ERR_INVALID_ARG = -1
 GQA_ERR_UNSUPPORTED = -2
 GQA_ERR_NOMEM = -3
 GQA_ERR_HIP = -4
+GQA_ERR_SCRATCH = -5
+GQA_NOALLOC_SCRATCH_BYTES = 64 << 20  # fixed split-KV workspace of gqa_attn_fwd_noalloc, per GPU
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -59,6 +62,8 @@ def load_library():
     c_int, c_float, vp = ctypes.c_int, ctypes.c_float, ctypes.c_void_p
     lib.gqa_attn_fwd.argtypes = [vp, vp, vp, vp, vp] + [c_int] * 7 + [c_float, c_int, c_int, vp]
     lib.gqa_attn_fwd.restype = c_int
+    lib.gqa_attn_fwd_noalloc.argtypes = [vp, vp, vp, vp, vp] + [c_int] * 7 + [c_float, c_int, c_int, vp]
+    lib.gqa_attn_fwd_noalloc.restype = c_int
     lib.gqa_attn_fwd_paged.argtypes = [vp] * 7 + [c_int] * 8 + [c_int, c_float, c_int, c_int, vp]
     lib.gqa_attn_fwd_paged.restype = c_int
     lib.gqa_attn_fwd_kv8.argtypes = [vp] * 3 + [c_float, c_float] + [vp, vp] + [c_int] * 7 + [c_float, c_int, c_int, vp]
@@ -119,6 +124,19 @@ def gqa_attn_fwd(q, k, v, out, lse, causal: bool, scale: float, pack_gqa: int = 
     q/out: [B, Sq, Hq, d] bf16, k/v: [B, Sk, Hk, d] bf16, lse: [B, Hq, Sq] fp32,
     all contiguous on the same GPU. ``stream`` defaults to torch's current stream.
     """
+    _fwd_call("gqa_attn_fwd", q, k, v, out, lse, causal, scale, pack_gqa, num_splits, stream)
+
+
+def gqa_attn_fwd_noalloc(q, k, v, out, lse, causal: bool, scale: float, pack_gqa: int = -1,
+                         num_splits: int = 0, stream=None) -> None:
+    """gqa_attn_fwd that never allocates: split calls keep their partials in the
+    library's fixed per-GPU scratch array (GQA_NOALLOC_SCRATCH_BYTES); a call that
+    needs more raises GqaAttnError(GQA_ERR_SCRATCH). Split calls that overlap in
+    time on one GPU share that array and race."""
+    _fwd_call("gqa_attn_fwd_noalloc", q, k, v, out, lse, causal, scale, pack_gqa, num_splits, stream)
+
+
+def _fwd_call(entry, q, k, v, out, lse, causal, scale, pack_gqa, num_splits, stream):
     import torch
     for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
         if t.dtype != torch.bfloat16 or not t.is_contiguous() or t.dim() != 4 or not t.is_cuda:
@@ -135,9 +153,9 @@ def gqa_attn_fwd(q, k, v, out, lse, causal: bool, scale: float, pack_gqa: int = 
     elif hasattr(stream, "cuda_stream"):
         stream = stream.cuda_stream
     with torch.cuda.device(q.device):
-        st = load_library().gqa_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
-                                         B, Sq, Sk, Hq, Hk, d, int(bool(causal)), float(scale),
-                                         int(pack_gqa), int(num_splits), stream)
+        st = getattr(load_library(), entry)(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                                            B, Sq, Sk, Hq, Hk, d, int(bool(causal)), float(scale),
+                                            int(pack_gqa), int(num_splits), stream)
     if st != GQA_OK:
         raise GqaAttnError(st)
 

@@ -93,6 +93,7 @@ const char* gqa_attn_strerror(int status) {
         case GQA_ERR_UNSUPPORTED: return "unsupported head dimension or alignment";
         case GQA_ERR_NOMEM: return "split-KV workspace allocation failed";
         case GQA_ERR_HIP: return "HIP runtime or launch error";
+        case GQA_ERR_SCRATCH: return "split-KV workspace larger than the fixed no-allocation scratch buffer";
         default: return "unknown status";
     }
 }
@@ -156,6 +157,7 @@ struct Call {
     const int* cu_q = nullptr;
     const int* cu_k = nullptr;
     int total_q = 0, total_k = 0;
+    bool noalloc = false;   // split workspace from the fixed device scratch array, no allocation
 };
 
 int run(const Call& c) {
@@ -245,9 +247,16 @@ int run(const Call& c) {
     void* ws = nullptr;
     const size_t ws_bytes = c.varlen ? (size_t)plan.ns * (size_t)c.total_q * s.Hq * ((size_t)d * 4 + 8)
                                      : (size_t)plan.workspace_bytes;
-    if (ws_alloc(&ws, ws_bytes, dev, c.stream) != hipSuccess || !ws) {
-        (void)hipGetLastError();
-        return GQA_ERR_NOMEM;
+    if (c.noalloc) {
+        // every partial the combine reads is written by this call's attention
+        // kernel (empty splits write O_s = 0, LSE_s = -inf), so nothing is cleared
+        if (ws_bytes > (size_t)gqa::kScratchBytes) return GQA_ERR_SCRATCH;
+        if (gqa::scratch_address(dev, &ws) != hipSuccess || !ws) return GQA_ERR_HIP;
+    } else {
+        if (ws_alloc(&ws, ws_bytes, dev, c.stream) != hipSuccess || !ws) {
+            (void)hipGetLastError();
+            return GQA_ERR_NOMEM;
+        }
     }
     const int64_t rows = c.varlen ? (int64_t)c.total_q * s.Hq : (int64_t)s.B * s.Sq * s.Hq;
     p.opart = (float*)ws;
@@ -279,7 +288,7 @@ int run(const Call& c) {
         if (cgrid > INT_MAX) e = hipErrorInvalidValue;
         else e = gqa::launch_combine(cp, d, cgrid, c.stream);
     }
-    const hipError_t ef = hipFreeAsync(ws, c.stream);
+    const hipError_t ef = c.noalloc ? hipSuccess : hipFreeAsync(ws, c.stream);
     if (e != hipSuccess || ef != hipSuccess) return GQA_ERR_HIP;
     return GQA_OK;
 }
@@ -301,6 +310,27 @@ int gqa_attn_fwd(const void* q, const void* k, const void* v, void* out, float* 
         if (!q || !k || !v || !out) return GQA_ERR_INVALID_ARG;
         if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return GQA_ERR_UNSUPPORTED;
         Call c{q, k, v, out, lse, s, scale, pack_gqa, num_splits, false, nullptr, nullptr, 0, 0, 0, stream};
+        return run(c);
+    } catch (...) {
+        return GQA_ERR_HIP;
+    }
+}
+
+int gqa_attn_fwd_noalloc(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Sq,
+                         int Sk, int Hq, int Hk, int d, int causal, float scale, int pack_gqa, int num_splits,
+                         hipStream_t stream) {
+    try {
+        const gqa::Shape s{B, Sq, Sk, Hq, Hk, d, causal ? 1 : 0};
+        int st = gqa::check_sizes(s, scale, pack_gqa, num_splits);
+        if (st != GQA_OK) return st;
+        if ((long long)B * Sq == 0) return GQA_OK;
+        if (!q || !k || !v || !out) return GQA_ERR_INVALID_ARG;
+        if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return GQA_ERR_UNSUPPORTED;
+        // the first call on a device looks up that device's copy of the scratch array
+        void* scratch = nullptr;
+        if (gqa::scratch_address(current_device(), &scratch) != hipSuccess || !scratch) return GQA_ERR_HIP;
+        Call c{q, k, v, out, lse, s, scale, pack_gqa, num_splits, false, nullptr, nullptr, 0, 0, 0, stream};
+        c.noalloc = true;
         return run(c);
     } catch (...) {
         return GQA_ERR_HIP;

@@ -105,4 +105,9 @@ int make_plan(const Shape& s, int pack_gqa, int num_splits, int num_cus, Plan* p
 inline int combine_rows_per_block(int d) { return kThreads / (d / 4); }
 constexpr int kCombineWideSplits = 16;
 
+// Fixed split-KV workspace of gqa_attn_fwd_noalloc (a file-scope device array,
+// one copy per GPU): 64 MiB holds the partials of every decode-shaped call up
+// to B*Hq = 4096 query rows at 8 splits (d=128), or 32 splits of 1024 rows.
+constexpr long long kScratchBytes = 64LL << 20;
+
 }  // namespace gqa

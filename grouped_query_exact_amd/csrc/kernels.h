@@ -90,4 +90,8 @@ hipError_t launch_decode(const FwdParams& p, int d, bool causal, bool split, boo
                          hipStream_t stream);
 hipError_t launch_combine(const CombineParams& p, int d, long long grid, hipStream_t stream);
 
+// Device address of the fixed workspace on device `dev` (the current device),
+// looked up once per device (gqa_attn_scratch.hip).
+hipError_t scratch_address(int dev, void** ptr);
+
 }  // namespace gqa

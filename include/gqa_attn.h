@@ -39,7 +39,8 @@
  * share it. That pool keeps up to 256 MiB of freed workspace reserved for
  * later calls and returns anything above that to the device at the next
  * synchronisation; the device's default pool is not modified. Other state:
- * a per-device cache of the compute-unit count.
+ * a per-device cache of the compute-unit count (and, for
+ * gqa_attn_fwd_noalloc, its fixed scratch array).
  *
  * Calls are asynchronous with respect to the host and never synchronize the
  * stream. They are thread-safe. No C++ exception crosses this boundary. A
@@ -72,7 +73,9 @@ typedef enum {
                                  query rows per head unit; paged: page_size %
                                  16 != 0, table pointers not 4-byte aligned */
     GQA_ERR_NOMEM = -3,       /* the split-KV workspace could not be allocated */
-    GQA_ERR_HIP = -4          /* a HIP call or kernel launch failed */
+    GQA_ERR_HIP = -4,         /* a HIP call or kernel launch failed */
+    GQA_ERR_SCRATCH = -5      /* gqa_attn_fwd_noalloc: the split-KV workspace of
+                                 the call exceeds GQA_NOALLOC_SCRATCH_BYTES */
 } gqa_status_t;
 
 /* Forward pass.
@@ -92,6 +95,30 @@ int gqa_attn_fwd(const void* q, const void* k, const void* v, void* out, float* 
                  int B, int Sq, int Sk, int Hq, int Hk, int d,
                  int causal, float scale, int pack_gqa, int num_splits,
                  hipStream_t stream);
+
+/* Size of the fixed split-KV workspace of gqa_attn_fwd_noalloc, per GPU. */
+#define GQA_NOALLOC_SCRATCH_BYTES (64LL << 20)
+
+/* gqa_attn_fwd for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, semantics, checks and kernels as gqa_attn_fwd; the only
+ * difference is where a split call (num_splits resolving to > 1) keeps its
+ * fp32 partials: in a fixed device array of GQA_NOALLOC_SCRATCH_BYTES that
+ * the library holds on every GPU it runs on until the process ends, instead
+ * of a stream-ordered allocation. The call never allocates or frees memory
+ * (no hipMalloc, hipMallocAsync, hipFree or allocating library routine).
+ * The workspace a call needs is gqa_attn_plan's workspace_bytes
+ * (num_splits * B*Sq*Hq * (4*d + 8)); a call that needs more returns
+ * GQA_ERR_SCRATCH before anything is launched. The array's device address is
+ * looked up on a device's first call (GQA_ERR_HIP if that fails). Every
+ * call on one GPU shares that GPU's array: split calls that may overlap in
+ * time on one GPU (different streams, or threads) race and must be ordered
+ * by the caller. A call writes every partial it reads, so no state carries
+ * over from the previous call. */
+int gqa_attn_fwd_noalloc(const void* q, const void* k, const void* v, void* out, float* lse,
+                         int B, int Sq, int Sk, int Hq, int Hk, int d,
+                         int causal, float scale, int pack_gqa, int num_splits,
+                         hipStream_t stream);
 
 /* Backward pass: gradients of the forward pass for an upstream gradient dout.
  *

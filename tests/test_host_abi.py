@@ -33,7 +33,8 @@ def lib():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    assert names == ["gqa_attn_bwd", "gqa_attn_choose", "gqa_attn_fwd", "gqa_attn_fwd_kv8", "gqa_attn_fwd_paged",
+    assert names == ["gqa_attn_bwd", "gqa_attn_choose", "gqa_attn_fwd", "gqa_attn_fwd_kv8", "gqa_attn_fwd_noalloc",
+                     "gqa_attn_fwd_paged",
                      "gqa_attn_fwd_paged_kv8", "gqa_attn_fwd_qk8", "gqa_attn_fwd_varlen", "gqa_attn_plan",
                      "gqa_attn_strerror"]
 
@@ -50,7 +51,7 @@ def test_library_exports_every_declared_symbol():
 def test_strerror():
     import grouped_query_exact_amd as g
     assert g.gqa_attn_strerror(0) == "success"
-    for st in (g.GQA_ERR_INVALID_ARG, g.GQA_ERR_UNSUPPORTED, g.GQA_ERR_NOMEM, g.GQA_ERR_HIP):
+    for st in (g.GQA_ERR_INVALID_ARG, g.GQA_ERR_UNSUPPORTED, g.GQA_ERR_NOMEM, g.GQA_ERR_HIP, g.GQA_ERR_SCRATCH):
         assert g.gqa_attn_strerror(st) not in ("success", "unknown status")
     assert g.gqa_attn_strerror(12345) == "unknown status"
 
@@ -84,6 +85,27 @@ def _fwd(q=1, k=1, v=1, out=1, lse=None, B=1, Sq=4, Sk=4, Hq=2, Hk=1, d=64, caus
 def test_invalid_arguments_are_rejected(kw):
     import grouped_query_exact_amd as g
     assert _fwd(**kw) == g.GQA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw", [dict(Hq=6, Hk=4), dict(Sk=0), dict(pack=2), dict(ns=-1), dict(q=None),
+                                dict(scale=float("nan"))])
+def test_noalloc_invalid_arguments_are_rejected(kw):
+    """The no-allocation entry point runs gqa_attn_fwd's checks before anything else."""
+    import grouped_query_exact_amd as g
+    L = lib()
+    a = dict(q=1, k=1, v=1, out=1, B=1, Sq=4, Sk=4, Hq=2, Hk=1, d=64, causal=0, scale=0.125, pack=-1, ns=0)
+    a.update(kw)
+    P = lambda x: None if x is None else ctypes.c_void_p(x * 4096)
+    st = L.gqa_attn_fwd_noalloc(P(a["q"]), P(a["k"]), P(a["v"]), P(a["out"]), None, a["B"], a["Sq"], a["Sk"],
+                                a["Hq"], a["Hk"], a["d"], a["causal"], a["scale"], a["pack"], a["ns"], None)
+    assert st == g.GQA_ERR_INVALID_ARG
+
+
+def test_noalloc_scratch_size_matches_header():
+    import grouped_query_exact_amd as g
+    text = open(HEADER).read()
+    assert re.search(r"#define GQA_NOALLOC_SCRATCH_BYTES \(64LL << 20\)", text)
+    assert g.GQA_NOALLOC_SCRATCH_BYTES == 64 << 20
 
 
 @pytest.mark.parametrize("d", [0, 32, 96, 256])
