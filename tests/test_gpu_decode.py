@@ -141,3 +141,61 @@ def test_many_splits_tiled_empty_rows(d):
                 assert torch.all(O[:, :dead].float() == 0)
                 assert torch.all(torch.isneginf(L[:, :, :dead]))
                 assert torch.all(torch.isfinite(L[:, :, dead:]))
+
+
+def _many_items_check(O, L, Or, Lr, vmax, tag):
+    """A launch of many split workgroups against the same call unsplit: the strict variant gate."""
+    assert_variants_agree(Or, Lr, O, L, vmax, tag=tag, strict=True)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_many_split_workgroups(d):
+    """Many more (head unit, split) workgroups than the GPU keeps resident (64 sequences x 8 KV
+    groups x 16 splits = 8192, up to 47 splits): against the oracle and, strictly, the unsplit call;
+    causal and not, pack on and off."""
+    B, Sq, Sk, Hq, Hk = 64, 1, 1500, 32, 8
+    q, k, v = _qkv(9900 + d, B, Sq, Sk, Hq, Hk, d)
+    scale = gi.fp32(1 / math.sqrt(d))
+    vmax = float(v.float().abs().max())
+    for causal in (False, True):
+        Or, Lr = gpu_run(q, k, v, causal, scale, 1, 1)
+        compare_to_oracle(Or, Lr, q, k, v, causal, scale, batches=[0, 37, 63], tag=f"d={d} unsplit")
+        for pack, ns in ((1, 16), (0, 3), (1, 47)):
+            O, L = gpu_run(q, k, v, causal, scale, pack, ns)
+            compare_to_oracle(O, L, q, k, v, causal, scale, batches=[0, 37, 63], tag=f"d={d} pack={pack} ns={ns}")
+            _many_items_check(O, L, Or, Lr, vmax, f"d={d} causal={causal} pack={pack} ns={ns}")
+
+
+def test_many_splits_varlen_with_empty_sequences():
+    """Variable-length decode with empty key and query sequences among many split workgroups."""
+    import grouped_query_exact_amd as g
+    import oracle
+    import numpy as np
+    rs = np.random.default_rng(5)
+    lk = [int(x) for x in rs.integers(0, 3000, 96)]
+    lk[3] = 0
+    lk[50] = 0
+    lq = [1 + (b % 3) for b in range(96)]
+    lq[7] = 0
+    Hq, Hk, d = 32, 8, 128
+    q, k, v, cq, ck = gi.varlen_batch(9950, lq, lk, Hq, Hk, d)
+    scale = gi.fp32(1 / math.sqrt(d))
+    res = {}
+    for ns in (1, 9, 24):
+        out = torch.full((q.shape[0], Hq, d), float("nan"), dtype=torch.bfloat16, device="cuda:0")
+        lse = torch.full((Hq, q.shape[0]), float("nan"), dtype=torch.float32, device="cuda:0")
+        g.gqa_attn_fwd_varlen(q.cuda(), k.cuda(), v.cuda(), out, lse, cq.cuda(), ck.cuda(), max(lq), max(lk), True,
+                              scale, 1, ns)
+        torch.cuda.synchronize()
+        res[ns] = (out, lse)
+        Or, Lr = oracle.attention_varlen_fp64(q.double().numpy(), k.double().numpy(), v.double().numpy(),
+                                              cq.tolist(), ck.tolist(), True, scale, sequences=[0, 3, 7, 50, 95])
+        cols = np.concatenate([np.arange(int(cq[b]), int(cq[b + 1])) for b in (0, 3, 7, 50, 95)])
+        Og = out.double().cpu().numpy()[cols]
+        assert np.abs(Og - Or[cols]).max() <= 2e-2, f"ns={ns}"
+        fin = np.isfinite(Lr[:, cols])
+        Lg = lse.double().cpu().numpy()[:, cols]
+        assert np.array_equal(fin, np.isfinite(Lg)) and np.abs(Lg[fin] - Lr[:, cols][fin]).max() <= 1e-3, f"ns={ns}"
+    for ns in (9, 24):
+        assert_variants_agree(res[1][0].unsqueeze(0), None, res[ns][0].unsqueeze(0), None,
+                              float(v.float().abs().max()), tag=f"varlen ns={ns}", strict=True)

@@ -143,3 +143,25 @@ def test_kv8_one_sequence_long():
         O, L = run_kv8(q, k8, v8, ks, vs, False, scale, -1, ns)
         Or, Lr = oracle.attention_kv8_fp64(f64(q), k8.numpy(), v8.numpy(), ks, vs, False, scale)
         check(O, L, Or, Lr, f"ks={ks} vs={vs} ns={ns}")
+
+
+def test_kv8_many_split_workgroups():
+    """fp8 K/V with many more split workgroups than the GPU keeps resident (64 x 8 x 24 = 12288):
+    bit for bit the bf16 path on the same values at the same split count, and the oracle."""
+    B, Sq, Sk, Hq, Hk, d = 64, 2, 2000, 32, 8, 128
+    k8, v8 = gi.random_fp8(8800, (B, Sk, Hk, d)), gi.random_fp8(8801, (B, Sk, Hk, d))
+    q = gi.random_bf16(8802, (B, Sq, Hq, d))
+    scale = gi.fp32(1 / math.sqrt(d))
+    kb = k8.view(torch.float8_e4m3fn).to(torch.bfloat16)
+    vb = v8.view(torch.float8_e4m3fn).to(torch.bfloat16)
+    for causal in (False, True):
+        O8, L8 = run_kv8(q, k8, v8, 1.0, 1.0, causal, scale, 1, 24)
+        import grouped_query_exact_amd as g
+        ob = torch.empty((B, Sq, Hq, d), dtype=torch.bfloat16, device=DEV)
+        lb = torch.empty((B, Hq, Sq), dtype=torch.float32, device=DEV)
+        g.gqa_attn_fwd(q.to(DEV), kb.to(DEV), vb.to(DEV), ob, lb, causal, scale, 1, 24)
+        torch.cuda.synchronize()
+        assert torch.equal(O8, ob) and torch.equal(L8, lb), f"causal={causal}"
+        sel = [0, 31, 63]
+        Or, Lr = oracle.attention_kv8_fp64(f64(q[sel]), k8[sel].numpy(), v8[sel].numpy(), 1.0, 1.0, causal, scale)
+        check(O8[sel], L8[sel], Or, Lr, f"kv8 many items causal={causal}")

@@ -195,3 +195,26 @@ def test_paged_decode_full_size_sampled():
     O, L = run_paged(q, kv, False, gi.fp32(1 / math.sqrt(128)))
     assert torch.isfinite(O.float()).all()
     compare_paged(O, L, q, kv, False, gi.fp32(1 / math.sqrt(128)), batches=[0, 1, 17, 33, 48, 63], tag="full size")
+
+
+def test_paged_decode_many_split_workgroups():
+    """Paged decode with many more split workgroups than the GPU keeps resident (48 x 8 x 20),
+    pages of 16 keys in random pool order: bit for bit the contiguous call at the same splits."""
+    import grouped_query_exact_amd as g
+    B, Sq, Hq, Hk, d, ps = 48, 1, 32, 8, 128, 16
+    lens = [700 + 13 * b for b in range(B)]
+    kv = gi.paged_kv(7700, lens, ps, Hk, d).to(DEV)
+    q = gi.random_bf16(7701, (B, Sq, Hq, d)).to(DEV)
+    scale = gi.fp32(1 / math.sqrt(d))
+    for causal in (False, True):
+        out = torch.empty((B, Sq, Hq, d), dtype=torch.bfloat16, device=DEV)
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=DEV)
+        g.gqa_attn_fwd_paged(q, kv.k_cache, kv.v_cache, kv.block_table, kv.seqlens_k, out, lse, causal, scale, 1, 20)
+        torch.cuda.synchronize()
+        for b in (0, 23, 47):
+            kb, vb = gi.batch_slice(7700, b, 1, lens[b], Hq, Hk, d)[1:]
+            ob = torch.empty((1, Sq, Hq, d), dtype=torch.bfloat16, device=DEV)
+            lb = torch.empty((1, Hq, Sq), dtype=torch.float32, device=DEV)
+            g.gqa_attn_fwd(q[b:b + 1], kb[None].to(DEV), vb[None].to(DEV), ob, lb, causal, scale, 1, 20)
+            torch.cuda.synchronize()
+            assert torch.equal(out[b:b + 1], ob) and torch.equal(lse[b:b + 1], lb), f"b={b} causal={causal}"
