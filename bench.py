@@ -11,13 +11,13 @@ launches between two HIP events on the launch stream.
 
 Also measured in the same run and reported in the same JSON line (unless
 --quick), each as the median (and minimum) of >= 20 individually timed calls
-after warm-up, in this order: split-KV decode (B=64, Sq=1, Sk=8192;
+after warm-up. Before the headline: split-KV decode (B=64, Sq=1, Sk=8192;
 ns = auto, 1, 4, 8 and pack off) as HBM GB/s of Q+K+V+O+LSE bytes, the same
 decode over a paged cache and with fp8 K/V; the tiny workload (B=1, Hq=6,
 Hk=2, d=64, S=128, causal and not, pack on and off) and the short ragged
 workload (B=212, S=77, pack on and off, GB/s and the pack speedup), both
 timed with a 512 MiB write between calls so that no input stays in the
-caches; the Llama-2 prefill shape (B=4); the whole batch sweep (B = 16, 64,
+caches. After the headline: the Llama-2 prefill shape (B=4); the whole batch sweep (B = 16, 64,
 128, 256 with (pack 1, ns 1), (pack 0, ns 4) and auto); the headline shape
 with fp8 Q and K (rated against the mixed fp8/bf16 peak); a variable-length
 prefill batch next to an equal-token batched call; and the backward pass at
@@ -377,6 +377,15 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    extra = {}
+    steps_x = max(20, args.extra_steps)
+    if not args.quick:
+        # the memory-bound and small workloads first, each after its own warm-up
+        # (measured right after the compute-bound prefill they ran ~4% slower)
+        extra.update(extra_decode(g, gi, dev, steps_x))
+        torch.cuda.empty_cache()
+        extra.update(extra_small(g, gi, dev, steps_x))
+        torch.cuda.empty_cache()
     w = gi.sweep(args.batch)
     q, k, v = gi.make_qkv_device(w, dev)
     log(f"inputs ready: {w.name}")
@@ -446,15 +455,10 @@ def main():
 
     gpu_ms = {w.name: ms}
     if not args.quick:
-        steps = max(20, args.extra_steps)
-        extra = {}
-        extra.update(extra_decode(g, gi, dev, steps))
+        extra.update(extra_prefill(g, gi, dev, steps_x))
         torch.cuda.empty_cache()
-        extra.update(extra_small(g, gi, dev, steps))
-        torch.cuda.empty_cache()
-        extra.update(extra_prefill(g, gi, dev, steps))
-        torch.cuda.empty_cache()
-        extra["timing"] = f"median and minimum of {steps} individually event-timed calls after warm-up"
+        extra["timing"] = (f"median and minimum of {steps_x} individually event-timed calls after warm-up; "
+                           f"decode and the small workloads before the headline, the prefill workloads after it")
         result["extra"] = extra
         gpu_ms.update({
             "tiny_causal": extra["tiny_b1_hq6_hk2_d64_s128"]["causal_pack1"]["ms_median"],

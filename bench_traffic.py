@@ -57,8 +57,10 @@ KERNEL_SRCS = [os.path.join(ROOT, "grouped_query_exact_amd", "csrc", f)
 BWD_SRCS = [os.path.join(ROOT, "grouped_query_exact_amd", "csrc", "gqa_attn_bwd.hip")]
 PROFILES = os.path.join(ROOT, "profiles")
 COPY_BYTES = 1 << 30
-WARMUP = 5
-MEASURED = 20
+WARMUP = 5            # warm-up calls at least, and
+WARMUP_SECONDS = 0.5  # at least this long (at most WARMUP_MAX calls)
+WARMUP_MAX = 400
+MEASURED = 20         # calls whose dispatches the statistics use (the last ones of each kernel)
 KERNELS = ("attn_fwd_kernel", "attn_fwd_pingpong_kernel", "attn_decode_kernel", "combine_kernel",
            "combine_wide_kernel", "bwd_dq_kernel", "bwd_dkdv_kernel")
 PASSES = {
@@ -132,11 +134,20 @@ def child(name):
         call = lambda: g.gqa_attn_fwd_kv8(q, k8, v8, 1.0, 1.0, out, lse, w.causal, w.scale)
     else:
         call = lambda: g.gqa_attn_fwd(q, k, v, out, lse, w.causal, w.scale, pack, ns)
-    for _ in range(WARMUP + MEASURED):
+    # warm up by time as well as by count: short calls in a fresh process run
+    # well below their steady-state clock for the first few hundred milliseconds
+    t0 = time.perf_counter()
+    n = 0
+    while n < WARMUP or (time.perf_counter() - t0 < WARMUP_SECONDS and n < WARMUP_MAX):
+        call()
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
+    for _ in range(MEASURED):
         call()
     torch.cuda.synchronize()
     plan = g.gqa_attn_plan(w.B, w.Sq, w.Sk, w.Hq, w.Hk, w.d, w.causal, pack, ns)
-    print(json.dumps({"workload": name, "warmup": WARMUP, "measured": MEASURED, "plan": plan}), flush=True)
+    print(json.dumps({"workload": name, "warmup": n, "measured": MEASURED, "plan": plan}), flush=True)
 
 
 def child_copy():
@@ -223,9 +234,9 @@ def read_counters(out_dir, tag):
     return {k: {c: [v[i] for i in sorted(v)] for c, v in cs.items()} for k, cs in per.items()}
 
 
-def measured_median(values, calls_per_step):
-    """Median of the values of the MEASURED calls (the last MEASURED * calls_per_step dispatches)."""
-    tail = values[-MEASURED * calls_per_step:] if len(values) >= MEASURED * calls_per_step else values
+def measured_median(values):
+    """Median over the MEASURED calls: a kernel's last MEASURED dispatches (each kernel runs once per call)."""
+    tail = values[-MEASURED:]
     return statistics.median(tail) if tail else float("nan")
 
 
@@ -243,10 +254,9 @@ def profile_workload(name, out, prof_out, fscale, wscale, copy_cmds):
     alg, flops = workload_bytes_flops(name)
     kernels = {}
     for kname, durs in trace.items():
-        n_per = max(1, round(len(durs) / (WARMUP + MEASURED)))  # e.g. two combine launches per call: none here
-        tail = durs[-MEASURED * n_per:]
+        tail = durs[-MEASURED:]
         kc = ctr.get(kname, {})
-        med = lambda c: measured_median(kc.get(c, []), n_per)
+        med = lambda c: measured_median(kc.get(c, []))
         e = {"calls": len(durs), "median_us": statistics.median(tail) / 1e3, "mean_us": sum(tail) / len(tail) / 1e3,
              "min_us": min(tail) / 1e3, "max_us": max(tail) / 1e3,
              "fetch_bytes": med("FETCH_SIZE") * 1024 * fscale, "write_bytes": med("WRITE_SIZE") * 1024 * wscale}
@@ -257,7 +267,8 @@ def profile_workload(name, out, prof_out, fscale, wscale, copy_cmds):
     call_us = sum(k["median_us"] for k in kernels.values())
     hbm = sum(k["fetch_bytes"] + k["write_bytes"] for k in kernels.values())
     md = [f"# {name}: {desc}", "",
-          f"{WARMUP} warm-up and {MEASURED} measured calls per profiled run, seeded N(0,1) inputs on the GPU. "
+          f"At least {WARMUP} warm-up calls and {WARMUP_SECONDS} s of them, then {MEASURED} measured calls per "
+          f"profiled run, seeded N(0,1) inputs on the GPU. "
           f"Forward kernel source hash {src_hash()}, backward source hash {src_hash(BWD_SRCS)}.", "",
           "Commands (REPO = repository root on the GPU box, run from /tmp with TMPDIR=/tmp):", ""]
     md += ["    " + c.replace(ROOT, "$REPO") for c in list(cmds.values()) + copy_cmds]

@@ -235,18 +235,36 @@ int run(const Call& c) {
                      plan.combine_grid, plan.workspace_bytes);
 
     auto launch = [&](bool split) {
-        if (plan.pingpong) return gqa::launch_pingpong(p, d, s.causal != 0, c.paged, c.stream);  // unsplit only
+        if (plan.pingpong) return gqa::launch_pingpong(p, d, s.causal != 0, c.paged, c.varlen, c.stream);  // unsplit only
         return plan.decode ? gqa::launch_decode(p, d, s.causal != 0, split, c.paged, c.kv8, c.varlen, c.stream)
                            : gqa::launch_attention(p, d, s.causal != 0, split, c.varlen, c.qk8, c.paged, c.stream);
     };
-    if (plan.ns == 1) {
+    // variable-length prefill whose sequences leave most of the grid empty runs
+    // from a work list that a scheduling kernel builds on the device: the
+    // (sequence, row tile) pairs that exist, heaviest first. The list holds at
+    // most one partial row tile per sequence beyond the full ones the packed
+    // tokens fill. The 8-wavefront kernel takes variable-length calls only so.
+    const bool sched = plan.worklist != 0;
+    if (plan.pingpong && c.varlen && !sched) return GQA_ERR_UNSUPPORTED;
+    long long sched_cap = 0;
+    size_t sched_bytes = 0;
+    if (sched) {
+        sched_cap = ((long long)c.total_q * plan.Gp + plan.block_m - 1) / plan.block_m + s.B;
+        const long long grid = sched_cap * plan.units_per_b * plan.ns;
+        if (sched_cap > INT_MAX / 4 || grid > INT_MAX) return GQA_ERR_INVALID_ARG;
+        p.grid = (int)grid;
+        sched_bytes = (((size_t)(1 + 2 * sched_cap) * 4) + 255) & ~(size_t)255;
+    }
+    if (plan.ns == 1 && !sched) {
         hipError_t e = launch(false);
         return e == hipSuccess ? GQA_OK : GQA_ERR_HIP;
     }
 
     void* ws = nullptr;
-    const size_t ws_bytes = c.varlen ? (size_t)plan.ns * (size_t)c.total_q * s.Hq * ((size_t)d * 4 + 8)
-                                     : (size_t)plan.workspace_bytes;
+    const size_t split_bytes = plan.ns == 1 ? 0
+                               : c.varlen ? (size_t)plan.ns * (size_t)c.total_q * s.Hq * ((size_t)d * 4 + 8)
+                                          : (size_t)plan.workspace_bytes;
+    const size_t ws_bytes = sched_bytes + split_bytes;
     if (c.noalloc) {
         // every partial the combine reads is written by this call's attention
         // kernel (empty splits write O_s = 0, LSE_s = -inf), so nothing is cleared
@@ -259,11 +277,31 @@ int run(const Call& c) {
         }
     }
     const int64_t rows = c.varlen ? (int64_t)c.total_q * s.Hq : (int64_t)s.B * s.Sq * s.Hq;
-    p.opart = (float*)ws;
-    p.lpart = (float*)ws + (int64_t)plan.ns * rows * d;
+    hipError_t e = hipSuccess;
+    if (sched) {
+        gqa::SchedParams sp{};
+        sp.cu_q = c.cu_q;
+        sp.cu_k = c.cu_k;
+        sp.worklist = (int*)ws;
+        sp.B = s.B;
+        sp.total_q = c.total_q;
+        sp.total_k = c.total_k;
+        sp.max_sq = s.Sq;
+        sp.Gp = plan.Gp;
+        sp.gmul = fd.mul;
+        sp.gshift = fd.shift;
+        sp.block_m = plan.block_m;
+        sp.causal = s.causal;
+        sp.cap = (int)sched_cap;
+        p.worklist = (const int*)ws;
+        e = gqa::launch_schedule(sp, c.stream);
+    }
+    float* parts = (float*)((char*)ws + sched_bytes);
+    p.opart = parts;
+    p.lpart = parts + (int64_t)plan.ns * rows * d;
     p.wpart = p.lpart + (int64_t)plan.ns * rows;
-    hipError_t e = launch(true);
-    if (e == hipSuccess) {
+    if (e == hipSuccess) e = launch(plan.ns > 1);
+    if (e == hipSuccess && plan.ns > 1) {
         gqa::CombineParams cp{};
         cp.opart = p.opart;
         cp.lpart = p.lpart;
@@ -410,7 +448,8 @@ int gqa_attn_fwd_varlen(const void* q, const void* k, const void* v, void* out, 
                         float scale, int pack_gqa, int num_splits, hipStream_t stream) {
     try {
         if (total_q < 0 || total_k < 0) return GQA_ERR_INVALID_ARG;
-        const gqa::Shape s{B, max_seqlen_q, max_seqlen_k, Hq, Hk, d, causal ? 1 : 0, 2, 2, 1};
+        gqa::Shape s{B, max_seqlen_q, max_seqlen_k, Hq, Hk, d, causal ? 1 : 0, 2, 2, 1};
+        s.total_q = total_q;
         int st = gqa::check_sizes(s, scale, pack_gqa, num_splits);
         if (st != GQA_OK) return st;
         if ((long long)B * max_seqlen_q == 0 || total_q == 0) return GQA_OK;

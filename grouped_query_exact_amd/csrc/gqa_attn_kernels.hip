@@ -141,10 +141,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         tmp /= p.row_tiles;
         unit = tmp % p.units_per_b;
         b = tmp / p.units_per_b;
+    } else if (p.worklist) {
+        // sequences of very different lengths: the (sequence, row tile) pairs
+        // that exist, heaviest first, from the scheduling kernel's work list
+        // (scalar loads); the grid's spare workgroups past its end exit at once
+        typedef const __attribute__((address_space(4))) int* cint_p;
+        const cint_p wl = (cint_p)p.worklist;
+        s = blockIdx.x % p.ns;
+        const int tmp = blockIdx.x / p.ns;
+        const int pair = tmp / p.units_per_b;
+        unit = tmp % p.units_per_b;
+        if (pair >= wl[0]) return;
+        b = __builtin_amdgcn_readfirstlane(wl[1 + 2 * pair]);
+        rt = __builtin_amdgcn_readfirstlane(wl[2 + 2 * pair]);
     } else {
-        // sequences of different lengths: the row tile is the slowest index,
-        // so the heaviest causal tiles of all sequences start first; items are
-        // not of equal cost, so they are dealt round-robin over the XCDs
+        // sequences of about equal length: every row tile of the longest in
+        // every sequence, the row tile the slowest index, so the heaviest
+        // causal tiles of all sequences start first; items are not of equal
+        // cost, so they are dealt round-robin over the XCDs
         s = blockIdx.x % p.ns;
         const int tmp = blockIdx.x / p.ns;
         const int nbu = p.B * p.units_per_b;
@@ -524,9 +538,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // its softmax phase of tile t, and a workgroup waits only for tile t's copies
 // at its top. Causal masking, the row/key bookkeeping, the lazy online
 // softmax in base 2 and the epilogue are those of attn_fwd_kernel.
-template <int D, bool CAUSAL, bool PAGED>
+template <int D, bool CAUSAL, bool PAGED, bool VARLEN>
 __global__ __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_pingpong_kernel(
     const FwdParams p) {
+    static_assert(!(PAGED && VARLEN), "paged calls have one query length");
     constexpr int TILE = kBlockN * D;
     constexpr int TILE_B = TILE * 2;
     constexpr int NCH = D / 8;
@@ -544,19 +559,33 @@ __global__ __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2
     const int lane = tid & 63;
     const int col = lane & 31, half = lane >> 5;
 
-    // ---- work item: (batch, head unit, row tile descending), XCD-contiguous
-    const int logical = xcd_remap(blockIdx.x, p.grid);
-    const int rt = p.row_tiles - 1 - (logical % p.row_tiles);
-    const int tmpu = logical / p.row_tiles;
-    const int unit = tmpu % p.units_per_b;
-    const int b = tmpu / p.units_per_b;
+    // ---- work item: (batch, head unit, row tile descending), XCD-contiguous;
+    // variable-length calls: the scheduling kernel's work list, as in
+    // attn_fwd_kernel (the plan routes them here only with one)
+    int rt, unit, b;
+    if (!VARLEN) {
+        const int logical = xcd_remap(blockIdx.x, p.grid);
+        rt = p.row_tiles - 1 - (logical % p.row_tiles);
+        const int tmpu = logical / p.row_tiles;
+        unit = tmpu % p.units_per_b;
+        b = tmpu / p.units_per_b;
+    } else {
+        typedef const __attribute__((address_space(4))) int* cint_p;
+        const cint_p wl = (cint_p)p.worklist;
+        const int pair = (int)blockIdx.x / p.units_per_b;
+        unit = (int)blockIdx.x % p.units_per_b;
+        if (pair >= wl[0]) return;  // uniform over the workgroup
+        b = __builtin_amdgcn_readfirstlane(wl[1 + 2 * pair]);
+        rt = __builtin_amdgcn_readfirstlane(wl[2 + 2 * pair]);
+    }
     const int g = p.Gp > 1 ? unit : unit / p.G;
     const int h0 = p.Gp > 1 ? unit * p.G : unit;
     const int r0 = rt * kPPBlockM;
-    const int Sq = p.Sq;
-    const int Sk = PAGED ? __builtin_amdgcn_readfirstlane(min(max(p.seqlens_k[b], 0), p.max_pages * p.page_size)) : p.Sk;
-    const int64_t qtok0 = (int64_t)b * Sq, ktok0 = (int64_t)b * p.Sk;
-    const int R = p.R;
+    int Sq = p.Sq, Sk = p.Sk;
+    int64_t qtok0 = (int64_t)b * p.Sq, ktok0 = (int64_t)b * p.Sk;
+    if (VARLEN) seq_extent(p, b, qtok0, Sq, ktok0, Sk);
+    if (PAGED) Sk = __builtin_amdgcn_readfirstlane(min(max(p.seqlens_k[b], 0), p.max_pages * p.page_size));
+    const int R = VARLEN ? Sq * p.Gp : p.R;
 
     // ---- this lane's row: token ti, head hh
     const int r = r0 + wave * 32 + col;
@@ -835,7 +864,7 @@ __global__ __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2
                 for (int i = 0; i < 8; ++i) ov[i] = (__bf16)(oacc[cb][run2 * 8 + i] * inv);
                 *(bf16x8*)(orow + cb * 32 + run2 * 16 + half * 8) = ov;
             }
-        if (half == 0 && p.lse) p.lse[((int64_t)b * p.Hq + hh) * Sq + ti] = lse_val;
+        if (half == 0 && p.lse) p.lse[lse_index(p, b, hh, qtok0, ti, VARLEN)] = lse_val;
     }
 }
 
@@ -1320,6 +1349,96 @@ __global__ __launch_bounds__(256) void combine_wide_kernel(const CombineParams p
     if (c4 == 0 && p.lse) p.lse[lse_row(p, row)] = live ? M + __logf(T) : -__builtin_inff();
 }
 
+// Work list of a variable-length prefill call. The tiled kernel's grid for
+// such a call would otherwise hold an item for every row tile of the longest
+// sequence in every sequence, most of which exit at once. This kernel lists
+// the (sequence, row tile) pairs that exist, ordered by their key tiles
+// (heaviest first, so the long causal tiles of all sequences start first and
+// the short ones fill the tail): a counting sort with one LDS histogram over
+// the cost, an exclusive scan of the bins from the top, and a scatter. Pairs
+// of equal cost land in any order (the results do not depend on the order).
+__global__ __launch_bounds__(kSchedThreads) void varlen_schedule_kernel(const SchedParams sp) {
+    __shared__ int hist[kSchedBins];
+    __shared__ int start[kSchedBins];
+    const int tid = threadIdx.x;
+    for (int i = tid; i < kSchedBins; i += kSchedThreads) hist[i] = 0;
+    __syncthreads();
+    // sequence b: its query tokens (clamped to max_sq) and keys, as seq_extent clamps them
+    auto extent = [&](int b, int& Sq, int& Sk) {
+        const int q0 = min(max(sp.cu_q[b], 0), sp.total_q);
+        const int q1 = min(max(sp.cu_q[b + 1], q0), sp.total_q);
+        const int k0 = min(max(sp.cu_k[b], 0), sp.total_k);
+        const int k1 = min(max(sp.cu_k[b + 1], k0), sp.total_k);
+        Sq = min(q1 - q0, sp.max_sq);
+        Sk = k1 - k0;
+    };
+    // key tiles of row tile rt (the attention kernel's count), as a bin
+    auto cost_bin = [&](int R, int Sq, int Sk, int rt) {
+        int kv_end = Sk;
+        if (sp.causal) {
+            const int r_last = min((rt + 1) * sp.block_m, R) - 1;
+            const int i_max = (int)fdiv((uint32_t)r_last, sp.gmul, sp.gshift);
+            kv_end = min(Sk, i_max + (Sk - Sq) + 1);
+        }
+        const int T = kv_end > 0 ? (kv_end + kBlockN - 1) / kBlockN : 0;
+        return min(T, kSchedBins - 1);
+    };
+    for (int b = tid; b < sp.B; b += kSchedThreads) {
+        int Sq, Sk;
+        extent(b, Sq, Sk);
+        const int R = Sq * sp.Gp;
+        for (int rt = 0; rt * sp.block_m < R; ++rt) atomicAdd(&hist[cost_bin(R, Sq, Sk, rt)], 1);
+    }
+    __syncthreads();
+    // exclusive scan of the bins from the heaviest down: thread t holds bin
+    // kSchedBins-1-t; scans within each wavefront, then over the wavefronts' totals
+    {
+        static_assert(kSchedThreads == kSchedBins && kSchedThreads == 1024, "one bin per thread, 16 wavefronts");
+        __shared__ int wsum[16];
+        const int lane = tid & 63, w = tid >> 6;
+        const int val = hist[kSchedBins - 1 - tid];
+        int x = val;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int y = __shfl_up(x, off, 64);
+            if (lane >= off) x += y;
+        }
+        if (lane == 63) wsum[w] = x;
+        __syncthreads();
+        if (w == 0) {
+            int t = lane < 16 ? wsum[lane] : 0;
+#pragma unroll
+            for (int off = 1; off < 16; off <<= 1) {
+                const int y = __shfl_up(t, off, 64);
+                if (lane >= off) t += y;
+            }
+            if (lane < 16) wsum[lane] = t;
+        }
+        __syncthreads();
+        const int incl = x + (w > 0 ? wsum[w - 1] : 0);
+        start[kSchedBins - 1 - tid] = incl - val;
+        if (tid == kSchedThreads - 1) sp.worklist[0] = min(incl, sp.cap);
+    }
+    __syncthreads();
+    for (int b = tid; b < sp.B; b += kSchedThreads) {
+        int Sq, Sk;
+        extent(b, Sq, Sk);
+        const int R = Sq * sp.Gp;
+        for (int rt = 0; rt * sp.block_m < R; ++rt) {
+            const int slot = atomicAdd(&start[cost_bin(R, Sq, Sk, rt)], 1);
+            if (slot < sp.cap) {
+                sp.worklist[1 + 2 * slot] = b;
+                sp.worklist[2 + 2 * slot] = rt;
+            }
+        }
+    }
+}
+
+hipError_t launch_schedule(const SchedParams& sp, hipStream_t stream) {
+    hipLaunchKernelGGL(varlen_schedule_kernel, dim3(1), dim3(kSchedThreads), 0, stream, sp);
+    return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- launchers
 template <int D, bool CAUSAL, bool SPLIT, bool VARLEN, bool QK8, bool PAGED>
 static hipError_t launch_attn(const FwdParams& p, hipStream_t stream) {
@@ -1352,16 +1471,18 @@ hipError_t launch_attention(const FwdParams& p, int d, bool causal, bool split, 
                     : launch_attn_dd<64>(p, causal, split, varlen, qk8, paged, stream);
 }
 
+template <bool CAUSAL, bool PAGED, bool VARLEN>
+static void launch_pp(const FwdParams& p, hipStream_t stream) {
+    hipLaunchKernelGGL((attn_fwd_pingpong_kernel<128, CAUSAL, PAGED, VARLEN>), dim3(p.grid), dim3(kPPThreads), 0,
+                       stream, p);
+}
+
 // d=128 only (the plan never picks this kernel at d=64)
-hipError_t launch_pingpong(const FwdParams& p, int d, bool causal, bool paged, hipStream_t stream) {
-    if (d != 128) return hipErrorInvalidValue;
-    if (paged) {
-        if (causal) hipLaunchKernelGGL((attn_fwd_pingpong_kernel<128, true, true>), dim3(p.grid), dim3(kPPThreads), 0, stream, p);
-        else hipLaunchKernelGGL((attn_fwd_pingpong_kernel<128, false, true>), dim3(p.grid), dim3(kPPThreads), 0, stream, p);
-    } else {
-        if (causal) hipLaunchKernelGGL((attn_fwd_pingpong_kernel<128, true, false>), dim3(p.grid), dim3(kPPThreads), 0, stream, p);
-        else hipLaunchKernelGGL((attn_fwd_pingpong_kernel<128, false, false>), dim3(p.grid), dim3(kPPThreads), 0, stream, p);
-    }
+hipError_t launch_pingpong(const FwdParams& p, int d, bool causal, bool paged, bool varlen, hipStream_t stream) {
+    if (d != 128 || (paged && varlen)) return hipErrorInvalidValue;
+    if (paged) causal ? launch_pp<true, true, false>(p, stream) : launch_pp<false, true, false>(p, stream);
+    else if (varlen) causal ? launch_pp<true, false, true>(p, stream) : launch_pp<false, false, true>(p, stream);
+    else causal ? launch_pp<true, false, false>(p, stream) : launch_pp<false, false, false>(p, stream);
     return hipGetLastError();
 }
 

@@ -112,16 +112,32 @@ int make_plan(const Shape& s, int pack_gqa, int num_splits, int num_cus, Plan* p
     p->key_tiles = p->R > 0 ? key_tiles_for(s, p->Gp, p->R, p->block_n) : 0;
     ns = std::max(1, std::min(ns, std::max(1, p->key_tiles)));
     p->ns = ns;
+    // Variable-length prefill whose sequences leave most of the grid empty
+    // (fewer than 3/4 of B * max_seqlen_q query tokens) runs from a work list
+    // that a scheduling kernel builds on the device: only the (sequence, row
+    // tile) items that exist, heaviest first. With about full sequences the
+    // plain grid is as good and saves that launch (measured on MI355X, Llama-2
+    // heads, causal: 8 x 2048 tokens 855 TFLOP/s from the grid against 801
+    // from the list; 16 sequences of 128..2048 tokens 704 against 742, and 48
+    // of 100..1839 tokens 673 against 721, from the list on the 8-wavefront
+    // kernel).
+    p->worklist = s.varlen && !p->decode && 4 * s.total_q < 3LL * s.B * s.Sq ? 1 : 0;
     // unsplit bf16 calls at d=128 with enough 256-row items to give every
     // compute unit kPPMinItemsPerCU of them run on the 8-wavefront kernel
     // (or one per compute unit when the items are long: an estimated average
-    // of at least kPPMinKeyTiles key tiles, from the first and last row tile)
-    // (variable-length calls stay on the 4-wavefront kernel: their grid holds
-    // an item for every row tile of the longest sequence in every sequence,
-    // and the empty ones cost the 8-wavefront kernel more: 16 sequences of
-    // 128..2048 tokens ran at 683 TFLOP/s on it against 730 on the 4-wavefront kernel)
+    // of at least kPPMinKeyTiles key tiles, from the first and last row
+    // tile); variable-length calls only from a work list, counting the items
+    // their tokens fill (without one, the empty items of the grid cost the
+    // 8-wavefront kernel more: 683 TFLOP/s on it against 730 on the
+    // 4-wavefront kernel for 16 sequences of 128..2048 tokens)
     p->pingpong = 0;
-    if (!p->decode && ns == 1 && s.d == 128 && s.q_bytes == 2 && s.kv_bytes == 2 && !s.varlen) {
+    const bool pp_shape = !p->decode && ns == 1 && s.d == 128 && s.q_bytes == 2 && s.kv_bytes == 2;
+    if (pp_shape && s.varlen) {
+        if (p->worklist) {
+            const long long items = p->units_per_b * (ceil_div(s.total_q * p->Gp, kPPBlockM) + s.B);
+            if (items >= (long long)kPPMinItemsPerCU * (num_cus > 0 ? num_cus : 256)) p->pingpong = 1;
+        }
+    } else if (pp_shape) {
         const long long items = (long long)s.B * p->units_per_b * ceil_div(p->R, kPPBlockM);
         const long long cus = num_cus > 0 ? num_cus : 256;
         if (items >= (long long)kPPMinItemsPerCU * cus) {

@@ -67,7 +67,8 @@ struct Shape {
     int B, Sq, Sk, Hq, Hk, d, causal;
     int kv_bytes = 2;  // bytes per stored K/V element: 2 (bf16) or 1 (fp8)
     int q_bytes = 2;   // bytes per stored Q element: 2 (bf16) or 1 (fp8 Q and K: tiled kernel only)
-    int varlen = 0;    // packed sequences of different lengths (4-wavefront tiled or decode kernel)
+    int varlen = 0;    // packed sequences of different lengths (Sq, Sk: the bounds max_seqlen_q, max_seqlen_k)
+    long long total_q = 0;  // variable-length calls: query tokens of all sequences
     int paged = 0;     // K/V in a pool of pages
 };
 
@@ -80,6 +81,7 @@ void choose(const Shape& s, int num_cus, int* pack_gqa, int* num_splits);
 struct Plan {
     int decode;         // 1: decode kernel (R <= kDecBlockM), 0: tiled kernel
     int pingpong;       // 1: the 8-wavefront tiled kernel (kPPBlockM rows), 0: 4 wavefronts
+    int worklist;       // variable-length prefill: items from the scheduling kernel's work list
     int threads;        // threads per attention workgroup
     int block_m;        // query rows per tile
     int block_n;        // keys per tile

@@ -41,7 +41,26 @@ struct FwdParams {
     const int* cu_q;         // [B+1] cumulative query lengths
     const int* cu_k;         // [B+1] cumulative key lengths
     int total_q, total_k;
+    // variable-length calls on the tiled kernel: the work list the scheduling
+    // kernel wrote (count, then (sequence, row tile) pairs, heaviest first);
+    // workgroup i takes pair (i / ns) / units_per_b, head unit (i / ns) % units_per_b
+    const int* worklist;
 };
+
+// The scheduling kernel of variable-length prefill (one workgroup).
+struct SchedParams {
+    const int* cu_q;
+    const int* cu_k;
+    int* worklist;           // [1 + 2 * cap]: count, then (b, rt) pairs
+    int B, total_q, total_k, max_sq, Gp;
+    uint32_t gmul, gshift;   // magic divisor of Gp
+    int block_m;             // rows per tile of the attention kernel
+    int causal;
+    int cap;                 // pairs the list can hold
+};
+hipError_t launch_schedule(const SchedParams& sp, hipStream_t stream);
+constexpr int kSchedThreads = 1024;
+constexpr int kSchedBins = 1024;  // cost bins (key tiles), the last one collects longer items
 
 struct CombineParams {
     const float* opart;
@@ -85,7 +104,7 @@ hipError_t launch_backward(const BwdParams& p, int d, bool causal, hipStream_t s
 hipError_t launch_attention(const FwdParams& p, int d, bool causal, bool split, bool varlen, bool qk8, bool paged,
                             hipStream_t stream);
 // unsplit bf16 prefill on the 8-wavefront kernel (p.row_tiles of kPPBlockM rows)
-hipError_t launch_pingpong(const FwdParams& p, int d, bool causal, bool paged, hipStream_t stream);
+hipError_t launch_pingpong(const FwdParams& p, int d, bool causal, bool paged, bool varlen, hipStream_t stream);
 hipError_t launch_decode(const FwdParams& p, int d, bool causal, bool split, bool paged, bool kv8, bool varlen,
                          hipStream_t stream);
 hipError_t launch_combine(const CombineParams& p, int d, long long grid, hipStream_t stream);

@@ -47,7 +47,9 @@
  * forward call whose split count resolves to 1 enqueues exactly one kernel
  * and nothing else (no allocation, memset or copy), so it can be captured in
  * a HIP graph and replayed; split calls also enqueue the workspace
- * allocation, the combine kernel and the release of the workspace.
+ * allocation, the combine kernel and the release of the workspace, and
+ * variable-length prefill calls of very different lengths a scheduling kernel
+ * and its workspace.
  */
 #ifndef GQA_ATTN_H
 #define GQA_ATTN_H
@@ -167,6 +169,13 @@ int gqa_attn_bwd(const void* q, const void* k, const void* v, const void* out, c
  * count to max_seqlen_q, so bad offsets give wrong results (tokens past
  * max_seqlen_q of a sequence are not written), never an out-of-bounds
  * access. Pointers as for gqa_attn_fwd (the offset arrays 4-byte aligned).
+ * Calls with more than 32 query rows per head unit whose sequences hold
+ * fewer than 3/4 of B * max_seqlen_q query tokens first run a small
+ * scheduling kernel that lists, from the offsets, the (sequence, row tile)
+ * work items that exist, heaviest first, into a stream-ordered workspace of
+ * 4 * (1 + 2 * (ceil(total_q * G / M) + B)) bytes (G = Hq/Hk with PackGQA,
+ * else 1; M = 128 rows per tile, 256 on the 8-wavefront kernel) taken from
+ * the library's pool with the split workspace, if any.
  * Returns a gqa_status_t (B*max_seqlen_q == 0 or total_q == 0: no-op). */
 int gqa_attn_fwd_varlen(const void* q, const void* k, const void* v, void* out, float* lse,
                         const int* cu_seqlens_q, const int* cu_seqlens_k,

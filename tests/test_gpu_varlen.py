@@ -148,3 +148,48 @@ def test_varlen_split_leaves_unwritten_tokens_untouched(lq, lk, max_sq):
             ok = [b for b, n in enumerate(lq) if n <= max_sq]  # sequences within max_seqlen_q: exact results
             check(out, lse, q, k, v, cq, ck, causal, scale, sequences=ok, tag=tag)
 
+
+
+def test_varlen_work_list_many_sequences():
+    """1500 short sequences (more than the scheduling kernel's 1024 threads), empty ones, and one
+    sequence whose 70000 keys put its row tiles in the top cost bin; causal with more keys than
+    queries, splits and not. Sampled sequences against the oracle."""
+    import numpy as np
+    rs = np.random.default_rng(12)
+    B = 1500
+    lq = [int(x) for x in rs.integers(0, 61, B)]
+    lk = [n + int(x) for n, x in zip(lq, rs.integers(0, 101, B))]
+    lq[10], lk[10] = 0, 0
+    lq[11] = 0
+    lq[700], lk[700] = 100, 70000
+    q, k, v, cq, ck = gi.varlen_batch(9700, lq, lk, 8, 2, 64)
+    scale = gi.fp32(1 / math.sqrt(64))
+    sel = [0, 10, 11, 12, 700, 1023, 1024, 1499]
+    for causal in (False, True):
+        for pack, ns in ((1, 1), (1, 3)):
+            O, L = run_varlen(q, k, v, cq, ck, causal, scale, pack, ns)
+            check(O, L, q, k, v, cq, ck, causal, scale, sequences=sel, tag=f"causal={causal} ns={ns}")
+
+
+@pytest.mark.parametrize("lens", [[300, 280, 290, 120],    # >= 3/4 of B * max_seqlen_q tokens: the plain grid
+                                  [300, 20, 290, 1]])      # fewer: the work list
+def test_varlen_grid_and_work_list_paths(lens):
+    """Both ways of laying out variable-length prefill items, causal and not, both packings
+    and a split, against the oracle on every sequence."""
+    q, k, v, cq, ck = gi.varlen_batch(9800 + len(lens) + lens[1], lens, lens, 8, 2, 128)
+    scale = gi.fp32(1 / math.sqrt(128))
+    for causal in (False, True):
+        for pack, ns in ((1, 1), (0, 1), (1, 2)):
+            O, L = run_varlen(q, k, v, cq, ck, causal, scale, pack, ns)
+            check(O, L, q, k, v, cq, ck, causal, scale, tag=f"lens={lens} causal={causal} pack={pack} ns={ns}")
+
+
+def test_varlen_llama_mix_8_wavefront_kernel_full():
+    """Llama-2 heads, 16 sequences of 40 to 940 tokens: the work list on the 8-wavefront kernel
+    (enough 256-row items); every sequence against the oracle."""
+    lens = [40 + 60 * i for i in range(16)]
+    q, k, v, cq, ck = gi.varlen_batch(9900, lens, lens, 32, 8, 128)
+    scale = gi.fp32(1 / math.sqrt(128))
+    for causal in (True, False):
+        O, L = run_varlen(q, k, v, cq, ck, causal, scale)
+        check(O, L, q, k, v, cq, ck, causal, scale, tag=f"causal={causal}")
