@@ -62,7 +62,8 @@ WARMUP_SECONDS = 0.5  # at least this long (at most WARMUP_MAX calls)
 WARMUP_MAX = 400
 MEASURED = 20         # calls whose dispatches the statistics use (the last ones of each kernel)
 KERNELS = ("attn_fwd_kernel", "attn_fwd_pingpong_kernel", "attn_decode_kernel", "combine_kernel",
-           "combine_wide_kernel", "bwd_dq_kernel", "bwd_dkdv_kernel")
+           "combine_wide_kernel", "bwd_dq_kernel", "bwd_dkdv_kernel", "varlen_schedule_kernel")
+VARLEN_LENS = [128 * (i + 1) for i in range(16)]  # packed sequences of the variable-length workload
 PASSES = {
     "fetch": ["FETCH_SIZE"],
     "write": ["WRITE_SIZE"],
@@ -82,6 +83,8 @@ WORKLOADS = {
     "llama2_prefill_b4_s2048_bwd": ("attn_bwd", "backward at the Llama-2 prefill shape, causal"),
     "qk8_sweep_b128_s2048": ("attn_fwd", "the headline shape with fp8 e4m3 Q and K (gqa_attn_fwd_qk8)"),
     "kv8_decode_b64_sk8192": ("attn_fwd", "the decode workload with fp8 e4m3 K and V (gqa_attn_fwd_kv8)"),
+    "varlen_16seq_128to2048": ("attn_fwd", "16 packed sequences of 128, 256, ..., 2048 tokens, causal, Hq=32, Hk=8, "
+                                           "d=128 (gqa_attn_fwd_varlen)"),
 }
 
 
@@ -111,13 +114,22 @@ def child(name):
     base = {"sweep_b128_s2048": gi.sweep(128), "llama2_prefill_b4_s2048": gi.LLAMA_PREFILL,
             "decode_b64_sk8192": gi.DECODE, "decode_b64_sk8192_ns4": gi.DECODE, "decode_b64_sk8192_ns8": gi.DECODE,
             "ragged_b212_s77": gi.RAGGED, "llama2_prefill_b4_s2048_bwd": gi.LLAMA_PREFILL,
-            "qk8_sweep_b128_s2048": gi.sweep(128), "kv8_decode_b64_sk8192": gi.DECODE}[name]
+            "qk8_sweep_b128_s2048": gi.sweep(128), "kv8_decode_b64_sk8192": gi.DECODE,
+            "varlen_16seq_128to2048": gi.LLAMA_PREFILL}[name]
     w = base
+    if name.startswith("varlen_"):  # one batch element of len(VARLEN_LENS) * ... tokens, packed
+        w = w.with_(B=1, Sq=sum(VARLEN_LENS), Sk=sum(VARLEN_LENS))
     q, k, v = _inputs(w, dev, 1234)
     out = torch.empty_like(q)
     lse = torch.empty((w.B, w.Hq, w.Sq), dtype=torch.float32, device=dev)
     pack, ns = {"decode_b64_sk8192_ns4": (1, 4), "decode_b64_sk8192_ns8": (1, 8)}.get(name, (-1, 0))
-    if name.endswith("_bwd"):
+    plan = None
+    if name.startswith("varlen_"):
+        cu = torch.tensor([0] + torch.tensor(VARLEN_LENS).cumsum(0).tolist(), dtype=torch.int32, device=dev)
+        qv, kv_, vv, ov = q[0], k[0], v[0], out[0]
+        call = lambda: g.gqa_attn_fwd_varlen(qv, kv_, vv, ov, lse[0], cu, cu, max(VARLEN_LENS), max(VARLEN_LENS),
+                                             w.causal, w.scale)
+    elif name.endswith("_bwd"):
         do = torch.randn_like(q, dtype=torch.float32).to(torch.bfloat16)
         g.gqa_attn_fwd(q, k, v, out, lse, w.causal, w.scale)
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
@@ -146,7 +158,8 @@ def child(name):
     for _ in range(MEASURED):
         call()
     torch.cuda.synchronize()
-    plan = g.gqa_attn_plan(w.B, w.Sq, w.Sk, w.Hq, w.Hk, w.d, w.causal, pack, ns)
+    if not name.startswith("varlen_"):
+        plan = g.gqa_attn_plan(w.B, w.Sq, w.Sk, w.Hq, w.Hk, w.d, w.causal, pack, ns)
     print(json.dumps({"workload": name, "warmup": n, "measured": MEASURED, "plan": plan}), flush=True)
 
 
@@ -178,6 +191,11 @@ def workload_bytes_flops(name):
         qb, kb, rb = w.B * w.Sq * w.Hq * w.d * 2, w.B * w.Sk * w.Hk * w.d * 2, w.B * w.Hq * w.Sq * 4
         # Q O dO read, dQ written; K V read, dK dV written; LSE read, D and base-2 LSE written and read
         return 4 * qb + 4 * kb + 5 * rb, 2.5 * w.flops
+    if name.startswith("varlen_"):
+        w, tot = gi.LLAMA_PREFILL, sum(VARLEN_LENS)
+        flops = sum(4.0 * w.Hq * n * n * w.d / 2 for n in VARLEN_LENS)
+        # Q, O bf16; K, V bf16; LSE fp32; the offsets and the work list are a few KB
+        return 4 * tot * w.Hq * w.d + 4 * tot * w.Hk * w.d + 4 * tot * w.Hq, flops
     w = {"sweep_b128_s2048": gi.sweep(128), "llama2_prefill_b4_s2048": gi.LLAMA_PREFILL,
          "ragged_b212_s77": gi.RAGGED}.get(name, gi.DECODE)
     return w.io_bytes, w.flops
@@ -263,9 +281,12 @@ def profile_workload(name, out, prof_out, fscale, wscale, copy_cmds):
         for c in set(sum(PASSES.values(), [])) - {"FETCH_SIZE", "WRITE_SIZE"}:
             e[c] = med(c)
         kernels[short_name(kname)] = e
-    main = max(kernels, key=lambda k: kernels[k]["median_us"])
-    call_us = sum(k["median_us"] for k in kernels.values())
-    hbm = sum(k["fetch_bytes"] + k["write_bytes"] for k in kernels.values())
+    # kernels dispatched fewer times than there are measured calls ran once for
+    # the set-up (the backward's forward pass), not in every call
+    per_call = {k: e for k, e in kernels.items() if e["calls"] >= MEASURED}
+    main = max(per_call, key=lambda k: per_call[k]["median_us"])
+    call_us = sum(k["median_us"] for k in per_call.values())
+    hbm = sum(k["fetch_bytes"] + k["write_bytes"] for k in per_call.values())
     md = [f"# {name}: {desc}", "",
           f"At least {WARMUP} warm-up calls and {WARMUP_SECONDS} s of them, then {MEASURED} measured calls per "
           f"profiled run, seeded N(0,1) inputs on the GPU. "
@@ -275,10 +296,10 @@ def profile_workload(name, out, prof_out, fscale, wscale, copy_cmds):
     md += ["", f"Kernel trace (rocprofv3 --kernel-trace; statistics over the {MEASURED} measured calls):", "",
            "| kernel | dispatches | median (us) | mean (us) | min (us) | max (us) |", "|---|---|---|---|---|---|"]
     for kn, e in kernels.items():
-        md.append(f"| `{kn}` | {e['calls']} | {e['median_us']:.2f} | {e['mean_us']:.2f} | {e['min_us']:.2f} | "
-                  f"{e['max_us']:.2f} |")
+        md.append(f"| `{kn}`{'' if kn in per_call else ' (set-up, once)'} | {e['calls']} | {e['median_us']:.2f} | "
+                  f"{e['mean_us']:.2f} | {e['min_us']:.2f} | {e['max_us']:.2f} |")
     rate_flops = flops / (call_us * 1e-6) / 1e12
-    md += ["", f"One call at the medians: {call_us:.2f} us = {rate_flops:.1f} TFLOP/s of the metric's flops "
+    md += ["", f"One call at the medians (the kernels every call runs): {call_us:.2f} us = {rate_flops:.1f} TFLOP/s of the metric's flops "
                f"({flops / 1e9:.1f} GFLOP) and {alg / (call_us * 1e-6) / 1e9:.1f} GB/s of algorithmic bytes "
                f"({alg / 1e9:.4f} GB).", "",
            f"HBM traffic per call (median of the measured dispatches; FETCH_SIZE x{fscale:.3f}, WRITE_SIZE "
@@ -303,7 +324,7 @@ def profile_workload(name, out, prof_out, fscale, wscale, copy_cmds):
         f.write("\n".join(md))
     print(f"[profile] {name}: {call_us:.1f} us per call, main kernel {main} "
           f"MfmaUtil {kernels[main].get('MfmaUtil', float('nan')):.1f}%, HBM {hbm / alg:.3f} x algorithmic", flush=True)
-    return {"kernels": kernels, "main_kernel": main, "hbm_bytes_per_call": hbm, "algorithmic_bytes": alg,
+    return {"kernels": per_call, "main_kernel": main, "hbm_bytes_per_call": hbm, "algorithmic_bytes": alg,
             "hbm_bytes_per_launch": kernels[main]["fetch_bytes"] + kernels[main]["write_bytes"],
             "call_us_median": call_us, "measured": time.strftime("%Y-%m-%d %H:%M:%S")}
 
