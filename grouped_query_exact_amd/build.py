@@ -28,6 +28,7 @@ COMMON = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}", "-Wall", "-Wno
 SOURCES = [
     ("gqa_attn_kernels.hip", True),
     ("gqa_attn_bwd.hip", True),
+    ("gqa_attn_sched.hip", True),
     ("gqa_attn_scratch.hip", True),
     ("gqa_attn_api.cpp", False),
     ("host_logic.cpp", False),

@@ -1349,96 +1349,6 @@ __global__ __launch_bounds__(256) void combine_wide_kernel(const CombineParams p
     if (c4 == 0 && p.lse) p.lse[lse_row(p, row)] = live ? M + __logf(T) : -__builtin_inff();
 }
 
-// Work list of a variable-length prefill call. The tiled kernel's grid for
-// such a call would otherwise hold an item for every row tile of the longest
-// sequence in every sequence, most of which exit at once. This kernel lists
-// the (sequence, row tile) pairs that exist, ordered by their key tiles
-// (heaviest first, so the long causal tiles of all sequences start first and
-// the short ones fill the tail): a counting sort with one LDS histogram over
-// the cost, an exclusive scan of the bins from the top, and a scatter. Pairs
-// of equal cost land in any order (the results do not depend on the order).
-__global__ __launch_bounds__(kSchedThreads) void varlen_schedule_kernel(const SchedParams sp) {
-    __shared__ int hist[kSchedBins];
-    __shared__ int start[kSchedBins];
-    const int tid = threadIdx.x;
-    for (int i = tid; i < kSchedBins; i += kSchedThreads) hist[i] = 0;
-    __syncthreads();
-    // sequence b: its query tokens (clamped to max_sq) and keys, as seq_extent clamps them
-    auto extent = [&](int b, int& Sq, int& Sk) {
-        const int q0 = min(max(sp.cu_q[b], 0), sp.total_q);
-        const int q1 = min(max(sp.cu_q[b + 1], q0), sp.total_q);
-        const int k0 = min(max(sp.cu_k[b], 0), sp.total_k);
-        const int k1 = min(max(sp.cu_k[b + 1], k0), sp.total_k);
-        Sq = min(q1 - q0, sp.max_sq);
-        Sk = k1 - k0;
-    };
-    // key tiles of row tile rt (the attention kernel's count), as a bin
-    auto cost_bin = [&](int R, int Sq, int Sk, int rt) {
-        int kv_end = Sk;
-        if (sp.causal) {
-            const int r_last = min((rt + 1) * sp.block_m, R) - 1;
-            const int i_max = (int)fdiv((uint32_t)r_last, sp.gmul, sp.gshift);
-            kv_end = min(Sk, i_max + (Sk - Sq) + 1);
-        }
-        const int T = kv_end > 0 ? (kv_end + kBlockN - 1) / kBlockN : 0;
-        return min(T, kSchedBins - 1);
-    };
-    for (int b = tid; b < sp.B; b += kSchedThreads) {
-        int Sq, Sk;
-        extent(b, Sq, Sk);
-        const int R = Sq * sp.Gp;
-        for (int rt = 0; rt * sp.block_m < R; ++rt) atomicAdd(&hist[cost_bin(R, Sq, Sk, rt)], 1);
-    }
-    __syncthreads();
-    // exclusive scan of the bins from the heaviest down: thread t holds bin
-    // kSchedBins-1-t; scans within each wavefront, then over the wavefronts' totals
-    {
-        static_assert(kSchedThreads == kSchedBins && kSchedThreads == 1024, "one bin per thread, 16 wavefronts");
-        __shared__ int wsum[16];
-        const int lane = tid & 63, w = tid >> 6;
-        const int val = hist[kSchedBins - 1 - tid];
-        int x = val;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const int y = __shfl_up(x, off, 64);
-            if (lane >= off) x += y;
-        }
-        if (lane == 63) wsum[w] = x;
-        __syncthreads();
-        if (w == 0) {
-            int t = lane < 16 ? wsum[lane] : 0;
-#pragma unroll
-            for (int off = 1; off < 16; off <<= 1) {
-                const int y = __shfl_up(t, off, 64);
-                if (lane >= off) t += y;
-            }
-            if (lane < 16) wsum[lane] = t;
-        }
-        __syncthreads();
-        const int incl = x + (w > 0 ? wsum[w - 1] : 0);
-        start[kSchedBins - 1 - tid] = incl - val;
-        if (tid == kSchedThreads - 1) sp.worklist[0] = min(incl, sp.cap);
-    }
-    __syncthreads();
-    for (int b = tid; b < sp.B; b += kSchedThreads) {
-        int Sq, Sk;
-        extent(b, Sq, Sk);
-        const int R = Sq * sp.Gp;
-        for (int rt = 0; rt * sp.block_m < R; ++rt) {
-            const int slot = atomicAdd(&start[cost_bin(R, Sq, Sk, rt)], 1);
-            if (slot < sp.cap) {
-                sp.worklist[1 + 2 * slot] = b;
-                sp.worklist[2 + 2 * slot] = rt;
-            }
-        }
-    }
-}
-
-hipError_t launch_schedule(const SchedParams& sp, hipStream_t stream) {
-    hipLaunchKernelGGL(varlen_schedule_kernel, dim3(1), dim3(kSchedThreads), 0, stream, sp);
-    return hipGetLastError();
-}
-
 // ---------------------------------------------------------------- launchers
 template <int D, bool CAUSAL, bool SPLIT, bool VARLEN, bool QK8, bool PAGED>
 static hipError_t launch_attn(const FwdParams& p, hipStream_t stream) {
