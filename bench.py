@@ -67,17 +67,24 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def time_calls(fn, steps: int, warmup: int, flush=None):
+def time_calls(fn, steps: int, warmup: int, flush=None, warmup_s: float = 0.3):
     """Per-call times of fn (ms): HIP events around each call on torch's current stream.
 
+    Warm-up: at least `warmup` calls and at least `warmup_s` seconds of them
+    (at most 400 calls), so short calls are timed at the GPU's steady clock.
     flush (optional) runs before each call, outside the events. Returns
     {"median": ..., "min": ..., "mean": ..., "n": steps}.
     """
     import torch
-    for _ in range(warmup):
+    t0 = time.perf_counter()
+    n = 0
+    while n < warmup or (time.perf_counter() - t0 < warmup_s and n < 400):
         if flush is not None:
             flush()
         fn()
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     st = torch.cuda.current_stream()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
