@@ -96,14 +96,14 @@ def test_zero_queries_give_mean_of_values():
 
 
 def test_causal_first_row_is_first_value():
-    """Causal row 0 sees key 0 only: O_0 = V_0 and LSE_0 = scale * q_0 . k_0.
+    """Causal row 0 sees key 0 only: O_0 = V_0 exactly and LSE_0 = scale * q_0 . k_0.
 
-    The kernels hold an integral running maximum, so the one probability is
-    p = 2^(s*c - ceil(s*c)) in (1/2, 1]; it enters P V rounded to bf16 and the row
-    sum in fp32, which puts O_0 within one bf16 step of V_0 (relative error of the
-    rounding <= 2^-9, half a bf16 step at most).
+    The one probability p enters P V rounded to bf16, and the output is
+    normalised by the sum of the bf16 probabilities the products applied, so
+    O_0 = bf16(p) V_0 / bf16(p): V_0 up to the fp32 reciprocal, which the bf16
+    rounding of the output removes (bit for bit). With two splits the split
+    without visible keys carries weight 0 in the merge.
     """
-    from _parity import bf16_steps
     B, Sq, Sk, Hq, Hk, d = 2, 96, 96, 8, 2, 128
     q, k, v = _qkv(31, B, Sq, Sk, Hq, Hk, d)
     scale = gi.fp32(1 / math.sqrt(d))
@@ -111,7 +111,7 @@ def test_causal_first_row_is_first_value():
         O, L = gpu_run(q, k, v, True, scale, pack, ns)
         G = Hq // Hk
         for h in range(Hq):
-            assert int(bf16_steps(O[:, 0, h, :].cpu().contiguous(), v[:, 0, h // G, :].contiguous()).max()) <= 1, h
+            assert torch.equal(O[:, 0, h, :].cpu(), v[:, 0, h // G, :]), (pack, ns, h)
             s0 = scale * (f64(q[:, 0, h, :]) * f64(k[:, 0, h // G, :])).sum(-1)
             assert np.allclose(f64(L[:, h, 0]), s0, atol=2e-5)
 
