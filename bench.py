@@ -149,6 +149,17 @@ def extra_decode(g, gi, dev, steps):
         dec[name] = rate_entry(t, nbytes=wd.io_bytes,
                                kernel="attn_decode_kernel" + (" + combine_kernel" if pl["num_splits"] > 1 else ""))
         log(f"decode pack={pack} ns={ns}: median {t['median'] * 1e3:.1f} us")
+    # the split calls through the entry point that allocates nothing: the
+    # partials live in the library's fixed device array, so a call enqueues
+    # no stream-ordered allocation and release (each of which leaves the GPU
+    # idle for a few microseconds between calls)
+    od = torch.empty_like(qd)
+    ld = torch.empty((wd.B, wd.Hq, wd.Sq), dtype=torch.float32, device=dev)
+    for ns in (4, 8):
+        t = time_calls(lambda: g.gqa_attn_fwd_noalloc(qd, kd, vd, od, ld, wd.causal, wd.scale, 1, ns), steps, 5)
+        dec[f"pack1_ns{ns}_noalloc"] = rate_entry(t, nbytes=wd.io_bytes,
+                                                  kernel="attn_decode_kernel + combine_kernel (gqa_attn_fwd_noalloc)")
+        log(f"decode pack=1 ns={ns} no-allocation entry point: median {t['median'] * 1e3:.1f} us")
     del kd, vd
     out = {"decode_b64_sk8192": dec}
     # the same decode over a paged cache: pages of 256 keys in random pool order
