@@ -32,11 +32,12 @@
  * All tensor pointers are device pointers on the current HIP device and must
  * be 16-byte aligned. d must be 64 or 128.
  *
- * Ownership: the caller owns every tensor. The library allocates only the
- * split-KV workspace (fp32 partial outputs and log-sums), stream-ordered on
- * the caller's stream (hipMallocFromPoolAsync/hipFreeAsync) from a memory
- * pool the library creates per device, so calls on different streams never
- * share it. That pool keeps up to 256 MiB of freed workspace reserved for
+ * Ownership: the caller owns every tensor. The library allocates only
+ * transient workspaces (the split-KV fp32 partial outputs and log-sums, the
+ * work list of variable-length prefill, the backward's D and base-2
+ * log-sum-exp), stream-ordered on the caller's stream
+ * (hipMallocFromPoolAsync/hipFreeAsync) from a memory pool the library
+ * creates per device, so calls on different streams never share them. That pool keeps up to 256 MiB of freed workspace reserved for
  * later calls and returns anything above that to the device at the next
  * synchronisation; the device's default pool is not modified. Other state:
  * a per-device cache of the compute-unit count (and, for
