@@ -193,3 +193,42 @@ def test_varlen_llama_mix_8_wavefront_kernel_full():
     for causal in (True, False):
         O, L = run_varlen(q, k, v, cq, ck, causal, scale)
         check(O, L, q, k, v, cq, ck, causal, scale, tag=f"causal={causal}")
+
+
+@pytest.mark.parametrize("shape", ["small", "8-wavefront"])
+def test_varlen_malformed_offsets_stay_in_bounds(shape):
+    """Offsets that decrease, overlap, start below 0 or run past total_q/total_k: the kernels
+    clamp every sequence into [0, total_q) x [0, total_k), so the call succeeds and nothing
+    outside out and lse is written (guard rows around them keep their NaNs). Results for such
+    offsets are unspecified; each path (plain grid, work list, splits) must stay in bounds."""
+    import grouped_query_exact_amd as g
+    if shape == "small":
+        Hq, Hk, d, total_q, total_k, max_sq, max_sk = 8, 2, 128, 300, 400, 128, 400
+        cqs = [[0, 100, 50, 300], [-20, 250, 1000, 1000], [0, 300, 300, 300]]
+        cks = [[0, 150, 100, 400], [-5, 200, 5000, 7], [0, 0, 400, 10]]
+    else:  # enough 256-row items for the 8-wavefront kernel with a work list
+        Hq, Hk, d, total_q, total_k, max_sq, max_sk = 32, 8, 128, 8192, 8192, 512, 1024
+        B = 64
+        base = np.linspace(0, total_q, B + 1).astype(int)
+        bad_q = base.copy(); bad_q[10] = base[30]; bad_q[40] = -100; bad_q[B] = total_q + 900
+        bad_k = base.copy(); bad_k[5] = base[9]; bad_k[20] = total_k + 50
+        cqs, cks = [bad_q.tolist()], [bad_k.tolist()]
+    q = gi.random_bf16(9950, (total_q, Hq, d)).to(DEV)
+    k = gi.random_bf16(9951, (total_k, Hk, d)).to(DEV)
+    v = gi.random_bf16(9952, (total_k, Hk, d)).to(DEV)
+    scale = gi.fp32(1 / math.sqrt(d))
+    pad = 48
+    for cq, ck in zip(cqs, cks):
+        cq_t = torch.tensor(cq, dtype=torch.int32, device=DEV)
+        ck_t = torch.tensor(ck, dtype=torch.int32, device=DEV)
+        for causal in (False, True):
+            for pack, ns in ((1, 1), (0, 1), (1, 3), (-1, 0)):
+                big_o = torch.full((total_q + 2 * pad, Hq, d), float("nan"), dtype=torch.bfloat16, device=DEV)
+                big_l = torch.full((Hq * total_q + 2 * pad,), float("nan"), dtype=torch.float32, device=DEV)
+                out = big_o[pad:pad + total_q]
+                lse = big_l[pad:pad + Hq * total_q].view(Hq, total_q)
+                g.gqa_attn_fwd_varlen(q, k, v, out, lse, cq_t, ck_t, max_sq, max_sk, causal, scale, pack, ns)
+                torch.cuda.synchronize()
+                tag = f"{shape} cq={cq[:4]} causal={causal} pack={pack} ns={ns}"
+                assert torch.isnan(big_o[:pad].float()).all() and torch.isnan(big_o[pad + total_q:].float()).all(), tag
+                assert torch.isnan(big_l[:pad]).all() and torch.isnan(big_l[pad + Hq * total_q:]).all(), tag
