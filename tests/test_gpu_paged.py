@@ -218,3 +218,45 @@ def test_paged_decode_many_split_workgroups():
             g.gqa_attn_fwd(q[b:b + 1], kb[None].to(DEV), vb[None].to(DEV), ob, lb, causal, scale, 1, 20)
             torch.cuda.synchronize()
             assert torch.equal(out[b:b + 1], ob) and torch.equal(lse[b:b + 1], lb), f"b={b} causal={causal}"
+
+
+@pytest.mark.parametrize("Sq", [1, 40])
+def test_paged_malformed_tables_stay_in_the_pool(Sq):
+    """Block-table entries below 0 or past the pool and key lengths below 0 or past the table's
+    capacity: the kernels clamp pages into [0, num_pages) and lengths into [0, capacity], so every
+    read stays in the pool. The pool sits between NaN guard pages and holds only finite values, so
+    a read outside it would show up as a non-finite output. Decode (Sq=1) and chunked prefill (40
+    new tokens), bf16 and fp8 pools, causal and not, unsplit and split."""
+    import grouped_query_exact_amd as g
+    B, Hq, Hk, d, ps, max_pages, num_pages, gp = 6, 8, 2, 128, 32, 6, 10, 3
+    rs = np.random.default_rng(77)
+    table = torch.from_numpy(rs.integers(-4, num_pages + 4, (B, max_pages)).astype(np.int32)).to(DEV)
+    seqlens = torch.tensor([-7, 0, 5, 100, max_pages * ps, max_pages * ps + 500], dtype=torch.int32, device=DEV)
+    q = gi.random_bf16(9960, (B, Sq, Hq, d)).to(DEV)
+    scale = gi.fp32(1 / math.sqrt(d))
+    for fp8 in (False, True):
+        if fp8 and Sq > 1:
+            continue  # fp8 pools take decode-shaped calls only
+        dt = torch.uint8 if fp8 else torch.bfloat16
+        pools = []
+        for seed in (9961, 9962):
+            big = torch.full((num_pages + 2 * gp, ps, Hk, d), float("nan"), dtype=torch.float32, device=DEV)
+            big[gp:gp + num_pages] = gi.random_bf16(seed, (num_pages, ps, Hk, d)).float().to(DEV)
+            big = big.to(torch.float8_e4m3fn).view(torch.uint8) if fp8 else big.to(torch.bfloat16)
+            assert big.dtype == dt
+            pools.append(big[gp:gp + num_pages])
+        kc, vc = pools
+        for causal in (False, True):
+            for ns in (1, 3):
+                out = torch.empty_like(q)
+                lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=DEV)
+                if fp8:
+                    g.gqa_attn_fwd_paged_kv8(q, kc, vc, 1.0, 1.0, table, seqlens, out, lse, causal, scale, -1, ns)
+                else:
+                    g.gqa_attn_fwd_paged(q, kc, vc, table, seqlens, out, lse, causal, scale, -1, ns)
+                torch.cuda.synchronize()
+                tag = f"Sq={Sq} fp8={fp8} causal={causal} ns={ns}"
+                assert torch.isfinite(out.float()).all(), f"{tag}: a read left the pool"
+                assert not torch.isnan(lse).any(), tag
+                # the two sequences without keys (length <= 0) give O = 0
+                assert torch.all(out[:2].float() == 0), tag
