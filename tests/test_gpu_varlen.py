@@ -232,3 +232,30 @@ def test_varlen_malformed_offsets_stay_in_bounds(shape):
                 tag = f"{shape} cq={cq[:4]} causal={causal} pack={pack} ns={ns}"
                 assert torch.isnan(big_o[:pad].float()).all() and torch.isnan(big_o[pad + total_q:].float()).all(), tag
                 assert torch.isnan(big_l[:pad]).all() and torch.isnan(big_l[pad + Hq * total_q:]).all(), tag
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_varlen_work_list_equals_plain_grid_bitwise(d):
+    """The same sequences called with max_seqlen_q = the longest sequence (tokens fill over 3/4 of
+    the grid: the plain grid) and with a larger bound (the work list): the tiled kernel's per-row
+    arithmetic does not depend on the order it takes the items in, so outputs and LSE are equal
+    bit for bit, unsplit and split."""
+    import grouped_query_exact_amd as g
+    lens = [300, 280, 290, 120]
+    Hq, Hk = 6, 2
+    q, k, v, cq, ck = gi.varlen_batch(9990 + d, lens, lens, Hq, Hk, d)
+    scale = gi.fp32(1 / math.sqrt(d))
+    total = sum(lens)
+    for causal in (False, True):
+        for pack, ns in ((1, 1), (0, 1), (1, 3)):
+            res = []
+            for max_q in (max(lens), 2 * max(lens)):
+                out = torch.empty((total, Hq, d), dtype=torch.bfloat16, device=DEV)
+                lse = torch.empty((Hq, total), dtype=torch.float32, device=DEV)
+                g.gqa_attn_fwd_varlen(q.to(DEV), k.to(DEV), v.to(DEV), out, lse, cq.to(DEV), ck.to(DEV), max_q,
+                                      max(lens), causal, scale, pack, ns)
+                torch.cuda.synchronize()
+                res.append((out, lse))
+            tag = f"d={d} causal={causal} pack={pack} ns={ns}"
+            assert torch.equal(res[0][0], res[1][0]), f"{tag}: O"
+            assert torch.equal(res[0][1], res[1][1]), f"{tag}: LSE"
