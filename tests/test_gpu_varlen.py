@@ -259,3 +259,30 @@ def test_varlen_work_list_equals_plain_grid_bitwise(d):
             tag = f"d={d} causal={causal} pack={pack} ns={ns}"
             assert torch.equal(res[0][0], res[1][0]), f"{tag}: O"
             assert torch.equal(res[0][1], res[1][1]), f"{tag}: LSE"
+
+
+def test_varlen_8_wavefront_work_list_equals_batched_bitwise():
+    """Eight sequences of 2048 tokens (Llama-2 heads, causal and not): the batched call runs on the
+    8-wavefront kernel's plain grid; the same tokens as a variable-length call with max_seqlen_q =
+    4096 run on that kernel from the work list. Same per-row arithmetic: equal bit for bit."""
+    import grouped_query_exact_amd as g
+    B, S, Hq, Hk, d = 8, 2048, 32, 8, 128
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(9995)
+    q = torch.randn((B, S, Hq, d), generator=gen, device=DEV).to(torch.bfloat16)
+    k = torch.randn((B, S, Hk, d), generator=gen, device=DEV).to(torch.bfloat16)
+    v = torch.randn((B, S, Hk, d), generator=gen, device=DEV).to(torch.bfloat16)
+    cu = torch.arange(0, (B + 1) * S, S, dtype=torch.int32, device=DEV)
+    scale = gi.fp32(1 / math.sqrt(d))
+    assert g.gqa_attn_plan(B, S, S, Hq, Hk, d, True, -1, 0, 256)["threads"] == 512  # 8-wavefront kernel
+    for causal in (True, False):
+        ob = torch.empty_like(q)
+        lb = torch.empty((B, Hq, S), dtype=torch.float32, device=DEV)
+        g.gqa_attn_fwd(q, k, v, ob, lb, causal, scale)
+        ov = torch.empty((B * S, Hq, d), dtype=torch.bfloat16, device=DEV)
+        lv = torch.empty((Hq, B * S), dtype=torch.float32, device=DEV)
+        g.gqa_attn_fwd_varlen(q.view(B * S, Hq, d), k.view(B * S, Hk, d), v.view(B * S, Hk, d), ov, lv, cu, cu,
+                              2 * S, S, causal, scale)
+        torch.cuda.synchronize()
+        assert torch.equal(ov.view(B, S, Hq, d), ob), f"O causal={causal}"
+        assert torch.equal(lv, lb.permute(1, 0, 2).reshape(Hq, B * S)), f"LSE causal={causal}"
