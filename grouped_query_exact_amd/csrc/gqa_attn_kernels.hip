@@ -554,6 +554,7 @@ __global__ __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2
     constexpr int COPIES = 2 * NLOAD;
     static_assert(NS == 4, "the stage reuse and the wait counts below assume 4 stages");
     static_assert(kPPThreads == 512 && kPPBlockM == 256, "8 wavefronts of 32 rows");
+    static_assert(D == 128, "a 256-row Q tile fills two ring stages");
     __shared__ __attribute__((aligned(16))) uint16_t smem[NS * 2 * TILE];
     LDS char* lds = (LDS char*)smem;
 
@@ -563,16 +564,25 @@ __global__ __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2
     const int lane = tid & 63;
     const int col = lane & 31, half = lane >> 5;
 
-    // ---- work item: (batch, head unit, row tile descending), XCD-contiguous;
-    // variable-length calls: the scheduling kernel's work list, as in
-    // attn_fwd_kernel (the plan routes them here only with one)
-    int rt, unit, b;
-    if (!VARLEN) {
+    // ---- work: a pair of row tiles of one (batch, head unit), the heavy one
+    // (rt1, descending) first and its light partner rt2 = row_tiles-1-rt1 after
+    // it; variable-length calls: one item from the scheduling kernel's work list
+    int rt1, rt2 = -1, unit, b;
+    if (!VARLEN && !CAUSAL) {  // non-causal items all cost the same: one per workgroup
         const int logical = xcd_remap(blockIdx.x, p.grid);
-        rt = p.row_tiles - 1 - (logical % p.row_tiles);
+        rt1 = p.row_tiles - 1 - (logical % p.row_tiles);
         const int tmpu = logical / p.row_tiles;
         unit = tmpu % p.units_per_b;
         b = tmpu / p.units_per_b;
+    } else if (!VARLEN) {
+        const int npairs = (p.row_tiles + 1) >> 1;
+        const int logical = xcd_remap(blockIdx.x, p.grid);
+        const int pr = logical % npairs;
+        const int tmpu = logical / npairs;
+        unit = tmpu % p.units_per_b;
+        b = tmpu / p.units_per_b;
+        rt1 = p.row_tiles - 1 - pr;
+        if (pr < rt1) rt2 = pr;
     } else {
         typedef const __attribute__((address_space(4))) int* cint_p;
         const cint_p wl = (cint_p)p.worklist;
@@ -580,39 +590,19 @@ __global__ __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2
         unit = (int)blockIdx.x % p.units_per_b;
         if (pair >= wl[0]) return;  // uniform over the workgroup
         b = __builtin_amdgcn_readfirstlane(wl[1 + 2 * pair]);
-        rt = __builtin_amdgcn_readfirstlane(wl[2 + 2 * pair]);
+        rt1 = __builtin_amdgcn_readfirstlane(wl[2 + 2 * pair]);
     }
     const int g = p.Gp > 1 ? unit : unit / p.G;
     const int h0 = p.Gp > 1 ? unit * p.G : unit;
-    const int r0 = rt * kPPBlockM;
     int Sq = p.Sq, Sk = p.Sk;
     int64_t qtok0 = (int64_t)b * p.Sq, ktok0 = (int64_t)b * p.Sk;
     if (VARLEN) seq_extent(p, b, qtok0, Sq, ktok0, Sk);
     if (PAGED) Sk = __builtin_amdgcn_readfirstlane(min(max(p.seqlens_k[b], 0), p.max_pages * p.page_size));
     const int R = VARLEN ? Sq * p.Gp : p.R;
-
-    // ---- this lane's row: token ti, head hh
-    const int r = r0 + wave * 32 + col;
-    const bool row_valid = r < R;
-    const int rc = min(r, R - 1);
-    const int ti = (int)fdiv((uint32_t)rc, p.gmul, p.gshift);
-    const int hh = h0 + (rc - ti * p.Gp);
     const int koff = Sk - Sq;  // bottom-right causal offset
-
-    // ---- key tiles of the item and of this wavefront's rows
-    const int r_last = min(r0 + kPPBlockM, R) - 1;
-    const int i_max = (int)fdiv((uint32_t)r_last, p.gmul, p.gshift);
-    int kv_end = Sk;
-    if (CAUSAL) kv_end = min(Sk, i_max + koff + 1);
-    const int nt = kv_end > 0 ? (kv_end + kBlockN - 1) / kBlockN : 0;
-    const int rw0 = r0 + wave * 32;
-    const bool wave_active = rw0 < R;
-    const int iw_min = (int)fdiv((uint32_t)min(rw0, R - 1), p.gmul, p.gshift);
-    const int iw_max = (int)fdiv((uint32_t)(min(rw0 + 32, R) - 1), p.gmul, p.gshift);
 
     // ---- K/V tile copies: fixed per-thread 16-byte chunks, scalar tile base
     const int64_t kv_stride_b = (int64_t)p.Hk * D * 2;
-    // contiguous: this sequence's rows of head g; paged: head g of pool page 0
     const char* kbase = (const char*)(p.k + (PAGED ? (int64_t)g * D : (ktok0 * p.Hk + g) * D));
     const char* vbase = (const char*)(p.v + (PAGED ? (int64_t)g * D : (ktok0 * p.Hk + g) * D));
     uint32_t goff[NLOAD];
@@ -623,77 +613,6 @@ __global__ __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2
         const int logical_ch = (ci % NCH) ^ swz<D>(row);
         goff[u] = (uint32_t)(row * kv_stride_b + logical_ch * 16);
     }
-    // the LDS destination is uniform; it is passed through a scalar register
-    auto stage_dst = [&](int stage, int tensor, int u) __attribute__((always_inline)) {
-        const uint32_t a = (uint32_t)(size_t)(lds + (stage & (NS - 1)) * 2 * TILE_B + tensor * TILE_B) + (u * 8 + wave) * 1024;
-        return (LDS void*)(size_t)__builtin_amdgcn_readfirstlane(a);
-    };
-    auto issue = [&](int t) __attribute__((always_inline)) {
-        const int kv0 = t * kBlockN;
-        if (PAGED) {  // as in attn_fwd_kernel: each copy's 4 key rows lie in one page
-            const __attribute__((address_space(4))) int* table =
-                (const __attribute__((address_space(4))) int*)p.block_table;
-#pragma unroll
-            for (int u = 0; u < NLOAD; ++u) {
-                const int key_first = min(kv0 + (u * 8 + wave) * 64 / NCH, Sk - 1);
-                const int pidx = (int)fdiv((uint32_t)key_first, p.pmul, p.pshift);
-                const int page = __builtin_amdgcn_readfirstlane(
-                    min(max(table[(int64_t)b * p.max_pages + pidx], 0), p.num_pages - 1));
-                const int64_t page_off = (int64_t)page * p.page_size * kv_stride_b;
-                uint32_t off;
-                if (kv0 + kBlockN <= Sk) {  // full tile: the copy's rows start at or after the page's first key
-                    off = goff[u] - (uint32_t)((pidx * p.page_size - kv0) * kv_stride_b);
-                } else {
-                    const int ci = (u * 8 + wave) * 64 + lane;
-                    const int row = ci / NCH;
-                    const int logical_ch = (ci % NCH) ^ swz<D>(row);
-                    const int key = min(kv0 + row, Sk - 1) - pidx * p.page_size;
-                    off = (uint32_t)(key * kv_stride_b + logical_ch * 16);
-                }
-                lds_dma16(kbase + page_off, off, stage_dst(t, 0, u));
-                lds_dma16(vbase + page_off, off, stage_dst(t, 1, u));
-            }
-            return;
-        }
-        const char* kg = kbase + kv0 * kv_stride_b;
-        const char* vg = vbase + kv0 * kv_stride_b;
-        if (kv0 + kBlockN <= Sk) {
-#pragma unroll
-            for (int u = 0; u < NLOAD; ++u) {
-                lds_dma16(kg, goff[u], stage_dst(t, 0, u));
-                lds_dma16(vg, goff[u], stage_dst(t, 1, u));
-            }
-        } else {  // ragged last tile: rows past the end re-read the last key (masked later)
-#pragma unroll
-            for (int u = 0; u < NLOAD; ++u) {
-                const int ci = (u * 8 + wave) * 64 + lane;
-                const int row = ci / NCH;
-                const int logical_ch = (ci % NCH) ^ swz<D>(row);
-                const int key = min(kv0 + row, Sk - 1) - kv0;
-                const uint32_t off = (uint32_t)(key * kv_stride_b + logical_ch * 16);
-                lds_dma16(kg, off, stage_dst(t, 0, u));
-                lds_dma16(vg, off, stage_dst(t, 1, u));
-            }
-        }
-    };
-
-    // ---- prologue: tile 0, the Q rows (B operand of S^T = K Q^T), tile 1
-    if (nt > 0) issue(0);
-    bf16x8 qreg[D / 16];
-    {
-        const uint16_t* qrow = p.q + ((qtok0 + ti) * p.Hq + hh) * D;
-#pragma unroll
-        for (int dc = 0; dc < D / 16; ++dc) {
-            u32x4 w = *(const u32x4*)(qrow + dc * 16 + half * 8);
-            w = (w & p.qand) ^ p.qsign;
-            qreg[dc] = __builtin_bit_cast(bf16x8, w);
-        }
-    }
-    // wait for Q here, before the tile loop, so that no wait on it lands inside
-#pragma unroll
-    for (int dc = 0; dc < D / 16; ++dc) asm volatile("" ::"v"(qreg[dc]));
-    if (nt > 1) issue(1);
-
     // ---- per-lane LDS operand offsets (as in attn_fwd_kernel)
     const int krow0 = pi32(col);
     uint32_t kofs[D / 16];
@@ -710,166 +629,321 @@ __global__ __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2
             const int vcol = cb * 32 + qq * 16 + rho * 4;
             vofs[cb][rr] = vrow * (D * 2) + (((vcol >> 3) ^ swz<D>(vrow)) * 16) + (vcol & 7) * 2;
         }
-
-    f32x16 oacc[D / 32];
-#pragma unroll
-    for (int cb = 0; cb < D / 32; ++cb) oacc[cb] = f32x16{};
-    float m_run = -__builtin_inff();  // running max, scaled log2 units
-    float l_part[4] = {0.f, 0.f, 0.f, 0.f};  // fp32 P: the LSE
-    float w_part[4] = {0.f, 0.f, 0.f, 0.f};  // bf16 P: the output's normaliser
     const float c = p.c;
-    const int jlim = CAUSAL ? min(Sk - 1, ti + koff) : Sk - 1;  // last key visible to this row
-    f32x16 sacc[2];  // S(t): from the product phase to the softmax phase
-    bf16x8 pk[4];    // P(t): from the softmax phase to the next product phase
 
-    // waves whose rows see none of tile t's keys skip its arithmetic (monotone in t)
-    auto act = [&](int t) __attribute__((always_inline)) {
-        return wave_active && !(CAUSAL && t * kBlockN > iw_max + koff);
-    };
-    auto s_part = [&](int t) __attribute__((always_inline)) {
-        const LDS char* kt = lds + (t & (NS - 1)) * 2 * TILE_B;
+    // The light item's Q rows reach LDS by copy during the heavy item's last
+    // two tiles, into the two ring stages those tiles leave unused (rows
+    // 0-127 and 128-255 of the tile, 16-byte chunk ch of row r at slot
+    // 16r + (ch ^ (r & 15)) of its stage), and its tile 0 during the heavy
+    // item's drain step. Its ring starts two stages after the heavy item's.
+    int ring = 0;          // stage of the item's tile 0
+    bool q_staged = false; // the item's Q rows and tile 0 were copied by the previous item
+    // the two items run as two inlined copies of one body (no loop back edge,
+    // so nothing of the first item stays live into the second)
+    auto do_item = [&](auto item_c) __attribute__((always_inline)) {
+        constexpr int item = decltype(item_c)::value;
+        const int rt = item == 0 ? rt1 : rt2;
+        const int r0 = rt * kPPBlockM;
+        // ---- this lane's row: token ti, head hh
+        const int r = r0 + wave * 32 + col;
+        const bool row_valid = r < R;
+        const int rc = min(r, R - 1);
+        const int ti = (int)fdiv((uint32_t)rc, p.gmul, p.gshift);
+        const int hh = h0 + (rc - ti * p.Gp);
+        // ---- key tiles of the item and of this wavefront's rows
+        const int r_last = min(r0 + kPPBlockM, R) - 1;
+        const int i_max = (int)fdiv((uint32_t)r_last, p.gmul, p.gshift);
+        int kv_end = Sk;
+        if (CAUSAL) kv_end = min(Sk, i_max + koff + 1);
+        const int nt = kv_end > 0 ? (kv_end + kBlockN - 1) / kBlockN : 0;
+        const int rw0 = r0 + wave * 32;
+        const bool wave_active = rw0 < R;
+        const int iw_min = (int)fdiv((uint32_t)min(rw0, R - 1), p.gmul, p.gshift);
+        const int iw_max = (int)fdiv((uint32_t)(min(rw0 + 32, R) - 1), p.gmul, p.gshift);
+        // the next item (if any) is staged through LDS when this one has at least two tiles
+        const bool stage_next = item == 0 && rt2 >= 0 && nt >= 2;
+
+        // the LDS destination is uniform; it is passed through a scalar register
+        auto stage_dst = [&](int t, int tensor, int u) __attribute__((always_inline)) {
+            const uint32_t a = (uint32_t)(size_t)(lds + ((ring + t) & (NS - 1)) * 2 * TILE_B + tensor * TILE_B) + (u * 8 + wave) * 1024;
+            return (LDS void*)(size_t)__builtin_amdgcn_readfirstlane(a);
+        };
+        // tile t of the item (t may run past nt-1 only through issue_next below)
+        auto issue_kv = [&](int t, int ring_of_t) __attribute__((always_inline)) {
+            const int kv0 = t * kBlockN;
+            auto dst = [&](int tensor, int u) __attribute__((always_inline)) {
+                const uint32_t a = (uint32_t)(size_t)(lds + ((ring_of_t + t) & (NS - 1)) * 2 * TILE_B + tensor * TILE_B) + (u * 8 + wave) * 1024;
+                return (LDS void*)(size_t)__builtin_amdgcn_readfirstlane(a);
+            };
+            if (PAGED) {
+                const __attribute__((address_space(4))) int* table =
+                    (const __attribute__((address_space(4))) int*)p.block_table;
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) sacc[mb] = f32x16{};
-#pragma unroll
-        for (int dc = 0; dc < D / 16; ++dc)
-#pragma unroll
-            for (int mb = 0; mb < 2; ++mb) {
-                const bf16x8 a = *(const LDS bf16x8*)(kt + kofs[dc] + mb * 32 * D * 2);
-                sacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[dc], sacc[mb], 0, 0, 0);
+                for (int u = 0; u < NLOAD; ++u) {
+                    const int key_first = min(kv0 + (u * 8 + wave) * 64 / NCH, Sk - 1);
+                    const int pidx = (int)fdiv((uint32_t)key_first, p.pmul, p.pshift);
+                    const int page = __builtin_amdgcn_readfirstlane(
+                        min(max(table[(int64_t)b * p.max_pages + pidx], 0), p.num_pages - 1));
+                    const int64_t page_off = (int64_t)page * p.page_size * kv_stride_b;
+                    uint32_t off;
+                    if (kv0 + kBlockN <= Sk) {
+                        off = goff[u] - (uint32_t)((pidx * p.page_size - kv0) * kv_stride_b);
+                    } else {
+                        const int ci = (u * 8 + wave) * 64 + lane;
+                        const int row = ci / NCH;
+                        const int logical_ch = (ci % NCH) ^ swz<D>(row);
+                        const int key = min(kv0 + row, Sk - 1) - pidx * p.page_size;
+                        off = (uint32_t)(key * kv_stride_b + logical_ch * 16);
+                    }
+                    lds_dma16(kbase + page_off, off, dst(0, u));
+                    lds_dma16(vbase + page_off, off, dst(1, u));
+                }
+                return;
             }
-        // the operand reads run eight ahead of the products
-        constexpr int NR = D / 8, PRE = 8;
-        __builtin_amdgcn_sched_group_barrier(0x100, PRE, 0);
+            const char* kg = kbase + kv0 * kv_stride_b;
+            const char* vg = vbase + kv0 * kv_stride_b;
+            if (kv0 + kBlockN <= Sk) {
 #pragma unroll
-        for (int i = 0; i < (NR - PRE) / 2; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                for (int u = 0; u < NLOAD; ++u) {
+                    lds_dma16(kg, goff[u], dst(0, u));
+                    lds_dma16(vg, goff[u], dst(1, u));
+                }
+            } else {
+#pragma unroll
+                for (int u = 0; u < NLOAD; ++u) {
+                    const int ci = (u * 8 + wave) * 64 + lane;
+                    const int row = ci / NCH;
+                    const int logical_ch = (ci % NCH) ^ swz<D>(row);
+                    const int key = min(kv0 + row, Sk - 1) - kv0;
+                    const uint32_t off = (uint32_t)(key * kv_stride_b + logical_ch * 16);
+                    lds_dma16(kg, off, dst(0, u));
+                    lds_dma16(vg, off, dst(1, u));
+                }
+            }
+        };
+        auto issue = [&](int t) __attribute__((always_inline)) { issue_kv(t, ring); };
+        // half `part` (rows 128*part ..) of the next item's Q tile into stage ring+nt+part
+        auto issue_next_q = [&](int part) __attribute__((always_inline)) {
+            const uint32_t sbase = (uint32_t)(size_t)(lds + ((ring + nt + part) & (NS - 1)) * 2 * TILE_B);
+            // offsets from the item's first token: at most 256 tokens of Hq rows
+            const int tok_first = (int)fdiv((uint32_t)min(rt2 * kPPBlockM, R - 1), p.gmul, p.gshift);
+            const char* qb = (const char*)(p.q + (qtok0 + tok_first) * p.Hq * D);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int slot = (u * 8 + wave) * 64 + lane;  // 16-byte slot of the stage
+                const int rl = slot >> 4;                      // row of the half
+                const int ch = (slot & 15) ^ (rl & 15);
+                const int rq = min(rt2 * kPPBlockM + part * 128 + rl, R - 1);
+                const int tq = (int)fdiv((uint32_t)rq, p.gmul, p.gshift);
+                const int hq = h0 + (rq - tq * p.Gp);
+                const uint32_t off = (uint32_t)((((tq - tok_first) * p.Hq + hq) * D * 2) + ch * 16);
+                lds_dma16(qb, off, (LDS void*)(size_t)__builtin_amdgcn_readfirstlane(sbase + (u * 8 + wave) * 1024));
+            }
+        };
+
+        // ---- prologue: the Q rows (B operand of S^T = K Q^T), tiles 0 and 1
+        bf16x8 qreg[D / 16];
+        if (!q_staged) {
+            if (item > 0) __syncthreads();  // every wavefront is done with the previous item's stages
+            if (nt > 0) issue(0);
+            const uint16_t* qrow = p.q + ((qtok0 + ti) * p.Hq + hh) * D;
+#pragma unroll
+            for (int dc = 0; dc < D / 16; ++dc) {
+                u32x4 w = *(const u32x4*)(qrow + dc * 16 + half * 8);
+                w = (w & p.qand) ^ p.qsign;
+                qreg[dc] = __builtin_bit_cast(bf16x8, w);
+            }
+            // wait for Q here, before the tile loop, so that no wait on it lands inside
+#pragma unroll
+            for (int dc = 0; dc < D / 16; ++dc) asm volatile("" ::"v"(qreg[dc]));
+            if (nt > 1) issue(1);
+        } else {
+            // this thread's Q copies landed before the previous item's stores;
+            // the barrier makes every thread's copies visible and frees the
+            // previous item's last stage
+            __syncthreads();
+            const int rl = wave * 32 + col, part = rl >> 7, rh = rl & 127;
+            const LDS char* qs = lds + ((ring - 2 + part) & (NS - 1)) * 2 * TILE_B + rh * 256;
+#pragma unroll
+            for (int dc = 0; dc < D / 16; ++dc) {
+                u32x4 w = *(const LDS u32x4*)(qs + (((2 * dc + half) ^ (rh & 15)) * 16));
+                w = (w & p.qand) ^ p.qsign;
+                qreg[dc] = __builtin_bit_cast(bf16x8, w);
+            }
+#pragma unroll
+            for (int dc = 0; dc < D / 16; ++dc) asm volatile("" ::"v"(qreg[dc]));
+            wait_vmem();  // tile 0 (and the previous item's stores)
+            if (nt > 1) issue(1);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, PRE, 0);
-    };
-    auto pv_part = [&](int t) __attribute__((always_inline)) {
-        const LDS char* vt = lds + (t & (NS - 1)) * 2 * TILE_B + TILE_B;
+
+        f32x16 oacc[D / 32];
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-            for (int cb = 0; cb < D / 32; ++cb) {
-                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS s16x4*)(vt + vofs[cb][0] + kk * 16 * D * 2));
-                const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS s16x4*)(vt + vofs[cb][1] + kk * 16 * D * 2));
-                const s16x8 av = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-                oacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), pk[kk], oacc[cb], 0, 0, 0);
+        for (int cb = 0; cb < D / 32; ++cb) oacc[cb] = f32x16{};
+        float m_run = -__builtin_inff();  // running max, scaled log2 units
+        float l_part[4] = {0.f, 0.f, 0.f, 0.f};  // fp32 P: the LSE
+        float w_part[4] = {0.f, 0.f, 0.f, 0.f};  // bf16 P: the output's normaliser
+        const int jlim = CAUSAL ? min(Sk - 1, ti + koff) : Sk - 1;  // last key visible to this row
+        f32x16 sacc[2];
+        bf16x8 pk[4];
+        // waves whose rows see none of tile t's keys skip its arithmetic (monotone in t)
+        auto act = [&](int t) __attribute__((always_inline)) {
+            return wave_active && !(CAUSAL && t * kBlockN > iw_max + koff);
+        };
+        auto s_part = [&](int t) __attribute__((always_inline)) {
+            const LDS char* kt = lds + ((ring + t) & (NS - 1)) * 2 * TILE_B;
+    #pragma unroll
+            for (int mb = 0; mb < 2; ++mb) sacc[mb] = f32x16{};
+    #pragma unroll
+            for (int dc = 0; dc < D / 16; ++dc)
+    #pragma unroll
+                for (int mb = 0; mb < 2; ++mb) {
+                    const bf16x8 a = *(const LDS bf16x8*)(kt + kofs[dc] + mb * 32 * D * 2);
+                    sacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[dc], sacc[mb], 0, 0, 0);
+                }
+            // the operand reads run eight ahead of the products
+            constexpr int NR = D / 8, PRE = 8;
+            __builtin_amdgcn_sched_group_barrier(0x100, PRE, 0);
+    #pragma unroll
+            for (int i = 0; i < (NR - PRE) / 2; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
             }
-    };
-    auto softmax = [&](int t) __attribute__((always_inline)) {
-        const int kv0 = t * kBlockN;
-        const bool need_mask = (kv0 + kBlockN > Sk) || (CAUSAL && kv0 + kBlockN - 1 > iw_min + koff);
-        // keys of this lane's slots: kv0 + 32*mb + 16*(i/8) + 8*half + (i%8)
-        if (need_mask) {
-            const int lim = jlim - kv0 - half * 8;
-#pragma unroll
+            __builtin_amdgcn_sched_group_barrier(0x008, PRE, 0);
+        };
+        auto pv_part = [&](int t) __attribute__((always_inline)) {
+            const LDS char* vt = lds + ((ring + t) & (NS - 1)) * 2 * TILE_B + TILE_B;
+    #pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+    #pragma unroll
+                for (int cb = 0; cb < D / 32; ++cb) {
+                    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS s16x4*)(vt + vofs[cb][0] + kk * 16 * D * 2));
+                    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS s16x4*)(vt + vofs[cb][1] + kk * 16 * D * 2));
+                    const s16x8 av = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                    oacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), pk[kk], oacc[cb], 0, 0, 0);
+                }
+        };
+        auto softmax = [&](int t) __attribute__((always_inline)) {
+            const int kv0 = t * kBlockN;
+            const bool need_mask = (kv0 + kBlockN > Sk) || (CAUSAL && kv0 + kBlockN - 1 > iw_min + koff);
+            // keys of this lane's slots: kv0 + 32*mb + 16*(i/8) + 8*half + (i%8)
+            if (need_mask) {
+                const int lim = jlim - kv0 - half * 8;
+    #pragma unroll
+                for (int mb = 0; mb < 2; ++mb)
+    #pragma unroll
+                    for (int i = 0; i < 16; ++i)
+                        if (mb * 32 + ((i >> 3) << 4) + (i & 7) > lim) sacc[mb][i] = -__builtin_inff();
+            }
+            float mx;
+            {
+                float t0 = fmaxf(fmaxf(sacc[0][0], sacc[0][1]), sacc[0][2]);
+                float t1 = fmaxf(fmaxf(sacc[0][3], sacc[0][4]), sacc[0][5]);
+                float t2 = fmaxf(fmaxf(sacc[0][6], sacc[0][7]), sacc[0][8]);
+                float t3 = fmaxf(fmaxf(sacc[0][9], sacc[0][10]), sacc[0][11]);
+                t0 = fmaxf(fmaxf(t0, sacc[0][12]), sacc[0][13]);
+                t1 = fmaxf(fmaxf(t1, sacc[0][14]), sacc[0][15]);
+                t2 = fmaxf(fmaxf(t2, sacc[1][0]), sacc[1][1]);
+                t3 = fmaxf(fmaxf(t3, sacc[1][2]), sacc[1][3]);
+                t0 = fmaxf(fmaxf(t0, sacc[1][4]), sacc[1][5]);
+                t1 = fmaxf(fmaxf(t1, sacc[1][6]), sacc[1][7]);
+                t2 = fmaxf(fmaxf(t2, sacc[1][8]), sacc[1][9]);
+                t3 = fmaxf(fmaxf(t3, sacc[1][10]), sacc[1][11]);
+                t0 = fmaxf(fmaxf(t0, sacc[1][12]), sacc[1][13]);
+                t1 = fmaxf(fmaxf(t1, sacc[1][14]), sacc[1][15]);
+                mx = xhalf_max(fmaxf(fmaxf(t0, t1), fmaxf(t2, t3)));
+            }
+            // lazy running-max update; O holds every product up to tile t-1 here
+            const float mxs = (mx == -__builtin_inff()) ? -__builtin_inff() : mx * c;
+            const float alpha = raise_max(m_run, mxs);
+            if (__ballot(alpha != 1.f)) {
+    #pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    l_part[i] *= alpha;
+                    w_part[i] *= alpha;
+                }
+    #pragma unroll
+                for (int cb = 0; cb < D / 32; ++cb)
+    #pragma unroll
+                    for (int i = 0; i < 16; ++i) oacc[cb][i] *= alpha;
+            }
+            const float moff = (m_run == -__builtin_inff()) ? 0.f : m_run;
+    #pragma unroll
             for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-                for (int i = 0; i < 16; ++i)
-                    if (mb * 32 + ((i >> 3) << 4) + (i & 7) > lim) sacc[mb][i] = -__builtin_inff();
-        }
-        float mx;
-        {
-            float t0 = fmaxf(fmaxf(sacc[0][0], sacc[0][1]), sacc[0][2]);
-            float t1 = fmaxf(fmaxf(sacc[0][3], sacc[0][4]), sacc[0][5]);
-            float t2 = fmaxf(fmaxf(sacc[0][6], sacc[0][7]), sacc[0][8]);
-            float t3 = fmaxf(fmaxf(sacc[0][9], sacc[0][10]), sacc[0][11]);
-            t0 = fmaxf(fmaxf(t0, sacc[0][12]), sacc[0][13]);
-            t1 = fmaxf(fmaxf(t1, sacc[0][14]), sacc[0][15]);
-            t2 = fmaxf(fmaxf(t2, sacc[1][0]), sacc[1][1]);
-            t3 = fmaxf(fmaxf(t3, sacc[1][2]), sacc[1][3]);
-            t0 = fmaxf(fmaxf(t0, sacc[1][4]), sacc[1][5]);
-            t1 = fmaxf(fmaxf(t1, sacc[1][6]), sacc[1][7]);
-            t2 = fmaxf(fmaxf(t2, sacc[1][8]), sacc[1][9]);
-            t3 = fmaxf(fmaxf(t3, sacc[1][10]), sacc[1][11]);
-            t0 = fmaxf(fmaxf(t0, sacc[1][12]), sacc[1][13]);
-            t1 = fmaxf(fmaxf(t1, sacc[1][14]), sacc[1][15]);
-            mx = xhalf_max(fmaxf(fmaxf(t0, t1), fmaxf(t2, t3)));
-        }
-        // lazy running-max update; O holds every product up to tile t-1 here
-        const float mxs = (mx == -__builtin_inff()) ? -__builtin_inff() : mx * c;
-        const float alpha = raise_max(m_run, mxs);
-        if (__ballot(alpha != 1.f)) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                l_part[i] *= alpha;
-                w_part[i] *= alpha;
+    #pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mb][i], c, -moff));
+                    l_part[i & 3] += x;
+                    pk[mb * 2 + (i >> 3)][i & 7] = (__bf16)x;
+                }
+    #pragma unroll
+            for (int r = 0; r < 4; ++r) add_bf16x8(pk[r], w_part);
+        };
+        auto product_phase = [&](int t) __attribute__((always_inline)) {
+            __builtin_amdgcn_s_setprio(1);
+            if (t < nt && act(t)) s_part(t);
+            if (t > 0 && act(t - 1)) pv_part(t - 1);
+            __builtin_amdgcn_s_setprio(0);
+        };
+        // softmax phase of tile t (any t in [-1, nt]); the copies of tile t+2 go first
+        auto softmax_phase = [&](int t_copy, int t_soft) __attribute__((always_inline)) {
+            if (t_copy + NS - 2 < nt) issue(t_copy + NS - 2);
+            else if (stage_next && t_copy + NS - 2 < nt + 2) issue_next_q(t_copy + NS - 2 - nt);
+            else if (stage_next && t_copy + NS - 2 == nt + 2) {
+                // the Q copies of this thread land first, then the next item's tile 0 goes out
+                wait_vmem();
+                issue_kv(0, ring + nt + 2);
             }
-#pragma unroll
-            for (int cb = 0; cb < D / 32; ++cb)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) oacc[cb][i] *= alpha;
-        }
-        const float moff = (m_run == -__builtin_inff()) ? 0.f : m_run;
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mb][i], c, -moff));
-                l_part[i & 3] += x;
-                pk[mb * 2 + (i >> 3)][i & 7] = (__bf16)x;
+            if (t_soft >= 0 && t_soft < nt && act(t_soft)) softmax(t_soft);
+        };
+        // top of tile t: this thread's copies of tile t have landed (at most tile
+        // t+1's copies are still in flight), then the barrier publishes the tile
+        // and frees the stage of tile t-2
+        auto top = [&](int t) __attribute__((always_inline)) {
+            if (t < nt) {
+                if (t + 1 < nt) wait_vmem_n<COPIES>();
+                else wait_vmem();
             }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) add_bf16x8(pk[r], w_part);
-    };
-    auto product_phase = [&](int t) __attribute__((always_inline)) {
-        __builtin_amdgcn_s_setprio(1);
-        if (t < nt && act(t)) s_part(t);
-        if (t > 0 && act(t - 1)) pv_part(t - 1);
-        __builtin_amdgcn_s_setprio(0);
-    };
-    // softmax phase of tile t (any t in [-1, nt]); the copies of tile t+2 go first
-    auto softmax_phase = [&](int t_copy, int t_soft) __attribute__((always_inline)) {
-        if (t_copy + NS - 2 < nt) issue(t_copy + NS - 2);
-        if (t_soft >= 0 && t_soft < nt && act(t_soft)) softmax(t_soft);
-    };
-    // top of tile t: this thread's copies of tile t have landed (at most tile
-    // t+1's copies are still in flight), then the barrier publishes the tile
-    // and frees the stage of tile t-2
-    auto top = [&](int t) __attribute__((always_inline)) {
-        if (t < nt) {
-            if (t + 1 < nt) wait_vmem_n<COPIES>();
-            else wait_vmem();
-        }
-        __syncthreads();
-    };
-    // the two groups run separate copies of the loop, so the compiler never
-    // merges two versions of the accumulators at a branch join
-    auto run = [&](auto is_b) __attribute__((always_inline)) {
-        for (int t = 0; t <= nt; ++t) {
-            top(t);
-            if (!decltype(is_b)::value) product_phase(t);
-            else softmax_phase(t, t - 1);
-            if (!CAUSAL) __syncthreads();
-            if (!decltype(is_b)::value) softmax_phase(t, t);
-            else product_phase(t);
-        }
-    };
-    if (grp == 0) run(std::false_type{});
-    else run(std::true_type{});
+            __syncthreads();
+        };
+        // the two groups run separate copies of the loop, so the compiler never
+        // merges two versions of the accumulators at a branch join
+        auto run = [&](auto is_b) __attribute__((always_inline)) {
+            for (int t = 0; t <= nt; ++t) {
+                top(t);
+                if (!decltype(is_b)::value) product_phase(t);
+                else softmax_phase(t, t - 1);
+                if (!CAUSAL) __syncthreads();
+                if (!decltype(is_b)::value) softmax_phase(t, t);
+                else product_phase(t);
+            }
+        };
+        if (grp == 0) run(std::false_type{});
+        else run(std::true_type{});
 
-    // ---- epilogue
-    const float l_tot = xhalf_sum((l_part[0] + l_part[1]) + (l_part[2] + l_part[3]));
-    const float w_tot = xhalf_sum((w_part[0] + w_part[1]) + (w_part[2] + w_part[3]));
-    const bool live = l_tot > 0.f;
-    const float inv = live ? 1.f / w_tot : 0.f;
-    const float lse_val = live ? (m_run + __log2f(l_tot)) * kLn2 : -__builtin_inff();
-    if (row_valid) {
-        uint16_t* orow = p.o + ((qtok0 + ti) * p.Hq + hh) * D;
-#pragma unroll
-        for (int cb = 0; cb < D / 32; ++cb)
-#pragma unroll
-            for (int run2 = 0; run2 < 2; ++run2) {
-                bf16x8 ov;
-#pragma unroll
-                for (int i = 0; i < 8; ++i) ov[i] = (__bf16)(oacc[cb][run2 * 8 + i] * inv);
-                *(bf16x8*)(orow + cb * 32 + run2 * 16 + half * 8) = ov;
-            }
-        if (half == 0 && p.lse) p.lse[lse_index(p, b, hh, qtok0, ti, VARLEN)] = lse_val;
-    }
+        // ---- epilogue
+        const float l_tot = xhalf_sum((l_part[0] + l_part[1]) + (l_part[2] + l_part[3]));
+        const float w_tot = xhalf_sum((w_part[0] + w_part[1]) + (w_part[2] + w_part[3]));
+        const bool live = l_tot > 0.f;
+        const float inv = live ? 1.f / w_tot : 0.f;
+        const float lse_val = live ? (m_run + __log2f(l_tot)) * kLn2 : -__builtin_inff();
+        if (row_valid) {
+            uint16_t* orow = p.o + ((qtok0 + ti) * p.Hq + hh) * D;
+    #pragma unroll
+            for (int cb = 0; cb < D / 32; ++cb)
+    #pragma unroll
+                for (int run2 = 0; run2 < 2; ++run2) {
+                    bf16x8 ov;
+    #pragma unroll
+                    for (int i = 0; i < 8; ++i) ov[i] = (__bf16)(oacc[cb][run2 * 8 + i] * inv);
+                    *(bf16x8*)(orow + cb * 32 + run2 * 16 + half * 8) = ov;
+                }
+            if (half == 0 && p.lse) p.lse[lse_index(p, b, hh, qtok0, ti, VARLEN)] = lse_val;
+        }
+        ring += nt + 2;
+        q_staged = stage_next;
+    };
+    do_item(std::integral_constant<int, 0>{});
+    if (CAUSAL && !VARLEN && rt2 >= 0) do_item(std::integral_constant<int, 1>{});
 }
 
 // Decode-shaped work (the pages' decode regime: one or a few new tokens per

@@ -154,6 +154,10 @@ int make_plan(const Shape& s, int pack_gqa, int num_splits, int num_cus, Plan* p
     }
     p->threads = p->decode ? kDecThreads : (p->pingpong ? kPPThreads : kThreads);
     p->grid = (long long)s.B * p->units_per_b * p->row_tiles * ns;
+    // causal launches of the 8-wavefront kernel pair each row tile with its
+    // mirror (row_tiles-1-rt) in one workgroup: equal key tiles per workgroup,
+    // and the light item's Q rows arrive while the heavy one finishes
+    if (p->pingpong && s.causal && !s.varlen) p->grid = (long long)s.B * p->units_per_b * ((p->row_tiles + 1) / 2);
     if (p->grid > INT_MAX) return GQA_ERR_INVALID_ARG;
     const long long rows = (long long)s.B * s.Sq * s.Hq;
     if (ns > 1) {

@@ -28,6 +28,10 @@ SHAPES = [
     (64, 300, 300, 6, 2, 128, 1),  # G = 3
     (32, 512, 448, 8, 2, 128, 0),  # unpacked: 2 row tiles per head
     (64, 300, 100, 8, 2, 128, 1),  # causal: tokens 0..199 see no key (bottom-right alignment)
+    # causal launches pair row tile rt with row_tiles-1-rt in one workgroup:
+    (16, 1800, 1800, 8, 2, 128, 1),  # 29 row tiles: the middle one runs alone; long heavy items
+    (64, 2048, 40, 8, 2, 128, 1),   # every item has at most one key tile: the light items load their own Q
+    (64, 2048, 150, 8, 2, 128, 1),  # heavy items of 2-3 key tiles: the light items' Q staged through LDS
 ]
 
 

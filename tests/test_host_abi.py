@@ -297,9 +297,13 @@ def test_plan_grid_and_workspace():
     assert p["pack_gqa"] == 1 and p["num_splits"] == 1 and p["workspace_bytes"] == 0
     assert p["block_n"] == 64
     assert p["row_tiles"] * p["block_m"] >= 2048 * 4
-    assert p["grid"] == 128 * 8 * p["row_tiles"]
-    # large unsplit bf16 calls: 8 wavefronts, 256-row tiles, one workgroup per compute unit
-    assert (p["block_m"], p["threads"], p["row_tiles"], p["grid"]) == (256, 512, 32, 32768)
+    # large unsplit bf16 calls: 8 wavefronts, 256-row tiles, one workgroup per compute unit; causal
+    # launches pair each row tile with its mirror, so the grid holds half the row tiles
+    assert (p["block_m"], p["threads"], p["row_tiles"], p["grid"]) == (256, 512, 32, 128 * 8 * 16)
+    p = g.gqa_attn_plan(128, 2048, 2048, 32, 8, 128, False, 1, 1, 256)
+    assert (p["block_m"], p["threads"], p["row_tiles"], p["grid"]) == (256, 512, 32, 128 * 8 * 32)
+    p = g.gqa_attn_plan(64, 1800, 1800, 32, 8, 128, True, 1, 1, 256)  # odd row tiles: the middle one alone
+    assert (p["threads"], p["row_tiles"], p["grid"]) == (512, 29, 64 * 8 * 15)
     # ... only with at least two such items per compute unit (212 * 2 = 424 < 512 here)
     p = g.gqa_attn_plan(212, 77, 77, 6, 2, 64, False, 1, 1, 256)
     assert (p["block_m"], p["threads"], p["grid"]) == (128, 256, 212 * 2 * 2)
@@ -382,7 +386,8 @@ int main() {
         if (p.pingpong != want8) { std::printf("bad 8-wave choice\n"); return 1; }
         if (p.block_m != (p.decode ? kDecBlockM : (p.pingpong ? kPPBlockM : kBlockM))) { std::printf("bad block_m\n"); return 1; }
         if (p.threads != (p.decode ? kDecThreads : (p.pingpong ? kPPThreads : kThreads))) { std::printf("bad threads\n"); return 1; }
-        if (p.grid != (long long)B * p.units_per_b * p.row_tiles * p.ns) { std::printf("bad grid\n"); return 1; }
+        const long long tiles_per_wg = (p.pingpong && causal) ? (p.row_tiles + 1) / 2 : p.row_tiles;  // mirrored pairs
+        if (p.grid != (long long)B * p.units_per_b * tiles_per_wg * p.ns) { std::printf("bad grid\n"); return 1; }
     }
     // fp8 K/V decode splits up to two workgroups per compute unit when each unit has at
     // least 256 key tiles and there are at least 32 head units, else up to four; at most
