@@ -248,8 +248,12 @@ int run(const Call& c) {
     if (plan.pingpong && c.varlen && !sched) return GQA_ERR_UNSUPPORTED;
     long long sched_cap = 0;
     size_t sched_bytes = 0;
+    // causal calls on the 8-wavefront kernel list pairs of row tiles: ceil(R_b / 2)
+    // entries per sequence, at most total_q * Gp / (2 * block_m) + B of them
+    const bool sched_pairs = sched && plan.pingpong && s.causal;
     if (sched) {
-        sched_cap = ((long long)c.total_q * plan.Gp + plan.block_m - 1) / plan.block_m + s.B;
+        const long long per = sched_pairs ? 2LL * plan.block_m : plan.block_m;
+        sched_cap = ((long long)c.total_q * plan.Gp + per - 1) / per + s.B;
         const long long grid = sched_cap * plan.units_per_b * plan.ns;
         if (sched_cap > INT_MAX / 4 || grid > INT_MAX) return GQA_ERR_INVALID_ARG;
         p.grid = (int)grid;
@@ -292,6 +296,7 @@ int run(const Call& c) {
         sp.gshift = fd.shift;
         sp.block_m = plan.block_m;
         sp.causal = s.causal;
+        sp.pair = sched_pairs ? 1 : 0;
         sp.cap = (int)sched_cap;
         p.worklist = (const int*)ws;
         e = gqa::launch_schedule(sp, c.stream);

@@ -566,7 +566,8 @@ __global__ __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2
 
     // ---- work: a pair of row tiles of one (batch, head unit), the heavy one
     // (rt1, descending) first and its light partner rt2 = row_tiles-1-rt1 after
-    // it; variable-length calls: one item from the scheduling kernel's work list
+    // it; variable-length calls: an entry of the scheduling kernel's work list
+    // (causal: the pair of row tiles R_b-1-pr and pr of sequence b)
     int rt1, rt2 = -1, unit, b;
     if (!VARLEN && !CAUSAL) {  // non-causal items all cost the same: one per workgroup
         const int logical = xcd_remap(blockIdx.x, p.grid);
@@ -590,7 +591,7 @@ __global__ __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2
         unit = (int)blockIdx.x % p.units_per_b;
         if (pair >= wl[0]) return;  // uniform over the workgroup
         b = __builtin_amdgcn_readfirstlane(wl[1 + 2 * pair]);
-        rt1 = __builtin_amdgcn_readfirstlane(wl[2 + 2 * pair]);
+        rt1 = __builtin_amdgcn_readfirstlane(wl[2 + 2 * pair]);  // causal: pr
     }
     const int g = p.Gp > 1 ? unit : unit / p.G;
     const int h0 = p.Gp > 1 ? unit * p.G : unit;
@@ -600,6 +601,11 @@ __global__ __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2
     if (PAGED) Sk = __builtin_amdgcn_readfirstlane(min(max(p.seqlens_k[b], 0), p.max_pages * p.page_size));
     const int R = VARLEN ? Sq * p.Gp : p.R;
     const int koff = Sk - Sq;  // bottom-right causal offset
+    if (VARLEN && CAUSAL) {
+        const int pr = rt1;
+        rt1 = (R + kPPBlockM - 1) / kPPBlockM - 1 - pr;
+        if (pr < rt1) rt2 = pr;
+    }
 
     // ---- K/V tile copies: fixed per-thread 16-byte chunks, scalar tile base
     const int64_t kv_stride_b = (int64_t)p.Hk * D * 2;
@@ -943,7 +949,7 @@ __global__ __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2
         q_staged = stage_next;
     };
     do_item(std::integral_constant<int, 0>{});
-    if (CAUSAL && !VARLEN && rt2 >= 0) do_item(std::integral_constant<int, 1>{});
+    if (CAUSAL && rt2 >= 0) do_item(std::integral_constant<int, 1>{});
 }
 
 // Decode-shaped work (the pages' decode regime: one or a few new tokens per

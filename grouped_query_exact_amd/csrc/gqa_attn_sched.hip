@@ -16,6 +16,11 @@
 // of the bins from the heaviest turns the counts into start slots; the second
 // pass takes a slot per pair and writes it. Pairs of equal cost land in any
 // order: the results do not depend on the order.
+//
+// Pair mode (causal calls on the 8-wavefront kernel): an entry (b, pr) stands
+// for row tiles R_b-1-pr and pr of sequence b, which one workgroup runs one
+// after the other (the middle tile of an odd count alone); its cost is the key
+// tiles of both, and sequence b has ceil(R_b / 2) entries.
 #include <hip/hip_runtime.h>
 
 #include "device_common.h"
@@ -67,15 +72,27 @@ __global__ __launch_bounds__(kSchedThreads) void varlen_schedule_kernel(const Sc
     __syncthreads();
 
     // the key tiles that row tile rt of a sequence reads (the attention
-    // kernels' count), as a bin
-    auto cost_bin = [&](int Sq, int Sk, int rt) {
+    // kernels' count)
+    auto tiles = [&](int Sq, int Sk, int rt) {
         int kv_end = Sk;
         if (sp.causal) {
             const int r_last = min((rt + 1) * sp.block_m, Sq * sp.Gp) - 1;
             const int i_max = (int)fdiv((uint32_t)r_last, sp.gmul, sp.gshift);
             kv_end = min(Sk, i_max + (Sk - Sq) + 1);
         }
-        const int T = kv_end > 0 ? (kv_end + kBlockN - 1) / kBlockN : 0;
+        return kv_end > 0 ? (kv_end + kBlockN - 1) / kBlockN : 0;
+    };
+    // the cost of entry e of a sequence (row tile e; pair mode: row tiles
+    // R-1-e and e), as a bin
+    auto cost_bin = [&](int Sq, int Sk, int e) {
+        int T;
+        if (sp.pair) {
+            const int R = (Sq * sp.Gp + sp.block_m - 1) / sp.block_m;
+            const int rt1 = R - 1 - e;
+            T = tiles(Sq, Sk, rt1) + (e < rt1 ? tiles(Sq, Sk, e) : 0);
+        } else {
+            T = tiles(Sq, Sk, e);
+        }
         return min(T, kSchedBins - 1);
     };
     // sequences c0 .. c0+1023 into seq_q, seq_k, seq_off; returns the chunk's pairs
@@ -91,6 +108,7 @@ __global__ __launch_bounds__(kSchedThreads) void varlen_schedule_kernel(const Sc
             Sq = min(q1 - q0, sp.max_sq);
             Sk = k1 - k0;
             nt = (Sq * sp.Gp + sp.block_m - 1) / sp.block_m;
+            if (sp.pair) nt = (nt + 1) >> 1;  // entries of the sequence
         }
         seq_q[tid] = Sq;
         seq_k[tid] = Sk;

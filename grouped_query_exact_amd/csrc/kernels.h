@@ -51,12 +51,13 @@ struct FwdParams {
 struct SchedParams {
     const int* cu_q;
     const int* cu_k;
-    int* worklist;           // [1 + 2 * cap]: count, then (b, rt) pairs
+    int* worklist;           // [1 + 2 * cap]: count, then (b, rt) entries (pair mode: (b, pr))
     int B, total_q, total_k, max_sq, Gp;
     uint32_t gmul, gshift;   // magic divisor of Gp
     int block_m;             // rows per tile of the attention kernel
     int causal;
-    int cap;                 // pairs the list can hold
+    int pair;                // 1: an entry is (b, pr), row tiles R_b-1-pr and pr of sequence b together
+    int cap;                 // entries the list can hold
 };
 hipError_t launch_schedule(const SchedParams& sp, hipStream_t stream);
 constexpr int kSchedThreads = 1024;

@@ -173,10 +173,12 @@ int gqa_attn_bwd(const void* q, const void* k, const void* v, const void* out, c
  * Calls with more than 32 query rows per head unit whose sequences hold
  * fewer than 3/4 of B * max_seqlen_q query tokens first run a small
  * scheduling kernel that lists, from the offsets, the (sequence, row tile)
- * work items that exist, heaviest first, into a stream-ordered workspace of
- * 4 * (1 + 2 * (ceil(total_q * G / M) + B)) bytes (G = Hq/Hk with PackGQA,
- * else 1; M = 128 rows per tile, 256 on the 8-wavefront kernel) taken from
- * the library's pool with the split workspace, if any.
+ * work items that exist, heaviest first (causal calls on the 8-wavefront
+ * kernel: pairs of a sequence's row tiles R-1-i and i, run by one workgroup),
+ * into a stream-ordered workspace of 4 * (1 + 2 * (ceil(total_q * G / M) + B))
+ * bytes (G = Hq/Hk with PackGQA, else 1; M = 128 rows per tile, 256 on the
+ * 8-wavefront kernel, 512 for its causal pairs) taken from the library's pool
+ * with the split workspace, if any.
  * Returns a gqa_status_t (B*max_seqlen_q == 0 or total_q == 0: no-op). */
 int gqa_attn_fwd_varlen(const void* q, const void* k, const void* v, void* out, float* lse,
                         const int* cu_seqlens_q, const int* cu_seqlens_k,
