@@ -195,6 +195,19 @@ def test_varlen_llama_mix_8_wavefront_kernel_full():
         check(O, L, q, k, v, cq, ck, causal, scale, tag=f"causal={causal}")
 
 
+def test_varlen_8_wavefront_pairs_unequal_key_counts():
+    """Causal calls on the 8-wavefront kernel take pairs of a sequence's row tiles (R-1-i and i)
+    from the work list. Sequences of 40 to 940 tokens (one to 15 row tiles, odd and even) with
+    300 cached keys before the chunk, half as many keys as queries (the first rows see no key)
+    or as many; every sequence against the oracle."""
+    lq = [40 + 60 * i for i in range(16)]
+    lk = [n + 300 if i % 3 == 0 else (n // 2 if i % 3 == 1 else n) for i, n in enumerate(lq)]
+    q, k, v, cq, ck = gi.varlen_batch(9905, lq, lk, 32, 8, 128)
+    scale = gi.fp32(1 / math.sqrt(128))
+    O, L = run_varlen(q, k, v, cq, ck, True, scale)
+    check(O, L, q, k, v, cq, ck, True, scale, tag="causal pairs, unequal key counts")
+
+
 @pytest.mark.parametrize("shape", ["small", "8-wavefront"])
 def test_varlen_malformed_offsets_stay_in_bounds(shape):
     """Offsets that decrease, overlap, start below 0 or run past total_q/total_k: the kernels
