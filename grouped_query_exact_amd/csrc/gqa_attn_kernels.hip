@@ -542,6 +542,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // issued by each group during its softmax phase of tile t, and a workgroup
 // waits only for tile t's copies at its top. Causal masking, the row/key bookkeeping, the lazy online
 // softmax in base 2 and the epilogue are those of attn_fwd_kernel.
+//
+// Causal launches give a workgroup two row tiles of one (batch, head unit),
+// rt and its mirror row_tiles-1-rt (variable-length calls: of one sequence,
+// from the work list), so that every workgroup reads about the same number
+// of key tiles; the second item's Q rows are copied into LDS during the
+// first item's last two tiles and its first K/V tile while the first drains.
 template <int D, bool CAUSAL, bool PAGED, bool VARLEN>
 __global__ __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_pingpong_kernel(
     const FwdParams p) {
