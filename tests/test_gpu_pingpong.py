@@ -102,3 +102,49 @@ def test_without_lse():
     Oa, _ = gpu_run(q, k, v, True, scale, pack, 1)
     Ob, Lb = gpu_run(q, k, v, True, scale, pack, 1, with_lse=False)
     assert Lb is None and torch.equal(Oa, Ob)
+
+
+def test_random_shapes_bitwise():
+    """Seeded random shapes that the plan sends to the 8-wavefront kernel (group sizes 1-8, query
+    and key counts up to 3000 with Sq > Sk, Sq < Sk and Sq = Sk, causal or not, three score
+    factors): the batched call (causal: paired row tiles) equals, bit for bit, the 4-wavefront
+    kernel (the same tokens as an equal-length variable-length call on the plain grid) and the
+    variable-length work list (max_seqlen_q twice the length)."""
+    import numpy as np
+    import grouped_query_exact_amd as g
+    ran = 0
+    for seed in range(160):
+        rs = np.random.RandomState(70000 + seed)
+        Hk = int(rs.choice([1, 2, 4, 8]))
+        G = int(rs.choice([1, 2, 3, 4, 5, 8]))
+        Hq, d = G * Hk, 128
+        Sq = int(rs.randint(1, 3000))
+        Sk = int(rs.choice([Sq, rs.randint(1, 3000)]))
+        causal = bool(rs.randint(0, 2))
+        B = int(rs.randint(1, 25))
+        if g.gqa_attn_plan(B, Sq, Sk, Hq, Hk, d, causal, -1, 0)["threads"] != 512:
+            continue
+        if B * Sq * Hq * d > 2.5e8 or B * Sk * Hk * d > 2.5e8:
+            continue
+        ran += 1
+        scale = float(rs.choice([1 / math.sqrt(d), 0.3, -0.05]))
+        gen = torch.Generator(device=DEV)
+        gen.manual_seed(seed)
+        q = torch.randn((B, Sq, Hq, d), generator=gen, device=DEV).to(torch.bfloat16)
+        k = torch.randn((B, Sk, Hk, d), generator=gen, device=DEV).to(torch.bfloat16)
+        v = torch.randn((B, Sk, Hk, d), generator=gen, device=DEV).to(torch.bfloat16)
+        ob = torch.full_like(q, float("nan"))
+        lb = torch.full((B, Hq, Sq), float("nan"), dtype=torch.float32, device=DEV)
+        g.gqa_attn_fwd(q, k, v, ob, lb, causal, scale)
+        cq = torch.arange(0, (B + 1) * Sq, Sq, dtype=torch.int32, device=DEV)
+        ck = torch.arange(0, (B + 1) * Sk, Sk, dtype=torch.int32, device=DEV)
+        tag = f"seed={seed} B={B} Sq={Sq} Sk={Sk} Hq={Hq} Hk={Hk} causal={causal}"
+        for mq in (Sq, 2 * Sq):
+            ov = torch.full((B * Sq, Hq, d), float("nan"), dtype=torch.bfloat16, device=DEV)
+            lv = torch.full((Hq, B * Sq), float("nan"), dtype=torch.float32, device=DEV)
+            g.gqa_attn_fwd_varlen(q.view(B * Sq, Hq, d), k.view(B * Sk, Hk, d), v.view(B * Sk, Hk, d), ov, lv, cq, ck,
+                                  mq, Sk, causal, scale)
+            torch.cuda.synchronize()
+            assert torch.equal(ov.view(B, Sq, Hq, d), ob), f"{tag} max_seqlen_q={mq}: O"
+            assert torch.equal(lv.view(Hq, B, Sq).permute(1, 0, 2), lb), f"{tag} max_seqlen_q={mq}: LSE"
+    assert ran >= 50, ran
