@@ -4,6 +4,7 @@
 #include <algorithm>
 #include <climits>
 #include <cmath>
+#include <cstdlib>
 
 #include "../../include/gqa_attn.h"
 
@@ -112,34 +113,39 @@ int make_plan(const Shape& s, int pack_gqa, int num_splits, int num_cus, Plan* p
     p->key_tiles = p->R > 0 ? key_tiles_for(s, p->Gp, p->R, p->block_n) : 0;
     ns = std::max(1, std::min(ns, std::max(1, p->key_tiles)));
     p->ns = ns;
-    // Variable-length prefill whose sequences leave most of the grid empty
-    // (fewer than 3/4 of B * max_seqlen_q query tokens) runs from a work list
-    // that a scheduling kernel builds on the device: only the (sequence, row
-    // tile) items that exist, heaviest first. With about full sequences the
-    // plain grid is as good and saves that launch (measured on MI355X, Llama-2
-    // heads, causal: 8 x 2048 tokens 855 TFLOP/s from the grid against 801
-    // from the list; 16 sequences of 128..2048 tokens 704 against 742, and 48
-    // of 100..1839 tokens 673 against 721, from the list on the 8-wavefront
-    // kernel).
-    p->worklist = s.varlen && !p->decode && 4 * s.total_q < 3LL * s.B * s.Sq ? 1 : 0;
-    // unsplit bf16 calls at d=128 with enough 256-row items to give every
+    // Unsplit bf16 calls at d=128 with enough 256-row items to give every
     // compute unit kPPMinItemsPerCU of them run on the 8-wavefront kernel
     // (or one per compute unit when the items are long: an estimated average
     // of at least kPPMinKeyTiles key tiles, from the first and last row
-    // tile); variable-length calls only from a work list, counting the items
-    // their tokens fill (without one, the empty items of the grid cost the
-    // 8-wavefront kernel more: 683 TFLOP/s on it against 730 on the
-    // 4-wavefront kernel for 16 sequences of 128..2048 tokens)
+    // tile). Variable-length calls count the items their tokens fill and take
+    // that kernel only from a work list (on the plain grid the empty items
+    // cost it more: 683 TFLOP/s on it against 730 on the 4-wavefront kernel
+    // for 16 sequences of 128..2048 tokens). GQA_ATTN_FORCE_TILED=1 in the
+    // environment keeps every prefill call on the 4-wavefront kernel (same
+    // results bit for bit; for comparisons).
+    const char* force_env = std::getenv("GQA_ATTN_FORCE_TILED");
+    const bool force_tiled = force_env && force_env[0] && !(force_env[0] == '0' && !force_env[1]);
+    const bool pp_shape = !force_tiled && !p->decode && ns == 1 && s.d == 128 && s.q_bytes == 2 && s.kv_bytes == 2;
+    const long long cus = num_cus > 0 ? num_cus : 256;
+    const bool pp_varlen = pp_shape && s.varlen &&
+                           p->units_per_b * (ceil_div(s.total_q * p->Gp, kPPBlockM) + s.B) >= (long long)kPPMinItemsPerCU * cus;
+    // Variable-length prefill runs from a work list that a scheduling kernel
+    // builds on the device (only the (sequence, row tile) items that exist,
+    // heaviest first) when its sequences leave most of the grid empty (fewer
+    // than 3/4 of B * max_seqlen_q query tokens), and always when it goes to
+    // the 8-wavefront kernel. Measured on MI355X, Llama-2 heads: for about
+    // full batches the 4-wavefront kernel's plain grid beats the list on the
+    // same kernel (8 x 2048 tokens, causal: 855 against 801 TFLOP/s), but the
+    // list on the 8-wavefront kernel beats both (8 x 2048, 12 sequences of
+    // 1500..1900 tokens, 16 x 1000, 32 x 512, 4 x 4096: causal 910, 865,
+    // 745, 539, 1026 against 857, 802, 715, 485, 967 from the grid;
+    // non-causal 1042, 997, 897, 756, 1124 against 928, 823, 817, 641, 989).
+    p->worklist = s.varlen && !p->decode && (4 * s.total_q < 3LL * s.B * s.Sq || pp_varlen) ? 1 : 0;
     p->pingpong = 0;
-    const bool pp_shape = !p->decode && ns == 1 && s.d == 128 && s.q_bytes == 2 && s.kv_bytes == 2;
-    if (pp_shape && s.varlen) {
-        if (p->worklist) {
-            const long long items = p->units_per_b * (ceil_div(s.total_q * p->Gp, kPPBlockM) + s.B);
-            if (items >= (long long)kPPMinItemsPerCU * (num_cus > 0 ? num_cus : 256)) p->pingpong = 1;
-        }
+    if (s.varlen) {
+        p->pingpong = pp_varlen ? 1 : 0;
     } else if (pp_shape) {
         const long long items = (long long)s.B * p->units_per_b * ceil_div(p->R, kPPBlockM);
-        const long long cus = num_cus > 0 ? num_cus : 256;
         if (items >= (long long)kPPMinItemsPerCU * cus) {
             p->pingpong = 1;
         } else if (items >= cus) {

@@ -171,7 +171,8 @@ int gqa_attn_bwd(const void* q, const void* k, const void* v, const void* out, c
  * max_seqlen_q of a sequence are not written), never an out-of-bounds
  * access. Pointers as for gqa_attn_fwd (the offset arrays 4-byte aligned).
  * Calls with more than 32 query rows per head unit whose sequences hold
- * fewer than 3/4 of B * max_seqlen_q query tokens first run a small
+ * fewer than 3/4 of B * max_seqlen_q query tokens, and every call that runs
+ * on the 8-wavefront kernel (unsplit, d = 128, enough rows), first run a small
  * scheduling kernel that lists, from the offsets, the (sequence, row tile)
  * work items that exist, heaviest first (causal calls on the 8-wavefront
  * kernel: pairs of a sequence's row tiles R-1-i and i, run by one workgroup),
@@ -287,7 +288,11 @@ int gqa_attn_choose(int B, int Sq, int Sk, int Hq, int Hk, int d, int causal, in
                     int* pack_gqa, int* num_splits);
 
 /* Launch plan of one call, for tests and benchmarks. Host only: no HIP call
- * is made when num_cus > 0. */
+ * is made when num_cus > 0.
+ * Environment: GQA_ATTN_FORCE_TILED=1 (read at every call's plan) keeps every
+ * prefill call on the 4-wavefront tiled kernel instead of the 8-wavefront
+ * one; the two compute the same results bit for bit, so the switch changes
+ * only the speed (for comparisons and diagnosis). */
 typedef struct {
     int pack_gqa;          /* resolved pack flag */
     int num_splits;        /* resolved and clamped split count */

@@ -25,6 +25,25 @@ import torch
 
 import oracle
 
+class force_tiled:
+    """Context manager: prefill calls inside it run on the 4-wavefront tiled kernel
+    (GQA_ATTN_FORCE_TILED=1, read by the library's planner at every call)."""
+
+    def __enter__(self):
+        import os
+        self._old = os.environ.get("GQA_ATTN_FORCE_TILED")
+        os.environ["GQA_ATTN_FORCE_TILED"] = "1"
+        return self
+
+    def __exit__(self, *exc):
+        import os
+        if self._old is None:
+            os.environ.pop("GQA_ATTN_FORCE_TILED", None)
+        else:
+            os.environ["GQA_ATTN_FORCE_TILED"] = self._old
+        return False
+
+
 TOL_O_MAX = 2e-2
 TOL_O_MEAN = 2e-3
 TOL_LSE = 1e-3

@@ -4,10 +4,10 @@ against the 4-wavefront tiled kernel (GPU).
 Unsplit bf16 calls at d=128 with at least two 256-row work items per compute
 unit run on the 8-wavefront kernel. The shapes below sit just past that threshold (512
 or more items on 256 compute units), so the oracle compares every element.
-Variable-length calls always use the 4-wavefront kernel: a batch of
-equal-length sequences through gqa_attn_fwd_varlen gives that kernel's result
-for the same rows, and since the two kernels share their per-row arithmetic
-(tile order, operand order, softmax and epilogue) they must agree bit for bit.
+With GQA_ATTN_FORCE_TILED=1 every prefill call runs on the 4-wavefront kernel:
+the same rows through it give that kernel's result, and since the two kernels
+share their per-row arithmetic (tile order, operand order, softmax and
+epilogue) they must agree bit for bit.
 """
 
 import math
@@ -16,7 +16,7 @@ import pytest
 import torch
 
 import gqa_inputs as gi
-from _parity import compare_to_oracle, gpu_run
+from _parity import compare_to_oracle, force_tiled, gpu_run
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -87,9 +87,11 @@ def test_bitwise_equal_to_4_wavefront_kernel(shape):
         O8, L8 = gpu_run(qd, kd, vd, causal, scale, pack, 1)
         O4 = torch.full((B * Sq, Hq, d), float("nan"), dtype=torch.bfloat16, device=DEV)
         L4 = torch.full((Hq, B * Sq), float("nan"), dtype=torch.float32, device=DEV)
-        g.gqa_attn_fwd_varlen(qd.view(B * Sq, Hq, d), kd.view(B * Sk, Hk, d), vd.view(B * Sk, Hk, d), O4, L4, cq, ck,
-                              Sq, Sk, causal, scale, pack, 1)
-        torch.cuda.synchronize()
+        with force_tiled():
+            assert g.gqa_attn_plan(B, Sq, Sk, Hq, Hk, d, causal, pack, 1)["threads"] == 256
+            g.gqa_attn_fwd_varlen(qd.view(B * Sq, Hq, d), kd.view(B * Sk, Hk, d), vd.view(B * Sk, Hk, d), O4, L4, cq,
+                                  ck, Sq, Sk, causal, scale, pack, 1)
+            torch.cuda.synchronize()
         assert torch.equal(O8.view(B * Sq, Hq, d), O4), f"O {shape} causal={causal}"
         assert torch.equal(L8.permute(1, 0, 2).reshape(Hq, B * Sq), L4), f"LSE {shape} causal={causal}"
 
@@ -108,8 +110,8 @@ def test_random_shapes_bitwise():
     """Seeded random shapes that the plan sends to the 8-wavefront kernel (group sizes 1-8, query
     and key counts up to 3000 with Sq > Sk, Sq < Sk and Sq = Sk, causal or not, three score
     factors): the batched call (causal: paired row tiles) equals, bit for bit, the 4-wavefront
-    kernel (the same tokens as an equal-length variable-length call on the plain grid) and the
-    variable-length work list (max_seqlen_q twice the length)."""
+    kernel (the same tokens as an equal-length variable-length call with GQA_ATTN_FORCE_TILED=1)
+    and the variable-length work list on the 8-wavefront kernel."""
     import numpy as np
     import grouped_query_exact_amd as g
     ran = 0
@@ -139,12 +141,17 @@ def test_random_shapes_bitwise():
         cq = torch.arange(0, (B + 1) * Sq, Sq, dtype=torch.int32, device=DEV)
         ck = torch.arange(0, (B + 1) * Sk, Sk, dtype=torch.int32, device=DEV)
         tag = f"seed={seed} B={B} Sq={Sq} Sk={Sk} Hq={Hq} Hk={Hk} causal={causal}"
-        for mq in (Sq, 2 * Sq):
+        for tiled in (True, False):
             ov = torch.full((B * Sq, Hq, d), float("nan"), dtype=torch.bfloat16, device=DEV)
             lv = torch.full((Hq, B * Sq), float("nan"), dtype=torch.float32, device=DEV)
-            g.gqa_attn_fwd_varlen(q.view(B * Sq, Hq, d), k.view(B * Sk, Hk, d), v.view(B * Sk, Hk, d), ov, lv, cq, ck,
-                                  mq, Sk, causal, scale)
+            call = lambda: g.gqa_attn_fwd_varlen(q.view(B * Sq, Hq, d), k.view(B * Sk, Hk, d), v.view(B * Sk, Hk, d),
+                                                 ov, lv, cq, ck, Sq, Sk, causal, scale)
+            if tiled:
+                with force_tiled():
+                    call()
+            else:
+                call()
             torch.cuda.synchronize()
-            assert torch.equal(ov.view(B, Sq, Hq, d), ob), f"{tag} max_seqlen_q={mq}: O"
-            assert torch.equal(lv.view(Hq, B, Sq).permute(1, 0, 2), lb), f"{tag} max_seqlen_q={mq}: LSE"
+            assert torch.equal(ov.view(B, Sq, Hq, d), ob), f"{tag} tiled={tiled}: O"
+            assert torch.equal(lv.view(Hq, B, Sq).permute(1, 0, 2), lb), f"{tag} tiled={tiled}: LSE"
     assert ran >= 50, ran

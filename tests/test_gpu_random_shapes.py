@@ -15,7 +15,7 @@ import torch
 
 import gqa_inputs as gi
 import oracle
-from _parity import TOL_LSE, TOL_O_MAX, TOL_O_MEAN, f64
+from _parity import TOL_LSE, TOL_O_MAX, TOL_O_MEAN, f64, force_tiled
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -219,8 +219,8 @@ def draw8(seed):
 
 @pytest.mark.parametrize("seed", range(16))
 def test_random_forward_8_wavefront(seed):
-    """The 8-wavefront kernel (d=128) on seeded shapes: bit for bit the 4-wavefront kernel (reached through
-    the variable-length entry point with equal lengths) on every row, the oracle on two batch elements."""
+    """The 8-wavefront kernel (d=128) on seeded shapes: bit for bit the 4-wavefront kernel (the same rows
+    with GQA_ATTN_FORCE_TILED=1) on every row, the oracle on two batch elements."""
     import grouped_query_exact_amd as g
     B, Sq, Sk, Hq, Hk, d, causal, pack = draw8(12000 + seed)
     tag = f"seed={seed} B={B} Sq={Sq} Sk={Sk} Hq={Hq} Hk={Hk} d={d} causal={causal} pack={pack}"
@@ -235,9 +235,10 @@ def test_random_forward_8_wavefront(seed):
     l4 = torch.empty((Hq, B * Sq), dtype=torch.float32, device=DEV)
     cq = torch.arange(0, (B + 1) * Sq, Sq, dtype=torch.int32, device=DEV)
     ck = torch.arange(0, (B + 1) * Sk, Sk, dtype=torch.int32, device=DEV)
-    g.gqa_attn_fwd_varlen(qd.view(B * Sq, Hq, d), kd.view(B * Sk, Hk, d), vd.view(B * Sk, Hk, d), o4, l4, cq, ck,
-                          Sq, Sk, causal, scale, pack, 1)
-    torch.cuda.synchronize()
+    with force_tiled():
+        g.gqa_attn_fwd_varlen(qd.view(B * Sq, Hq, d), kd.view(B * Sk, Hk, d), vd.view(B * Sk, Hk, d), o4, l4, cq, ck,
+                              Sq, Sk, causal, scale, pack, 1)
+        torch.cuda.synchronize()
     assert torch.equal(out.view(B * Sq, Hq, d), o4), "O " + tag
     assert torch.equal(lse.permute(1, 0, 2).reshape(Hq, B * Sq), l4), "LSE " + tag
     sel = sorted({0, B - 1})

@@ -291,6 +291,20 @@ def test_choose_heuristic_shapes():
         g.gqa_attn_choose(1, 4, 4, 6, 4, 64, False, 256)
 
 
+def test_plan_force_tiled_switch(monkeypatch):
+    """GQA_ATTN_FORCE_TILED=1 keeps prefill calls on the 4-wavefront kernel (128-row tiles, every row
+    tile its own workgroup); "0" or an empty value leaves the choice to the plan."""
+    import grouped_query_exact_amd as g
+    args = (128, 2048, 2048, 32, 8, 128, True, 1, 1, 256)
+    assert g.gqa_attn_plan(*args)["threads"] == 512
+    monkeypatch.setenv("GQA_ATTN_FORCE_TILED", "1")
+    p = g.gqa_attn_plan(*args)
+    assert (p["threads"], p["block_m"], p["grid"]) == (256, 128, 128 * 8 * 64)
+    for off in ("0", ""):
+        monkeypatch.setenv("GQA_ATTN_FORCE_TILED", off)
+        assert g.gqa_attn_plan(*args)["threads"] == 512
+
+
 def test_plan_grid_and_workspace():
     import grouped_query_exact_amd as g
     p = g.gqa_attn_plan(128, 2048, 2048, 32, 8, 128, True, 1, 1, 256)
