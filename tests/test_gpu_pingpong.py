@@ -35,6 +35,12 @@ SHAPES = [
 ]
 
 
+def _keys(Sk, causal):
+    """Non-causal calls whose rows read at most 8 key tiles keep the 4-wavefront kernel: those
+    variants of the shapes get 576 more keys (9 more tiles, the raggedness kept)."""
+    return Sk if causal or Sk > 8 * 64 else Sk + 576
+
+
 def _qkv(seed, B, Sq, Sk, Hq, Hk, d):
     return (gi.random_bf16(seed, (B, Sq, Hq, d)), gi.random_bf16(seed + 1, (B, Sk, Hk, d)),
             gi.random_bf16(seed + 2, (B, Sk, Hk, d)))
@@ -50,6 +56,7 @@ def _assert_selected(B, Sq, Sk, Hq, Hk, d, causal, pack):
 @pytest.mark.parametrize("causal", [True, False])
 def test_oracle_parity(shape, causal):
     B, Sq, Sk, Hq, Hk, d, pack = shape
+    Sk = _keys(Sk, causal)
     _assert_selected(B, Sq, Sk, Hq, Hk, d, causal, pack)
     q, k, v = _qkv(9700 + Sq + Sk + d, B, Sq, Sk, Hq, Hk, d)
     scale = gi.fp32(1 / math.sqrt(d))
@@ -65,9 +72,10 @@ def test_scales(scale):
     against the per-element rounding bound instead of the flat tolerance, as for the
     other stress inputs."""
     B, Sq, Sk, Hq, Hk, d, pack = SHAPES[1]
-    _assert_selected(B, Sq, Sk, Hq, Hk, d, True, pack)
+    Sk = _keys(Sk, False)
     q, k, v = _qkv(9800, B, Sq, Sk, Hq, Hk, d)
     for causal in (True, False):
+        _assert_selected(B, Sq, Sk, Hq, Hk, d, causal, pack)
         O, L = gpu_run(q, k, v, causal, gi.fp32(scale), pack, 1)
         compare_to_oracle(O, L, q, k, v, causal, gi.fp32(scale), tag=f"scale={scale} causal={causal}",
                           derived_bound=abs(scale) > 0.1)
@@ -76,12 +84,13 @@ def test_scales(scale):
 @pytest.mark.parametrize("shape", SHAPES, ids=[f"B{s[0]}_Sq{s[1]}_Sk{s[2]}_G{s[3] // s[4]}_d{s[5]}_p{s[6]}" for s in SHAPES])
 def test_bitwise_equal_to_4_wavefront_kernel(shape):
     import grouped_query_exact_amd as g
-    B, Sq, Sk, Hq, Hk, d, pack = shape
-    q, k, v = _qkv(9900 + Sq + Sk + d, B, Sq, Sk, Hq, Hk, d)
-    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
-    cq = torch.arange(0, (B + 1) * Sq, Sq, dtype=torch.int32, device=DEV)
-    ck = torch.arange(0, (B + 1) * Sk, Sk, dtype=torch.int32, device=DEV)
+    B, Sq, Sk0, Hq, Hk, d, pack = shape
     for causal in (True, False):
+        Sk = _keys(Sk0, causal)
+        q, k, v = _qkv(9900 + Sq + Sk + d, B, Sq, Sk, Hq, Hk, d)
+        qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+        cq = torch.arange(0, (B + 1) * Sq, Sq, dtype=torch.int32, device=DEV)
+        ck = torch.arange(0, (B + 1) * Sk, Sk, dtype=torch.int32, device=DEV)
         _assert_selected(B, Sq, Sk, Hq, Hk, d, causal, pack)
         scale = gi.fp32(1 / math.sqrt(d))
         O8, L8 = gpu_run(qd, kd, vd, causal, scale, pack, 1)

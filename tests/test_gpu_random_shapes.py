@@ -210,6 +210,8 @@ def draw8(seed):
     Sq = int(rs.choice([200, 255, 256, 257, 300, 511, 512, 513, 700, 1025]))
     Sk = int(rs.choice([63, 64, 65, 199, 300, 511, 513, 1024, 1100]))
     causal = bool(rs.randint(0, 2))
+    if not causal and Sk <= 8 * 64:  # non-causal rows of at most 8 key tiles keep the 4-wavefront kernel
+        Sk += 576
     pack = 1 if G > 1 and rs.randint(0, 3) else 0
     units = Hk if pack else G * Hk
     rt8 = -(-(Sq * (G if pack else 1)) // 256)
