@@ -1,6 +1,7 @@
 // C-ABI entry points of the GQA forward library (declared in include/gqa_attn.h).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <climits>
 #include <cmath>
@@ -70,6 +71,69 @@ hipMemPool_t lib_pool(int dev) {
 hipError_t ws_alloc(void** ptr, size_t bytes, int dev, hipStream_t stream) {
     hipMemPool_t pool = lib_pool(dev);
     return pool ? hipMallocFromPoolAsync(ptr, bytes, pool, stream) : hipMallocAsync(ptr, bytes, stream);
+}
+
+// Workspaces of up to kWsCacheBytes are kept per (device, stream) and reused
+// by later calls on that stream: calls on one stream run in order, so a
+// buffer that only that stream's work uses needs no allocation, release or
+// wait between them (a stream-ordered allocation and release per call left
+// the GPU idle for several microseconds between the kernels of consecutive
+// split decode calls). A call that needs more than the stream's buffer
+// holds releases it after the work already enqueued on that stream and
+// takes a larger one, stream-ordered. At most kWsCacheEntries streams get a
+// kept buffer; calls on further streams, calls being captured into a graph
+// and calls that need more than kWsCacheBytes allocate and release their
+// workspace per call, as before. Kept buffers live until the process ends.
+constexpr size_t kWsCacheBytes = 64ull << 20;
+constexpr int kWsCacheEntries = 16;
+struct WsEntry {
+    int dev;
+    hipStream_t stream;
+    void* ptr;
+    size_t bytes;
+};
+std::mutex g_ws_mu;
+WsEntry g_ws[kWsCacheEntries];
+int g_ws_used = 0;
+
+// A workspace of `bytes` for work enqueued on `stream` of device `dev`.
+// *kept tells whether it is a kept buffer (not to be released by the caller)
+// or a per-call allocation (to be released with hipFreeAsync on `stream`).
+hipError_t ws_acquire(void** ptr, size_t bytes, int dev, hipStream_t stream, bool* kept) {
+    *kept = false;
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cap) != hipSuccess) {
+        (void)hipGetLastError();
+        cap = hipStreamCaptureStatusActive;  // unknown: take the per-call path
+    }
+    if (bytes > kWsCacheBytes || cap != hipStreamCaptureStatusNone) return ws_alloc(ptr, bytes, dev, stream);
+    std::lock_guard<std::mutex> lock(g_ws_mu);
+    WsEntry* e = nullptr;
+    for (int i = 0; i < g_ws_used; ++i)
+        if (g_ws[i].dev == dev && g_ws[i].stream == stream) e = &g_ws[i];
+    if (!e) {
+        if (g_ws_used == kWsCacheEntries) return ws_alloc(ptr, bytes, dev, stream);
+        e = &g_ws[g_ws_used];
+        *e = WsEntry{dev, stream, nullptr, 0};
+        ++g_ws_used;
+    }
+    if (e->bytes < bytes) {
+        // grow in steps of 1 MiB, at least doubling, up to the cap
+        size_t want = std::max(bytes, std::min(2 * e->bytes, kWsCacheBytes));
+        want = (want + (1u << 20) - 1) & ~(size_t)((1u << 20) - 1);
+        want = std::min(std::max(want, bytes), kWsCacheBytes);
+        if (e->ptr && hipFreeAsync(e->ptr, stream) != hipSuccess) return hipErrorUnknown;
+        e->ptr = nullptr;
+        e->bytes = 0;
+        void* fresh = nullptr;
+        const hipError_t err = ws_alloc(&fresh, want, dev, stream);
+        if (err != hipSuccess || !fresh) return err != hipSuccess ? err : hipErrorOutOfMemory;
+        e->ptr = fresh;
+        e->bytes = want;
+    }
+    *ptr = e->ptr;
+    *kept = true;
+    return hipSuccess;
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -265,6 +329,7 @@ int run(const Call& c) {
     }
 
     void* ws = nullptr;
+    bool ws_kept = false;
     const size_t split_bytes = plan.ns == 1 ? 0
                                : c.varlen ? (size_t)plan.ns * (size_t)c.total_q * s.Hq * ((size_t)d * 4 + 8)
                                           : (size_t)plan.workspace_bytes;
@@ -275,7 +340,7 @@ int run(const Call& c) {
         if (ws_bytes > (size_t)gqa::kScratchBytes) return GQA_ERR_SCRATCH;
         if (gqa::scratch_address(dev, &ws) != hipSuccess || !ws) return GQA_ERR_HIP;
     } else {
-        if (ws_alloc(&ws, ws_bytes, dev, c.stream) != hipSuccess || !ws) {
+        if (ws_acquire(&ws, ws_bytes, dev, c.stream, &ws_kept) != hipSuccess || !ws) {
             (void)hipGetLastError();
             return GQA_ERR_NOMEM;
         }
@@ -331,7 +396,7 @@ int run(const Call& c) {
         if (cgrid > INT_MAX) e = hipErrorInvalidValue;
         else e = gqa::launch_combine(cp, d, cgrid, c.stream);
     }
-    const hipError_t ef = c.noalloc ? hipSuccess : hipFreeAsync(ws, c.stream);
+    const hipError_t ef = (c.noalloc || ws_kept) ? hipSuccess : hipFreeAsync(ws, c.stream);
     if (e != hipSuccess || ef != hipSuccess) return GQA_ERR_HIP;
     return GQA_OK;
 }
@@ -432,14 +497,15 @@ int gqa_attn_bwd(const void* q, const void* k, const void* v, const void* out, c
         void* ws = nullptr;
         const size_t rows = (size_t)B * Hq * (size_t)(Sq > 0 ? Sq : 1);
         const size_t ws_bytes = 2 * rows * 4;  // D, then -LSE*log2(e)
-        if (ws_alloc(&ws, ws_bytes, dev, stream) != hipSuccess || !ws) {
+        bool ws_kept = false;
+        if (ws_acquire(&ws, ws_bytes, dev, stream, &ws_kept) != hipSuccess || !ws) {
             (void)hipGetLastError();
             return GQA_ERR_NOMEM;
         }
         p.drow = (float*)ws;
         p.nlse2 = (float*)ws + rows;
         const hipError_t e = gqa::launch_backward(p, d, causal != 0, stream);
-        const hipError_t ef = hipFreeAsync(ws, stream);
+        const hipError_t ef = ws_kept ? hipSuccess : hipFreeAsync(ws, stream);
         if (e != hipSuccess || ef != hipSuccess) return GQA_ERR_HIP;
         return GQA_OK;
     } catch (...) {

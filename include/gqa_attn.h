@@ -37,8 +37,18 @@
  * work list of variable-length prefill, the backward's D and base-2
  * log-sum-exp), stream-ordered on the caller's stream
  * (hipMallocFromPoolAsync/hipFreeAsync) from a memory pool the library
- * creates per device, so calls on different streams never share them. That pool keeps up to 256 MiB of freed workspace reserved for
- * later calls and returns anything above that to the device at the next
+ * creates per device, so calls on different streams never share them.
+ * Workspaces of up to 64 MiB are kept per (device, stream handle), for the
+ * first 16 such pairs, and reused by later calls on the same stream without
+ * a new allocation (calls on one stream run in order); a call that needs
+ * more grows the kept buffer stream-ordered. Kept buffers are held until the
+ * process ends. Because they are tied to the stream handle, a stream that
+ * ran such calls must have finished its work before it is destroyed (for
+ * example hipStreamSynchronize first), so that a stream created later with
+ * the same handle cannot overlap it. Calls during graph capture, calls on
+ * further streams and larger workspaces are allocated and released per
+ * call. The pool keeps up to 256 MiB of freed workspace reserved for later
+ * calls and returns anything above that to the device at the next
  * synchronisation; the device's default pool is not modified. Other state:
  * a per-device cache of the compute-unit count (and, for
  * gqa_attn_fwd_noalloc, its fixed scratch array).
@@ -47,8 +57,8 @@
  * stream. They are thread-safe. No C++ exception crosses this boundary. A
  * forward call whose split count resolves to 1 enqueues exactly one kernel
  * and nothing else (no allocation, memset or copy), so it can be captured in
- * a HIP graph and replayed; split calls also enqueue the workspace
- * allocation, the combine kernel and the release of the workspace, and
+ * a HIP graph and replayed; split calls also enqueue the combine kernel
+ * (and, where the workspace is not a kept one, its allocation and release), and
  * variable-length prefill calls of very different lengths a scheduling kernel
  * and its workspace.
  */
