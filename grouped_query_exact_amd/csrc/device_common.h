@@ -138,4 +138,107 @@ __device__ __forceinline__ float xhalf_sum(float v) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// ---- Online-softmax step of the prefill kernels: one 64-key tile, this
+// lane's 32 scores in two 32-key MFMA blocks (slot i of block mb), half of
+// the row's 64 scores (the lane 32 away holds the other half).
+//
+// The running maximum m_run (scaled log2 units, an integer) is raised only
+// when the row needs it: the row has seen no key yet (m_run = -inf), or one
+// of its partial sums of this tile's probabilities exp2(s*c - m_run) exceeds
+// kFastSumLimit (so a probability exceeds kFastSumLimit/8). Otherwise the
+// tile's probabilities are formed against m_run as it stands, without the
+// row maximum of the tile. The decision depends on the row's own scores
+// only, so it is the same whatever rows share the wavefront. Probabilities
+// stay below kFastSumLimit and the sums of a row below 2^51 for any length
+// below 2^31 keys, far from the fp32 range; a raise goes to the integer
+// ceil(row maximum), so every probability is still exp2 of the score against
+// an integral maximum.
+constexpr float kFastSumLimit = 1048576.0f;  // 2^20
+
+// Probabilities of the tile against m_run (0 in place of -inf): pk (bf16,
+// the B operand of the output product) and the four partial fp32 sums tl
+// (slots i with i % 4 == j into tl[j]). Returns whether the row must raise
+// its maximum first (row-uniform).
+__device__ __forceinline__ bool softmax_exps(const f32x16 (&s)[2], float c, float m_run, float (&tl)[4],
+                                             bf16x8 (&pk)[4]) {
+    const bool fresh = m_run == -__builtin_inff();
+    const float moff = fresh ? 0.f : m_run;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) tl[j] = 0.f;
+    // each bf16 vector is written whole, so no earlier value of pk stays live
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            x[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r >> 1][(r & 1) * 8 + e], c, -moff));
+            tl[e & 3] += x[e];
+        }
+        pk[r] = bf16x8{(__bf16)x[0], (__bf16)x[1], (__bf16)x[2], (__bf16)x[3],
+                       (__bf16)x[4], (__bf16)x[5], (__bf16)x[6], (__bf16)x[7]};
+    }
+    const float big = xhalf_max(fmaxf(fmaxf(tl[0], tl[1]), fmaxf(tl[2], tl[3])));
+    return fresh || !(big <= kFastSumLimit);
+}
+
+// Row maximum of the tile's 64 scores (-inf where all are masked).
+__device__ __forceinline__ float row_max64(const f32x16 (&s)[2]) {
+    float t0 = fmaxf(fmaxf(s[0][0], s[0][1]), s[0][2]);
+    float t1 = fmaxf(fmaxf(s[0][3], s[0][4]), s[0][5]);
+    float t2 = fmaxf(fmaxf(s[0][6], s[0][7]), s[0][8]);
+    float t3 = fmaxf(fmaxf(s[0][9], s[0][10]), s[0][11]);
+    t0 = fmaxf(fmaxf(t0, s[0][12]), s[0][13]);
+    t1 = fmaxf(fmaxf(t1, s[0][14]), s[0][15]);
+    t2 = fmaxf(fmaxf(t2, s[1][0]), s[1][1]);
+    t3 = fmaxf(fmaxf(t3, s[1][2]), s[1][3]);
+    t0 = fmaxf(fmaxf(t0, s[1][4]), s[1][5]);
+    t1 = fmaxf(fmaxf(t1, s[1][6]), s[1][7]);
+    t2 = fmaxf(fmaxf(t2, s[1][8]), s[1][9]);
+    t3 = fmaxf(fmaxf(t3, s[1][10]), s[1][11]);
+    t0 = fmaxf(fmaxf(t0, s[1][12]), s[1][13]);
+    t1 = fmaxf(fmaxf(t1, s[1][14]), s[1][15]);
+    return xhalf_max(fmaxf(fmaxf(t0, t1), fmaxf(t2, t3)));
+}
+
+// The raise for rows with `need` (others keep m_run, alpha = 1): m_run
+// becomes ceil of the tile's scaled row maximum where that exceeds it; O and
+// the sums are multiplied by alpha = 2^(m_old - m_new) (0 for the row's
+// first visible key); then the tile's probabilities are formed again. A row
+// without `need` reproduces exactly what softmax_exps gave it.
+template <int NCB>
+__device__ __forceinline__ void softmax_raise(const f32x16 (&s)[2], float c, float& m_run, bool need,
+                                              float (&l_part)[4], float (&w_part)[4], f32x16 (&oacc)[NCB],
+                                              float (&tl)[4], bf16x8 (&pk)[4]) {
+    const float mx = row_max64(s);
+    const float mxs = (mx == -__builtin_inff()) ? -__builtin_inff() : mx * c;
+    float alpha = 1.f;
+    if (need && mxs > m_run) {
+        const float m_new = __builtin_ceilf(mxs);
+        alpha = m_run == -__builtin_inff() ? 0.f : __builtin_amdgcn_ldexpf(1.f, (int)fmaxf(m_run - m_new, -256.f));
+        m_run = m_new;
+    }
+    if (__ballot(alpha != 1.f)) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            l_part[i] *= alpha;
+            w_part[i] *= alpha;
+        }
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) oacc[cb][i] *= alpha;
+    }
+    (void)softmax_exps(s, c, m_run, tl, pk);
+}
+
+// Adds the tile to the row's running sums: fp32 probabilities (the LSE) and
+// the bf16 ones the output product applies (the output's normaliser).
+__device__ __forceinline__ void softmax_commit(float (&l_part)[4], float (&w_part)[4], const float (&tl)[4],
+                                               const bf16x8 (&pk)[4]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) l_part[j] += tl[j];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) add_bf16x8(pk[r], w_part);
+}
+
 }  // namespace gqa

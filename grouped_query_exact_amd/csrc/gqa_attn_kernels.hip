@@ -356,8 +356,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const LDS char* kt = lds + buf * 2 * TILE_B;
         const LDS char* vt = kt + TILE_B;
 
-        // S^T = K Q^T: two blocks of 32 keys
+        // S^T = K Q^T: two blocks of 32 keys (masked where needed)
         f32x16 sacc[2];
+        auto scores = [&]() __attribute__((always_inline)) {
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
             sacc[mb] = f32x16{};
@@ -387,53 +388,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 for (int i = 0; i < 16; ++i)
                     if (mb * 32 + ((i >> 3) << 4) + (i & 7) > lim) sacc[mb][i] = -__builtin_inff();
         }
-        float mx;
-        {
-            float t0 = fmaxf(fmaxf(sacc[0][0], sacc[0][1]), sacc[0][2]);
-            float t1 = fmaxf(fmaxf(sacc[0][3], sacc[0][4]), sacc[0][5]);
-            float t2 = fmaxf(fmaxf(sacc[0][6], sacc[0][7]), sacc[0][8]);
-            float t3 = fmaxf(fmaxf(sacc[0][9], sacc[0][10]), sacc[0][11]);
-            t0 = fmaxf(fmaxf(t0, sacc[0][12]), sacc[0][13]);
-            t1 = fmaxf(fmaxf(t1, sacc[0][14]), sacc[0][15]);
-            t2 = fmaxf(fmaxf(t2, sacc[1][0]), sacc[1][1]);
-            t3 = fmaxf(fmaxf(t3, sacc[1][2]), sacc[1][3]);
-            t0 = fmaxf(fmaxf(t0, sacc[1][4]), sacc[1][5]);
-            t1 = fmaxf(fmaxf(t1, sacc[1][6]), sacc[1][7]);
-            t2 = fmaxf(fmaxf(t2, sacc[1][8]), sacc[1][9]);
-            t3 = fmaxf(fmaxf(t3, sacc[1][10]), sacc[1][11]);
-            t0 = fmaxf(fmaxf(t0, sacc[1][12]), sacc[1][13]);
-            t1 = fmaxf(fmaxf(t1, sacc[1][14]), sacc[1][15]);
-            mx = xhalf_max(fmaxf(fmaxf(t0, t1), fmaxf(t2, t3)));
-        }
-        // lazy running-max update (per row; both lanes of a row agree)
-        const float mxs = (mx == -__builtin_inff()) ? -__builtin_inff() : mx * c;
-        const float alpha = raise_max(m_run, mxs);
-        if (__ballot(alpha != 1.f)) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                l_part[i] *= alpha;
-                w_part[i] *= alpha;
-            }
-#pragma unroll
-            for (int cb = 0; cb < D / 32; ++cb)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) oacc[cb][i] *= alpha;
-        }
-        const float moff = (m_run == -__builtin_inff()) ? 0.f : m_run;
-
-        // P = exp2(s*c - m) -> bf16 (B operand of O^T += V^T P^T). Masked scores
-        // are -inf and c > 0, so their P is exactly 0.
+        };
+        scores();
+        // online softmax: the running maximum is raised only for rows that
+        // need it (softmax_exps, always on a row's first visible key); then
+        // the wavefront forms the scores again from the tile still in LDS
+        // (one more pass over the tile keeps the accumulators in one set of
+        // registers at this kernel's register budget)
         bf16x8 pk[4];
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mb][i], c, -moff));
-                l_part[i & 3] += x;
-                pk[mb * 2 + (i >> 3)][i & 7] = (__bf16)x;
-            }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) add_bf16x8(pk[r], w_part);
+        float tl[4];
+        const bool need = softmax_exps(sacc, c, m_run, tl, pk);
+        if (__ballot(need)) {
+            scores();
+            softmax_raise(sacc, c, m_run, need, l_part, w_part, oacc, tl, pk);
+        }
+        softmax_commit(l_part, w_part, tl, pk);
 
         // O^T += V^T P^T
 #pragma unroll
@@ -834,7 +803,7 @@ __global__ __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2
                     oacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), pk[kk], oacc[cb], 0, 0, 0);
                 }
         };
-        auto softmax = [&](int t) __attribute__((always_inline)) {
+        auto mask = [&](int t) __attribute__((always_inline)) {
             const int kv0 = t * kBlockN;
             const bool need_mask = (kv0 + kBlockN > Sk) || (CAUSAL && kv0 + kBlockN - 1 > iw_min + koff);
             // keys of this lane's slots: kv0 + 32*mb + 16*(i/8) + 8*half + (i%8)
@@ -846,49 +815,26 @@ __global__ __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2
                     for (int i = 0; i < 16; ++i)
                         if (mb * 32 + ((i >> 3) << 4) + (i & 7) > lim) sacc[mb][i] = -__builtin_inff();
             }
-            float mx;
-            {
-                float t0 = fmaxf(fmaxf(sacc[0][0], sacc[0][1]), sacc[0][2]);
-                float t1 = fmaxf(fmaxf(sacc[0][3], sacc[0][4]), sacc[0][5]);
-                float t2 = fmaxf(fmaxf(sacc[0][6], sacc[0][7]), sacc[0][8]);
-                float t3 = fmaxf(fmaxf(sacc[0][9], sacc[0][10]), sacc[0][11]);
-                t0 = fmaxf(fmaxf(t0, sacc[0][12]), sacc[0][13]);
-                t1 = fmaxf(fmaxf(t1, sacc[0][14]), sacc[0][15]);
-                t2 = fmaxf(fmaxf(t2, sacc[1][0]), sacc[1][1]);
-                t3 = fmaxf(fmaxf(t3, sacc[1][2]), sacc[1][3]);
-                t0 = fmaxf(fmaxf(t0, sacc[1][4]), sacc[1][5]);
-                t1 = fmaxf(fmaxf(t1, sacc[1][6]), sacc[1][7]);
-                t2 = fmaxf(fmaxf(t2, sacc[1][8]), sacc[1][9]);
-                t3 = fmaxf(fmaxf(t3, sacc[1][10]), sacc[1][11]);
-                t0 = fmaxf(fmaxf(t0, sacc[1][12]), sacc[1][13]);
-                t1 = fmaxf(fmaxf(t1, sacc[1][14]), sacc[1][15]);
-                mx = xhalf_max(fmaxf(fmaxf(t0, t1), fmaxf(t2, t3)));
-            }
-            // lazy running-max update; O holds every product up to tile t-1 here
-            const float mxs = (mx == -__builtin_inff()) ? -__builtin_inff() : mx * c;
-            const float alpha = raise_max(m_run, mxs);
-            if (__ballot(alpha != 1.f)) {
-    #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    l_part[i] *= alpha;
-                    w_part[i] *= alpha;
+        };
+        // the online softmax of attn_fwd_kernel, row for row (O holds every
+        // product up to tile t-1 here). A wavefront whose rows have all seen
+        // no key yet finds the row maximum directly; otherwise, when a row
+        // needs a raise of its maximum, the scores are formed again from tile
+        // t, still in LDS. Either way each row takes the same steps as there.
+        auto softmax = [&](int t) __attribute__((always_inline)) {
+            mask(t);
+            float tl[4];
+            bool need = true, redo = true;
+            if (__ballot(m_run == -__builtin_inff()) != __builtin_amdgcn_read_exec()) {
+                need = softmax_exps(sacc, c, m_run, tl, pk);
+                redo = __ballot(need) != 0;
+                if (redo) {
+                    s_part(t);
+                    mask(t);
                 }
-    #pragma unroll
-                for (int cb = 0; cb < D / 32; ++cb)
-    #pragma unroll
-                    for (int i = 0; i < 16; ++i) oacc[cb][i] *= alpha;
             }
-            const float moff = (m_run == -__builtin_inff()) ? 0.f : m_run;
-    #pragma unroll
-            for (int mb = 0; mb < 2; ++mb)
-    #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mb][i], c, -moff));
-                    l_part[i & 3] += x;
-                    pk[mb * 2 + (i >> 3)][i & 7] = (__bf16)x;
-                }
-    #pragma unroll
-            for (int r = 0; r < 4; ++r) add_bf16x8(pk[r], w_part);
+            if (redo) softmax_raise(sacc, c, m_run, need, l_part, w_part, oacc, tl, pk);
+            softmax_commit(l_part, w_part, tl, pk);
         };
         auto product_phase = [&](int t) __attribute__((always_inline)) {
             __builtin_amdgcn_s_setprio(1);
