@@ -33,12 +33,16 @@
 //    registers of a lane hold runs of 8 consecutive keys and the output
 //    registers hold runs of 8 consecutive head-dimension columns.
 //  * Online softmax in base 2 with scale*log2(e) folded into one FMA, and a
-//    lazily updated integral row maximum: the running maximum is only raised
-//    (and the accumulator rescaled by an exact power of two) when a row's new
-//    maximum exceeds it by more than 2^8, and then to an integer. Every row's
-//    final O = acc / l uses the same maximum for numerator and denominator,
-//    so the result is the same exact softmax, and tilings that meet other
-//    maxima round the same probabilities to bf16 (see raise_max).
+//    lazily updated integral row maximum, raised (and the accumulator
+//    rescaled by an exact power of two) to an integer only when a row needs
+//    it. The prefill kernels form a tile's probabilities against the maximum
+//    as it stands and raise it only on a row's first visible key or when a
+//    partial sum of the tile's probabilities exceeds 2^20 (softmax_exps), so
+//    no per-tile row maximum is needed; the decode kernel raises when the
+//    tile's row maximum exceeds the running one by more than 2^8 (raise_max).
+//    Every row's final O = acc / l uses the same maximum for numerator and
+//    denominator, so the result is the same exact softmax, and tilings that
+//    meet other integral maxima round the same probabilities to bf16.
 //  * Causal tiles above the diagonal are never loaded; waves whose rows see
 //    none of a tile's keys skip its arithmetic; only boundary tiles evaluate
 //    the mask.
@@ -393,14 +397,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         // online softmax: the running maximum is raised only for rows that
         // need it (softmax_exps, always on a row's first visible key); then
         // the wavefront forms the scores again from the tile still in LDS
-        // (one more pass over the tile keeps the accumulators in one set of
-        // registers at this kernel's register budget)
+        // (bf16 at d=128 also on the item's first tile: keeping the first
+        // scores live past the fast path spilled registers there)
         bf16x8 pk[4];
         float tl[4];
-        const bool need = softmax_exps(sacc, c, m_run, tl, pk);
-        if (__ballot(need)) {
-            scores();
-            softmax_raise(sacc, c, m_run, need, l_part, w_part, oacc, tl, pk);
+        if constexpr (D == 64 || QK8) {
+            // registers to spare: a wavefront whose rows have all seen no
+            // key yet (the item's first tile) finds the maximum directly
+            bool need = true, redo = true;
+            if (__ballot(m_run == -__builtin_inff()) != __builtin_amdgcn_read_exec()) {
+                need = softmax_exps(sacc, c, m_run, tl, pk);
+                redo = __ballot(need) != 0;
+                if (redo) scores();
+            }
+            if (redo) softmax_raise(sacc, c, m_run, need, l_part, w_part, oacc, tl, pk);
+        } else {
+            const bool need = softmax_exps(sacc, c, m_run, tl, pk);
+            if (__ballot(need)) {
+                scores();
+                softmax_raise(sacc, c, m_run, need, l_part, w_part, oacc, tl, pk);
+            }
         }
         softmax_commit(l_part, w_part, tl, pk);
 
