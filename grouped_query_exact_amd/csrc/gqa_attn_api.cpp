@@ -256,6 +256,7 @@ int run(const Call& c) {
     p.units_per_b = plan.units_per_b;
     p.ns = plan.ns;
     p.grid = (int)plan.grid;
+    p.pair_rows = plan.pair_rows;
     // softmax(scale * s) = softmax(|scale| * (sign(scale) * s)): a negative
     // scale negates Q (exact in bf16). scale == 0 gives every visible key
     // the score 0, which the kernel reproduces exactly by reading Q as 0.

@@ -528,10 +528,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // waits only for tile t's copies at its top. Causal masking, the row/key bookkeeping, the lazy online
 // softmax in base 2 and the epilogue are those of attn_fwd_kernel.
 //
-// Causal launches give a workgroup two row tiles of one (batch, head unit),
-// rt and its mirror row_tiles-1-rt (variable-length calls: of one sequence,
-// from the work list), so that every workgroup reads about the same number
-// of key tiles; the second item's Q rows are copied into LDS during the
+// Causal launches whose pairs still give every compute unit one (p.pair_rows)
+// give a workgroup two row tiles of one (batch, head unit), rt and its
+// mirror row_tiles-1-rt (variable-length calls: of one sequence, from the
+// work list), so that every workgroup reads about the same number of key
+// tiles; the second item's Q rows are copied into LDS during the
 // first item's last two tiles and its first K/V tile while the first drains.
 template <int D, bool CAUSAL, bool PAGED, bool VARLEN>
 __global__ __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_pingpong_kernel(
@@ -560,7 +561,7 @@ __global__ __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2
     // it; variable-length calls: an entry of the scheduling kernel's work list
     // (causal: the pair of row tiles R_b-1-pr and pr of sequence b)
     int rt1, rt2 = -1, unit, b;
-    if (!VARLEN && !CAUSAL) {  // non-causal items all cost the same: one per workgroup
+    if (!VARLEN && (!CAUSAL || !p.pair_rows)) {  // one item per workgroup, heaviest first
         const int logical = xcd_remap(blockIdx.x, p.grid);
         rt1 = p.row_tiles - 1 - (logical % p.row_tiles);
         const int tmpu = logical / p.row_tiles;

@@ -170,8 +170,20 @@ int make_plan(const Shape& s, int pack_gqa, int num_splits, int num_cus, Plan* p
     p->grid = (long long)s.B * p->units_per_b * p->row_tiles * ns;
     // causal launches of the 8-wavefront kernel pair each row tile with its
     // mirror (row_tiles-1-rt) in one workgroup: equal key tiles per workgroup,
-    // and the light item's Q rows arrive while the heavy one finishes
-    if (p->pingpong && s.causal && !s.varlen) p->grid = (long long)s.B * p->units_per_b * ((p->row_tiles + 1) / 2);
+    // and the light item's Q rows arrive while the heavy one finishes. Only
+    // when the pairs still give every compute unit one: a chunk of new tokens
+    // against a long cached context has few row tiles of nearly equal cost,
+    // and pairing would leave half the GPU idle (measured on MI355X, 2048
+    // tokens against 65536 keys, Llama-2 heads: 2.81 ms paired on 128
+    // workgroups, against 1.92 ms unpaired on 256).
+    p->pair_rows = 0;
+    if (p->pingpong && s.causal && !s.varlen) {
+        const long long pairs = (long long)s.B * p->units_per_b * ((p->row_tiles + 1) / 2);
+        if (pairs >= cus) {
+            p->pair_rows = 1;
+            p->grid = pairs;
+        }
+    }
     if (p->grid > INT_MAX) return GQA_ERR_INVALID_ARG;
     const long long rows = (long long)s.B * s.Sq * s.Hq;
     if (ns > 1) {

@@ -82,6 +82,7 @@ struct Plan {
     int decode;         // 1: decode kernel (R <= kDecBlockM), 0: tiled kernel
     int pingpong;       // 1: the 8-wavefront tiled kernel (kPPBlockM rows), 0: 4 wavefronts
     int worklist;       // variable-length prefill: items from the scheduling kernel's work list
+    int pair_rows;      // causal batched 8-wavefront launches: two mirrored row tiles per workgroup
     int threads;        // threads per attention workgroup
     int block_m;        // query rows per tile
     int block_n;        // keys per tile

@@ -26,6 +26,7 @@ struct FwdParams {
     int units_per_b;    // Hk when packed, Hq otherwise
     int ns;             // key splits
     int grid;           // workgroups
+    int pair_rows;      // causal 8-wavefront launches: 1 = two row tiles (rt, row_tiles-1-rt) per workgroup
     float c;            // |scale| * log2(e), or 1 when scale == 0
     uint32_t qand;      // 0 when scale == 0 (Q read as zeros: every visible score is 0), else all ones
     uint32_t qsign;     // sign bits that negate Q (negative score factor): 0x80008000 bf16, 0x80808080 fp8; else 0

@@ -164,3 +164,23 @@ def test_random_shapes_bitwise():
             assert torch.equal(ov.view(B, Sq, Hq, d), ob), f"{tag} tiled={tiled}: O"
             assert torch.equal(lv.view(Hq, B, Sq).permute(1, 0, 2), lb), f"{tag} tiled={tiled}: LSE"
     assert ran >= 50, ran
+
+
+@pytest.mark.parametrize("shape", [(1, 2048, 8192, 32, 8, 128, 1), (2, 1000, 3000, 32, 8, 128, 1)],
+                         ids=["chunk2048_vs_8192", "B2_ragged1000_vs_3000"])
+def test_causal_unpaired_row_tiles(shape):
+    """Causal calls whose mirrored pairs of row tiles would not give every compute unit one (a
+    chunk of new tokens against a longer context) run one row tile per workgroup, heaviest
+    first: bit for bit the 4-wavefront kernel, and the oracle on sampled rows."""
+    import grouped_query_exact_amd as g
+    B, Sq, Sk, Hq, Hk, d, pack = shape
+    p = g.gqa_attn_plan(B, Sq, Sk, Hq, Hk, d, True, pack, 1, 256)
+    assert p["threads"] == 512 and p["grid"] == B * Hk * p["row_tiles"], p
+    q, k, v = _qkv(9990 + Sq, B, Sq, Sk, Hq, Hk, d)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    scale = gi.fp32(1 / math.sqrt(d))
+    O8, L8 = gpu_run(qd, kd, vd, True, scale, pack, 1)
+    with force_tiled():
+        O4, L4 = gpu_run(qd, kd, vd, True, scale, pack, 1)
+    assert torch.equal(O8, O4) and torch.equal(L8, L4), f"{shape}: differs from the 4-wavefront kernel"
+    compare_to_oracle(O8, L8, q, k, v, True, scale, rows=[0, 1, 255, 256, Sq // 2, Sq - 1], tag=f"{shape}")

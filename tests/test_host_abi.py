@@ -318,6 +318,10 @@ def test_plan_grid_and_workspace():
     assert (p["block_m"], p["threads"], p["row_tiles"], p["grid"]) == (256, 512, 32, 128 * 8 * 32)
     p = g.gqa_attn_plan(64, 1800, 1800, 32, 8, 128, True, 1, 1, 256)  # odd row tiles: the middle one alone
     assert (p["threads"], p["row_tiles"], p["grid"]) == (512, 29, 64 * 8 * 15)
+    # a chunk of 2048 tokens against 65536 keys: 256 row tiles would make only 128 pairs on
+    # 256 compute units, so each row tile gets its own workgroup
+    p = g.gqa_attn_plan(1, 2048, 65536, 32, 8, 128, True, 1, 1, 256)
+    assert (p["threads"], p["row_tiles"], p["grid"]) == (512, 32, 8 * 32)
     # ... only with at least two such items per compute unit (212 * 2 = 424 < 512 here)
     p = g.gqa_attn_plan(212, 77, 77, 6, 2, 64, False, 1, 1, 256)
     assert (p["block_m"], p["threads"], p["grid"]) == (128, 256, 212 * 2 * 2)
@@ -407,7 +411,11 @@ int main() {
         if (p.pingpong != want8) { std::printf("bad 8-wave choice\n"); return 1; }
         if (p.block_m != (p.decode ? kDecBlockM : (p.pingpong ? kPPBlockM : kBlockM))) { std::printf("bad block_m\n"); return 1; }
         if (p.threads != (p.decode ? kDecThreads : (p.pingpong ? kPPThreads : kThreads))) { std::printf("bad threads\n"); return 1; }
-        const long long tiles_per_wg = (p.pingpong && causal) ? (p.row_tiles + 1) / 2 : p.row_tiles;  // mirrored pairs
+        // causal 8-wavefront launches pair mirrored row tiles when the pairs give every unit one
+        const long long pairs = (long long)B * p.units_per_b * ((p.row_tiles + 1) / 2);
+        const bool paired = p.pingpong && causal && pairs >= 256;
+        if (p.pair_rows != (paired ? 1 : 0)) { std::printf("bad pairing\n"); return 1; }
+        const long long tiles_per_wg = paired ? (p.row_tiles + 1) / 2 : p.row_tiles;
         if (p.grid != (long long)B * p.units_per_b * tiles_per_wg * p.ns) { std::printf("bad grid\n"); return 1; }
     }
     // fp8 K/V decode splits up to two workgroups per compute unit when each unit has at
