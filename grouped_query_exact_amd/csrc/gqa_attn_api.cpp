@@ -300,7 +300,7 @@ int run(const Call& c) {
                      plan.combine_grid, plan.workspace_bytes);
 
     auto launch = [&](bool split) {
-        if (plan.pingpong) return gqa::launch_pingpong(p, d, s.causal != 0, c.paged, c.varlen, c.stream);  // unsplit only
+        if (plan.pingpong) return gqa::launch_pingpong(p, d, s.causal != 0, c.paged, c.varlen, c.qk8, c.stream);  // unsplit only
         return plan.decode ? gqa::launch_decode(p, d, s.causal != 0, split, c.paged, c.kv8, c.varlen, c.stream)
                            : gqa::launch_attention(p, d, s.causal != 0, split, c.varlen, c.qk8, c.paged, c.stream);
     };

@@ -534,16 +534,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // work list), so that every workgroup reads about the same number of key
 // tiles; the second item's Q rows are copied into LDS during the
 // first item's last two tiles and its first K/V tile while the first drains.
-template <int D, bool CAUSAL, bool PAGED, bool VARLEN>
+//
+// QK8 (fp8 e4m3 Q and K, contiguous batched calls): the scores run on the
+// fp8 matrix cores as in attn_fwd_kernel's QK8 instantiation (the fp8 K tile
+// fills the first half of its stage slot, with that kernel's swizzle), and
+// the light item of a pair loads its own Q rows.
+template <int D, bool CAUSAL, bool PAGED, bool VARLEN, bool QK8>
 __global__ __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_pingpong_kernel(
     const FwdParams p) {
     static_assert(!(PAGED && VARLEN), "paged calls have one query length");
+    static_assert(!QK8 || (!PAGED && !VARLEN), "fp8 Q/K: contiguous batched calls");
     constexpr int TILE = kBlockN * D;
     constexpr int TILE_B = TILE * 2;
     constexpr int NCH = D / 8;
     constexpr int NLOAD = kBlockN * NCH / kPPThreads;  // 16-byte copies per thread per tensor and tile
+    constexpr int NCH8 = D / 16;                       // 16-byte chunks per fp8 K row
+    constexpr int NLOADK = QK8 ? kBlockN * NCH8 / kPPThreads : NLOAD;  // ... of the K tile
     constexpr int NS = kPPStages;
-    constexpr int COPIES = 2 * NLOAD;
+    constexpr int COPIES = NLOADK + NLOAD;
     static_assert(NS == 4, "the stage reuse and the wait counts below assume 4 stages");
     static_assert(kPPThreads == 512 && kPPBlockM == 256, "8 wavefronts of 32 rows");
     static_assert(D == 128, "a 256-row Q tile fills two ring stages");
@@ -601,7 +609,9 @@ __global__ __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2
 
     // ---- K/V tile copies: fixed per-thread 16-byte chunks, scalar tile base
     const int64_t kv_stride_b = (int64_t)p.Hk * D * 2;
-    const char* kbase = (const char*)(p.k + (PAGED ? (int64_t)g * D : (ktok0 * p.Hk + g) * D));
+    const int64_t k_stride_b = QK8 ? (int64_t)p.Hk * D : kv_stride_b;
+    const char* kbase = QK8 ? (const char*)p.k + (ktok0 * p.Hk + g) * D
+                            : (const char*)(p.k + (PAGED ? (int64_t)g * D : (ktok0 * p.Hk + g) * D));
     const char* vbase = (const char*)(p.v + (PAGED ? (int64_t)g * D : (ktok0 * p.Hk + g) * D));
     uint32_t goff[NLOAD];
 #pragma unroll
@@ -611,11 +621,30 @@ __global__ __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2
         const int logical_ch = (ci % NCH) ^ swz<D>(row);
         goff[u] = (uint32_t)(row * kv_stride_b + logical_ch * 16);
     }
+    // fp8 K: chunk ci of the tile is row ci / NCH8, stored at its position in
+    // the row, holding the global chunk the row's swizzle puts there
+    uint32_t goffk[QK8 ? NLOADK : 1];
+    if constexpr (QK8) {
+#pragma unroll
+        for (int u = 0; u < NLOADK; ++u) {
+            const int ci = (u * 8 + wave) * 64 + lane;
+            const int row = ci / NCH8;
+            goffk[u] = (uint32_t)(row * k_stride_b + ((ci % NCH8) ^ swz8<D>(row)) * 16);
+        }
+    }
     // ---- per-lane LDS operand offsets (as in attn_fwd_kernel)
     const int krow0 = pi32(col);
-    uint32_t kofs[D / 16];
+    uint32_t kofs[QK8 ? 1 : D / 16];
+    uint32_t kofs8[QK8 ? D / 64 : 1][2];  // fp8: operand t, 16-byte halves of the lane's 32 bytes
+    if constexpr (!QK8) {
 #pragma unroll
-    for (int dc = 0; dc < D / 16; ++dc) kofs[dc] = krow0 * (D * 2) + (((2 * dc + half) ^ swz<D>(krow0)) * 16);
+        for (int dc = 0; dc < D / 16; ++dc) kofs[dc] = krow0 * (D * 2) + (((2 * dc + half) ^ swz<D>(krow0)) * 16);
+    } else {
+#pragma unroll
+        for (int t = 0; t < D / 64; ++t)
+#pragma unroll
+            for (int e = 0; e < 2; ++e) kofs8[t][e] = krow0 * D + (((4 * t + 2 * half + e) ^ swz8<D>(krow0)) * 16);
+    }
     const int u16 = lane & 15, qq = (lane >> 4) & 1;
     const int rho = ((u16 & 1) << 1) | ((u16 >> 1) & 1);
     uint32_t vofs[D / 32][2];
@@ -659,7 +688,7 @@ __global__ __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2
         const int iw_min = (int)fdiv((uint32_t)min(rw0, R - 1), p.gmul, p.gshift);
         const int iw_max = (int)fdiv((uint32_t)(min(rw0 + 32, R) - 1), p.gmul, p.gshift);
         // the next item (if any) is staged through LDS when this one has at least two tiles
-        const bool stage_next = item == 0 && rt2 >= 0 && nt >= 2;
+        const bool stage_next = !QK8 && item == 0 && rt2 >= 0 && nt >= 2;
 
         // the LDS destination is uniform; it is passed through a scalar register
         auto stage_dst = [&](int t, int tensor, int u) __attribute__((always_inline)) {
@@ -698,8 +727,32 @@ __global__ __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2
                 }
                 return;
             }
-            const char* kg = kbase + kv0 * kv_stride_b;
+            const char* kg = kbase + kv0 * k_stride_b;
             const char* vg = vbase + kv0 * kv_stride_b;
+            if constexpr (QK8) {
+                if (kv0 + kBlockN <= Sk) {
+#pragma unroll
+                    for (int u = 0; u < NLOADK; ++u) lds_dma16(kg, goffk[u], dst(0, u));
+#pragma unroll
+                    for (int u = 0; u < NLOAD; ++u) lds_dma16(vg, goff[u], dst(1, u));
+                } else {  // ragged last tile: rows past the end re-read the last key (masked later)
+#pragma unroll
+                    for (int u = 0; u < NLOADK; ++u) {
+                        const int ci = (u * 8 + wave) * 64 + lane;
+                        const int row = ci / NCH8;
+                        const int key = min(kv0 + row, Sk - 1) - kv0;
+                        lds_dma16(kg, (uint32_t)(key * k_stride_b + ((ci % NCH8) ^ swz8<D>(row)) * 16), dst(0, u));
+                    }
+#pragma unroll
+                    for (int u = 0; u < NLOAD; ++u) {
+                        const int ci = (u * 8 + wave) * 64 + lane;
+                        const int row = ci / NCH;
+                        const int key = min(kv0 + row, Sk - 1) - kv0;
+                        lds_dma16(vg, (uint32_t)(key * kv_stride_b + ((ci % NCH) ^ swz<D>(row)) * 16), dst(1, u));
+                    }
+                }
+                return;
+            }
             if (kv0 + kBlockN <= Sk) {
 #pragma unroll
                 for (int u = 0; u < NLOAD; ++u) {
@@ -740,8 +793,22 @@ __global__ __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2
         };
 
         // ---- prologue: the Q rows (B operand of S^T = K Q^T), tiles 0 and 1
-        bf16x8 qreg[D / 16];
-        if (!q_staged) {
+        bf16x8 qreg[QK8 ? 1 : D / 16];
+        i32x8 q8reg[QK8 ? D / 64 : 1];  // fp8: operand t holds d 64t .. 64t+63, lane half h bytes 32h ..
+        if constexpr (QK8) {
+            if (item > 0) __syncthreads();  // every wavefront is done with the previous item's stages
+            if (nt > 0) issue(0);
+            const uint8_t* qrow = (const uint8_t*)p.q + ((qtok0 + ti) * p.Hq + hh) * D;
+#pragma unroll
+            for (int t = 0; t < D / 64; ++t) {
+                const u32x4 w0 = (*(const u32x4*)(qrow + 64 * t + 32 * half) & p.qand) ^ p.qsign;
+                const u32x4 w1 = (*(const u32x4*)(qrow + 64 * t + 32 * half + 16) & p.qand) ^ p.qsign;
+                // wait for Q here (16-byte operands: the host pass checks the constraint too)
+                asm volatile("" ::"v"(w0), "v"(w1));
+                q8reg[t] = i32x8{(int)w0[0], (int)w0[1], (int)w0[2], (int)w0[3], (int)w1[0], (int)w1[1], (int)w1[2], (int)w1[3]};
+            }
+            if (nt > 1) issue(1);
+        } else if (!q_staged) {
             if (item > 0) __syncthreads();  // every wavefront is done with the previous item's stages
             if (nt > 0) issue(0);
             const uint16_t* qrow = p.q + ((qtok0 + ti) * p.Hq + hh) * D;
@@ -791,6 +858,24 @@ __global__ __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2
             const LDS char* kt = lds + ((ring + t) & (NS - 1)) * 2 * TILE_B;
     #pragma unroll
             for (int mb = 0; mb < 2; ++mb) sacc[mb] = f32x16{};
+            if constexpr (QK8) {  // all eight operand reads first, then the four fp8 products
+                i32x8 a[2][D / 64];
+    #pragma unroll
+                for (int mb = 0; mb < 2; ++mb)
+    #pragma unroll
+                    for (int tt = 0; tt < D / 64; ++tt) {
+                        const u32x4 a0 = *(const LDS u32x4*)(kt + kofs8[tt][0] + mb * 32 * D);
+                        const u32x4 a1 = *(const LDS u32x4*)(kt + kofs8[tt][1] + mb * 32 * D);
+                        a[mb][tt] = i32x8{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+                    }
+    #pragma unroll
+                for (int mb = 0; mb < 2; ++mb)
+    #pragma unroll
+                    for (int tt = 0; tt < D / 64; ++tt)
+                        // e4m3 x e4m3 (format 0 for A and B), block scale exponents 127 = 1.0
+                        sacc[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[mb][tt], q8reg[tt], sacc[mb], 0, 0, 0, 127, 0, 127);
+                return;
+            }
     #pragma unroll
             for (int dc = 0; dc < D / 16; ++dc)
     #pragma unroll
@@ -1434,16 +1519,18 @@ hipError_t launch_attention(const FwdParams& p, int d, bool causal, bool split, 
                     : launch_attn_dd<64>(p, causal, split, varlen, qk8, paged, stream);
 }
 
-template <bool CAUSAL, bool PAGED, bool VARLEN>
+template <bool CAUSAL, bool PAGED, bool VARLEN, bool QK8 = false>
 static void launch_pp(const FwdParams& p, hipStream_t stream) {
-    hipLaunchKernelGGL((attn_fwd_pingpong_kernel<128, CAUSAL, PAGED, VARLEN>), dim3(p.grid), dim3(kPPThreads), 0,
+    hipLaunchKernelGGL((attn_fwd_pingpong_kernel<128, CAUSAL, PAGED, VARLEN, QK8>), dim3(p.grid), dim3(kPPThreads), 0,
                        stream, p);
 }
 
 // d=128 only (the plan never picks this kernel at d=64)
-hipError_t launch_pingpong(const FwdParams& p, int d, bool causal, bool paged, bool varlen, hipStream_t stream) {
-    if (d != 128 || (paged && varlen)) return hipErrorInvalidValue;
-    if (paged) causal ? launch_pp<true, true, false>(p, stream) : launch_pp<false, true, false>(p, stream);
+hipError_t launch_pingpong(const FwdParams& p, int d, bool causal, bool paged, bool varlen, bool qk8,
+                           hipStream_t stream) {
+    if (d != 128 || (paged && varlen) || (qk8 && (paged || varlen))) return hipErrorInvalidValue;
+    if (qk8) causal ? launch_pp<true, false, false, true>(p, stream) : launch_pp<false, false, false, true>(p, stream);
+    else if (paged) causal ? launch_pp<true, true, false>(p, stream) : launch_pp<false, true, false>(p, stream);
     else if (varlen) causal ? launch_pp<true, false, true>(p, stream) : launch_pp<false, false, true>(p, stream);
     else causal ? launch_pp<true, false, false>(p, stream) : launch_pp<false, false, false>(p, stream);
     return hipGetLastError();

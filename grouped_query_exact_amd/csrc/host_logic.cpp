@@ -128,7 +128,9 @@ int make_plan(const Shape& s, int pack_gqa, int num_splits, int num_cus, Plan* p
     // results bit for bit; for comparisons).
     const char* force_env = std::getenv("GQA_ATTN_FORCE_TILED");
     const bool force_tiled = force_env && force_env[0] && !(force_env[0] == '0' && !force_env[1]);
-    const bool pp_shape = !force_tiled && !p->decode && ns == 1 && s.d == 128 && s.q_bytes == 2 && s.kv_bytes == 2;
+    // fp8 Q/K calls (q_bytes == 1) take it for contiguous batched calls
+    const bool pp_qk = s.q_bytes == 2 || (s.q_bytes == 1 && !s.varlen && !s.paged);
+    const bool pp_shape = !force_tiled && !p->decode && ns == 1 && s.d == 128 && pp_qk && s.kv_bytes == 2;
     const long long cus = num_cus > 0 ? num_cus : 256;
     const bool pp_varlen = pp_shape && s.varlen &&
                            p->units_per_b * (ceil_div(s.total_q * p->Gp, kPPBlockM) + s.B) >= (long long)kPPMinItemsPerCU * cus;

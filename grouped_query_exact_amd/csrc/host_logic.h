@@ -66,7 +66,7 @@ inline uint32_t fastdiv_host(uint32_t n, const FastDiv& f) {
 struct Shape {
     int B, Sq, Sk, Hq, Hk, d, causal;
     int kv_bytes = 2;  // bytes per stored K/V element: 2 (bf16) or 1 (fp8)
-    int q_bytes = 2;   // bytes per stored Q element: 2 (bf16) or 1 (fp8 Q and K: tiled kernel only)
+    int q_bytes = 2;   // bytes per stored Q element: 2 (bf16) or 1 (fp8 Q and K)
     int varlen = 0;    // packed sequences of different lengths (Sq, Sk: the bounds max_seqlen_q, max_seqlen_k)
     long long total_q = 0;  // variable-length calls: query tokens of all sequences
     int paged = 0;     // K/V in a pool of pages

@@ -130,3 +130,46 @@ def test_qk8_rejects_bad_factors():
     with pytest.raises(g.GqaAttnError) as e:
         g.gqa_attn_fwd_qk8(q8, k8, v, float("nan"), 1.0, out, None, True, 0.125)
     assert e.value.status == g.GQA_ERR_INVALID_ARG
+
+
+PP_SHAPES = [
+    # B, Sq, Sk, Hq, Hk, pack: at least 512 items of 256 packed rows (the 8-wavefront kernel)
+    (64, 256, 256, 8, 2, 1),
+    (64, 200, 333, 8, 2, 1),   # ragged rows and keys, Sq != Sk
+    (64, 300, 300, 6, 2, 1),   # G = 3
+    (32, 512, 448, 8, 2, 0),   # unpacked
+    (64, 300, 100, 8, 2, 1),   # causal: tokens 0..199 see no key
+    (16, 1800, 1800, 8, 2, 1), # causal pairs with an odd middle tile
+]
+
+
+@pytest.mark.parametrize("shape", PP_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_qk8_8_wavefront_kernel(shape):
+    """Large unsplit calls run on the 8-wavefront kernel with fp8 scores: bit for bit the
+    4-wavefront kernel (GQA_ATTN_FORCE_TILED=1) at unit, fractional and negative factors, and the
+    oracle on sampled rows (every row for the first shape)."""
+    import grouped_query_exact_amd as g
+    from _parity import force_tiled
+    B, Sq, Sk0, Hq, Hk, pack = shape
+    d = 128
+    scale = gi.fp32(1 / math.sqrt(d))
+    for causal in (True, False):
+        Sk = Sk0 if causal or Sk0 > 8 * 64 else Sk0 + 576  # non-causal rows of <= 8 key tiles keep 4 wavefronts
+        assert g.gqa_attn_plan(B, Sq, Sk, Hq, Hk, d, causal, pack, 1)["threads"] == 512
+        seed = 9900 + Sq + Sk + Hq
+        q8, k8 = gi.random_fp8(seed, (B, Sq, Hq, d)), gi.random_fp8(seed + 1, (B, Sk, Hk, d))
+        v = gi.random_bf16(seed + 2, (B, Sk, Hk, d))
+        for qs, ks in ((1.0, 1.0), (0.37, -2.5)):
+            O8, L8 = run_qk8(q8, k8, v, qs, ks, causal, scale, pack, 1)
+            with force_tiled():
+                O4, L4 = run_qk8(q8, k8, v, qs, ks, causal, scale, pack, 1)
+            tag = f"{shape} causal={causal} qs={qs} ks={ks}"
+            assert torch.equal(O8, O4) and torch.equal(L8, L4), f"{tag}: differs from the 4-wavefront kernel"
+            if qs == 1.0:
+                rows = None if shape == PP_SHAPES[0] else sorted({0, 1, Sq // 3, Sq // 2, Sq - 2, Sq - 1})
+                bs = None if shape == PP_SHAPES[0] else [0, B - 1]
+                Or, Lr = oracle.attention_qk8_fp64(q8.numpy(), k8.numpy(), f64(v), qs, ks, causal, scale, rows=rows,
+                                                   batches=bs)
+                Og = O8.cpu() if rows is None else O8.cpu()[bs][:, rows]
+                Lg = L8.cpu() if rows is None else L8.cpu()[bs][:, :, rows]
+                check(Og, Lg, Or, Lr, tag)
