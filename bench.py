@@ -257,7 +257,7 @@ def extra_prefill(g, gi, dev, steps):
     out["sweep_b128_fp8_qk"] = rate_entry(t, flops=w128.flops, peak_tflops=mixed_peak,
                                           peak_note=f"mixed peak {mixed_peak:.0f} TFLOP/s: QK^T at fp8 5.0 PF, "
                                                     f"P V at bf16 2.5 PF",
-                                          kernel="attn_fwd_kernel (fp8 Q/K scores, bf16 P V)")
+                                          kernel="attn_fwd_pingpong_kernel (fp8 Q/K scores, bf16 P V)")
     log(f"fp8 Q/K sweep B=128: median {t['median']:.4f} ms")
     del q8, k8, o8, l8, qb, kb, vb
     torch.cuda.empty_cache()

@@ -278,8 +278,8 @@ int gqa_attn_fwd_paged_kv8(const void* q, const void* k_cache, const void* v_cac
  * in the fp32 accumulation, and P V on the bf16 products exactly as
  * gqa_attn_fwd: the same tolerances as the bf16 path apply. Quantising Q and
  * K to e4m3 is the caller's step. q_scale, k_scale: any finite fp32 values
- * (INVALID_ARG otherwise). Every shape runs on the tiled kernel (no decode
- * specialisation); other rules as for gqa_attn_fwd. */
+ * (INVALID_ARG otherwise). Decode-shaped calls run on the tiled kernel (no
+ * decode specialisation); other rules as for gqa_attn_fwd. */
 int gqa_attn_fwd_qk8(const void* q, const void* k, const void* v, float q_scale, float k_scale,
                      void* out, float* lse, int B, int Sq, int Sk, int Hq, int Hk, int d,
                      int causal, float scale, int pack_gqa, int num_splits, hipStream_t stream);
