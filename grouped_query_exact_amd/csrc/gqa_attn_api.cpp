@@ -9,6 +9,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <mutex>
+#include <utility>
 
 #include "../../include/gqa_attn.h"
 #include "host_logic.h"
@@ -80,43 +81,58 @@ hipError_t ws_alloc(void** ptr, size_t bytes, int dev, hipStream_t stream) {
 // the GPU idle for several microseconds between the kernels of consecutive
 // split decode calls). A call that needs more than the stream's buffer
 // holds releases it after the work already enqueued on that stream and
-// takes a larger one, stream-ordered. At most kWsCacheEntries streams get a
+// takes a larger one, stream-ordered. A call holds its stream's buffer
+// (a lock of its own) from the lookup until its kernels are enqueued, so
+// host threads that share a stream cannot release a buffer between another
+// call's lookup and its launches. At most kWsCacheEntries streams get a
 // kept buffer; calls on further streams, calls being captured into a graph
 // and calls that need more than kWsCacheBytes allocate and release their
 // workspace per call, as before. Kept buffers live until the process ends.
 constexpr size_t kWsCacheBytes = 64ull << 20;
 constexpr int kWsCacheEntries = 16;
 struct WsEntry {
-    int dev;
-    hipStream_t stream;
-    void* ptr;
-    size_t bytes;
+    int dev = -1;
+    hipStream_t stream = nullptr;
+    void* ptr = nullptr;
+    size_t bytes = 0;
+    std::mutex mu;  // held by the call using the buffer
 };
-std::mutex g_ws_mu;
+std::mutex g_ws_mu;  // the table (lookup and insertion)
 WsEntry g_ws[kWsCacheEntries];
 int g_ws_used = 0;
 
+// A call's workspace: a kept buffer (held through `hold` until the lease
+// ends) or a per-call allocation (released by the caller with hipFreeAsync).
+struct WsLease {
+    void* ptr = nullptr;
+    bool kept = false;
+    std::unique_lock<std::mutex> hold;
+};
+
 // A workspace of `bytes` for work enqueued on `stream` of device `dev`.
-// *kept tells whether it is a kept buffer (not to be released by the caller)
-// or a per-call allocation (to be released with hipFreeAsync on `stream`).
-hipError_t ws_acquire(void** ptr, size_t bytes, int dev, hipStream_t stream, bool* kept) {
-    *kept = false;
+hipError_t ws_acquire(size_t bytes, int dev, hipStream_t stream, WsLease* lease) {
+    lease->ptr = nullptr;
+    lease->kept = false;
     hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
     if (hipStreamIsCapturing(stream, &cap) != hipSuccess) {
         (void)hipGetLastError();
         cap = hipStreamCaptureStatusActive;  // unknown: take the per-call path
     }
-    if (bytes > kWsCacheBytes || cap != hipStreamCaptureStatusNone) return ws_alloc(ptr, bytes, dev, stream);
-    std::lock_guard<std::mutex> lock(g_ws_mu);
+    if (bytes > kWsCacheBytes || cap != hipStreamCaptureStatusNone) return ws_alloc(&lease->ptr, bytes, dev, stream);
     WsEntry* e = nullptr;
-    for (int i = 0; i < g_ws_used; ++i)
-        if (g_ws[i].dev == dev && g_ws[i].stream == stream) e = &g_ws[i];
-    if (!e) {
-        if (g_ws_used == kWsCacheEntries) return ws_alloc(ptr, bytes, dev, stream);
-        e = &g_ws[g_ws_used];
-        *e = WsEntry{dev, stream, nullptr, 0};
-        ++g_ws_used;
+    {
+        std::lock_guard<std::mutex> lock(g_ws_mu);
+        for (int i = 0; i < g_ws_used; ++i)
+            if (g_ws[i].dev == dev && g_ws[i].stream == stream) e = &g_ws[i];
+        if (!e) {
+            if (g_ws_used == kWsCacheEntries) return ws_alloc(&lease->ptr, bytes, dev, stream);
+            e = &g_ws[g_ws_used];
+            e->dev = dev;
+            e->stream = stream;
+            ++g_ws_used;
+        }
     }
+    std::unique_lock<std::mutex> hold(e->mu);
     if (e->bytes < bytes) {
         // grow in steps of 1 MiB, at least doubling, up to the cap
         size_t want = std::max(bytes, std::min(2 * e->bytes, kWsCacheBytes));
@@ -131,8 +147,9 @@ hipError_t ws_acquire(void** ptr, size_t bytes, int dev, hipStream_t stream, boo
         e->ptr = fresh;
         e->bytes = want;
     }
-    *ptr = e->ptr;
-    *kept = true;
+    lease->ptr = e->ptr;
+    lease->kept = true;
+    lease->hold = std::move(hold);
     return hipSuccess;
 }
 
@@ -330,7 +347,7 @@ int run(const Call& c) {
     }
 
     void* ws = nullptr;
-    bool ws_kept = false;
+    WsLease lease;  // a kept buffer stays held until this call's kernels are enqueued
     const size_t split_bytes = plan.ns == 1 ? 0
                                : c.varlen ? (size_t)plan.ns * (size_t)c.total_q * s.Hq * ((size_t)d * 4 + 8)
                                           : (size_t)plan.workspace_bytes;
@@ -341,10 +358,11 @@ int run(const Call& c) {
         if (ws_bytes > (size_t)gqa::kScratchBytes) return GQA_ERR_SCRATCH;
         if (gqa::scratch_address(dev, &ws) != hipSuccess || !ws) return GQA_ERR_HIP;
     } else {
-        if (ws_acquire(&ws, ws_bytes, dev, c.stream, &ws_kept) != hipSuccess || !ws) {
+        if (ws_acquire(ws_bytes, dev, c.stream, &lease) != hipSuccess || !lease.ptr) {
             (void)hipGetLastError();
             return GQA_ERR_NOMEM;
         }
+        ws = lease.ptr;
     }
     const int64_t rows = c.varlen ? (int64_t)c.total_q * s.Hq : (int64_t)s.B * s.Sq * s.Hq;
     hipError_t e = hipSuccess;
@@ -397,7 +415,7 @@ int run(const Call& c) {
         if (cgrid > INT_MAX) e = hipErrorInvalidValue;
         else e = gqa::launch_combine(cp, d, cgrid, c.stream);
     }
-    const hipError_t ef = (c.noalloc || ws_kept) ? hipSuccess : hipFreeAsync(ws, c.stream);
+    const hipError_t ef = (c.noalloc || lease.kept) ? hipSuccess : hipFreeAsync(ws, c.stream);
     if (e != hipSuccess || ef != hipSuccess) return GQA_ERR_HIP;
     return GQA_OK;
 }
@@ -498,15 +516,16 @@ int gqa_attn_bwd(const void* q, const void* k, const void* v, const void* out, c
         void* ws = nullptr;
         const size_t rows = (size_t)B * Hq * (size_t)(Sq > 0 ? Sq : 1);
         const size_t ws_bytes = 2 * rows * 4;  // D, then -LSE*log2(e)
-        bool ws_kept = false;
-        if (ws_acquire(&ws, ws_bytes, dev, stream, &ws_kept) != hipSuccess || !ws) {
+        WsLease lease;  // a kept buffer stays held until the kernels are enqueued
+        if (ws_acquire(ws_bytes, dev, stream, &lease) != hipSuccess || !lease.ptr) {
             (void)hipGetLastError();
             return GQA_ERR_NOMEM;
         }
+        ws = lease.ptr;
         p.drow = (float*)ws;
         p.nlse2 = (float*)ws + rows;
         const hipError_t e = gqa::launch_backward(p, d, causal != 0, stream);
-        const hipError_t ef = ws_kept ? hipSuccess : hipFreeAsync(ws, stream);
+        const hipError_t ef = lease.kept ? hipSuccess : hipFreeAsync(ws, stream);
         if (e != hipSuccess || ef != hipSuccess) return GQA_ERR_HIP;
         return GQA_OK;
     } catch (...) {

@@ -98,3 +98,48 @@ def test_workspace_past_the_kept_limit_is_per_call():
     torch.cuda.synchronize()
     assert_variants_agree(O3, L3, O1, L1, float(v.float().abs().max()), tag="ns=3 per-call workspace vs unsplit")
     compare_to_oracle(O3, L3, q, k, v, w.causal, w.scale, rows=[0, 1, 777, 2047], tag="ns=3 per-call")
+
+
+def test_kept_workspace_shared_by_host_threads():
+    """Host threads that enqueue split calls of different sizes on one stream at the same time:
+    a call holds its stream's buffer from the lookup until its kernels are enqueued, so a growth by
+    another thread never releases a buffer between a call's lookup and its launches. Every output
+    equals the no-allocation entry point's, bit for bit."""
+    import threading
+    import grouped_query_exact_amd as g
+    s = torch.cuda.Stream(device=DEV)
+    cases = _cases()
+    inputs = []
+    for w, pack, ns in cases:
+        q, k, v = gi.make_qkv(w)
+        qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+        ref = _bufs(qd)
+        g.gqa_attn_fwd_noalloc(qd, kd, vd, ref[0], ref[1], w.causal, w.scale, pack, ns)
+        inputs.append((w, pack, ns, qd, kd, vd, ref))
+    outs = [[] for _ in range(4)]
+    bufs = [[_bufs(x[3]) for _ in range(6) for x in inputs] for _ in range(4)]  # allocated up front
+    torch.cuda.synchronize()  # the NaN fills run on the default stream
+    errors = []
+
+    def worker(i):
+        try:
+            for r in range(6):
+                order = list(range(len(inputs))) if (i + r) % 2 == 0 else list(range(len(inputs)))[::-1]
+                for j in order:
+                    w, pack, ns, qd, kd, vd, ref = inputs[j]
+                    O, L = bufs[i][r * len(inputs) + j]
+                    g.gqa_attn_fwd(qd, kd, vd, O, L, w.causal, w.scale, pack, ns, stream=s)
+                    outs[i].append((w, ns, O, L, ref))
+        except Exception as e:  # reported below, on the test's own thread
+            errors.append(repr(e))
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(4)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for per in outs:
+        for w, ns, O, L, ref in per:
+            assert torch.equal(O, ref[0]) and torch.equal(L, ref[1]), f"{w.name} ns={ns}: threads sharing a stream differ"
