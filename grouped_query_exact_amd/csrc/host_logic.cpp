@@ -177,7 +177,7 @@ int make_plan(const Shape& s, int pack_gqa, int num_splits, int num_cus, Plan* p
     // against a long cached context has few row tiles of nearly equal cost,
     // and pairing would leave half the GPU idle (measured on MI355X, 2048
     // tokens against 65536 keys, Llama-2 heads: 2.81 ms paired on 128
-    // workgroups, against 1.92 ms unpaired on 256).
+    // workgroups, 1.9-2.0 ms unpaired on 256).
     p->pair_rows = 0;
     if (p->pingpong && s.causal && !s.varlen) {
         const long long pairs = (long long)s.B * p->units_per_b * ((p->row_tiles + 1) / 2);
