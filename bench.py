@@ -385,7 +385,7 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py measures one GPU only: this build runs the attention on a single MI355X "
+        print(f"bench.py measures one GPU only: the attention runs on a single MI355X "
               f"(asked for --gpus {args.gpus}, WORLD_SIZE={world}).", file=sys.stderr)
         sys.exit(2)
 

@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Kernel traces, HBM traffic and pipe counters of the GQA kernels (rocprofv3).
 
-    python bench_traffic.py [--out-dir gpurun_out/traffic] [--workloads NAME ...]
+    python bench_traffic.py [--out-dir DIR] [--workloads NAME ...]   (DIR defaults to traffic_out/)
 
 For each workload below, a child process of this script (``--child NAME``)
 makes WARMUP calls and then MEASURED calls of one entry point on seeded
@@ -291,7 +291,7 @@ def profile_workload(name, out, prof_out, fscale, wscale, copy_cmds):
           f"At least {WARMUP} warm-up calls and {WARMUP_SECONDS} s of them, then {MEASURED} measured calls per "
           f"profiled run, seeded N(0,1) inputs on the GPU. "
           f"Forward kernel source hash {src_hash()}, backward source hash {src_hash(BWD_SRCS)}.", "",
-          "Commands (REPO = repository root on the GPU box, run from /tmp with TMPDIR=/tmp):", ""]
+          "Commands (REPO = repository root, run from /tmp with TMPDIR=/tmp):", ""]
     md += ["    " + c.replace(ROOT, "$REPO") for c in list(cmds.values()) + copy_cmds]
     md += ["", f"Kernel trace (rocprofv3 --kernel-trace; statistics over the {MEASURED} measured calls):", "",
            "| kernel | dispatches | median (us) | mean (us) | min (us) | max (us) |", "|---|---|---|---|---|---|"]
@@ -339,7 +339,7 @@ def bench_trace(out, prof_out):
     md = ["# sweep_b128_s2048: the headline measurement under the kernel trace", "",
           f"The command bench.py times (causal B=128, Sq=Sk=2048, Hq=32, Hk=8, d=128; {res['warmup']} warm-up and "
           f"{res['steps']} timed launches), traced. Forward kernel source hash {src_hash()}.", "",
-          "Command (REPO = repository root on the GPU box, run from /tmp with TMPDIR=/tmp):", "",
+          "Command (REPO = repository root, run from /tmp with TMPDIR=/tmp):", "",
           "    " + cmd.replace(ROOT, "$REPO"), "",
           "| kernel | dispatches | median of the timed launches (us) | mean of the timed launches (us) | "
           "mean of all (us) |", "|---|---|---|---|---|"]
@@ -357,7 +357,7 @@ def bench_trace(out, prof_out):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--child", help=argparse.SUPPRESS)
-    ap.add_argument("--out-dir", default=os.path.join(ROOT, "gpurun_out", "traffic"))
+    ap.add_argument("--out-dir", default=os.path.join(ROOT, "traffic_out"))
     ap.add_argument("--workloads", nargs="*", default=list(WORKLOADS))
     ap.add_argument("--bench-trace", action="store_true")
     a = ap.parse_args()
