@@ -173,3 +173,40 @@ def test_qk8_8_wavefront_kernel(shape):
                 Og = O8.cpu() if rows is None else O8.cpu()[bs][:, rows]
                 Lg = L8.cpu() if rows is None else L8.cpu()[bs][:, :, rows]
                 check(Og, Lg, Or, Lr, tag)
+
+
+def test_qk8_random_shapes_bitwise():
+    """Seeded random shapes that the plan sends to the 8-wavefront kernel (group sizes 1-8, query and
+    key counts up to 3000, causal or not, paired and unpaired causal row tiles, three score
+    factors): the fp8 Q/K call equals, bit for bit, the same call on the 4-wavefront kernel."""
+    import numpy as np
+    import grouped_query_exact_amd as g
+    from _parity import force_tiled
+    ran = 0
+    d = 128
+    for seed in range(120):
+        rs = np.random.RandomState(81000 + seed)
+        Hk = int(rs.choice([1, 2, 4, 8]))
+        G = int(rs.choice([1, 2, 3, 4, 5, 8]))
+        Hq = G * Hk
+        Sq = int(rs.randint(1, 3000))
+        Sk = int(rs.choice([Sq, rs.randint(1, 3000)]))
+        causal = bool(rs.randint(0, 2))
+        B = int(rs.randint(1, 25))
+        if g.gqa_attn_plan(B, Sq, Sk, Hq, Hk, d, causal, -1, 0)["threads"] != 512:
+            continue
+        if B * Sq * Hq * d > 2.5e8 or B * Sk * Hk * d > 2.5e8:
+            continue
+        ran += 1
+        scale = float(rs.choice([1 / math.sqrt(d), 0.3, -0.05]))
+        gen = torch.Generator(device=DEV)
+        gen.manual_seed(seed)
+        q8 = torch.randn((B, Sq, Hq, d), generator=gen, device=DEV).to(torch.float8_e4m3fn).view(torch.uint8)
+        k8 = torch.randn((B, Sk, Hk, d), generator=gen, device=DEV).to(torch.float8_e4m3fn).view(torch.uint8)
+        v = torch.randn((B, Sk, Hk, d), generator=gen, device=DEV).to(torch.bfloat16)
+        O8, L8 = run_qk8(q8, k8, v, 1.0, 1.0, causal, scale)
+        with force_tiled():
+            O4, L4 = run_qk8(q8, k8, v, 1.0, 1.0, causal, scale)
+        tag = f"seed={seed} B={B} Sq={Sq} Sk={Sk} Hq={Hq} Hk={Hk} causal={causal}"
+        assert torch.equal(O8, O4) and torch.equal(L8, L4), tag
+    assert ran >= 30, ran
