@@ -690,14 +690,10 @@ __global__ __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2
         // the next item (if any) is staged through LDS when this one has at least two tiles
         const bool stage_next = !QK8 && item == 0 && rt2 >= 0 && nt >= 2;
 
-        // the LDS destination is uniform; it is passed through a scalar register
-        auto stage_dst = [&](int t, int tensor, int u) __attribute__((always_inline)) {
-            const uint32_t a = (uint32_t)(size_t)(lds + ((ring + t) & (NS - 1)) * 2 * TILE_B + tensor * TILE_B) + (u * 8 + wave) * 1024;
-            return (LDS void*)(size_t)__builtin_amdgcn_readfirstlane(a);
-        };
         // tile t of the item (t may run past nt-1 only through issue_next below)
         auto issue_kv = [&](int t, int ring_of_t) __attribute__((always_inline)) {
             const int kv0 = t * kBlockN;
+            // the LDS destination is uniform; it is passed through a scalar register
             auto dst = [&](int tensor, int u) __attribute__((always_inline)) {
                 const uint32_t a = (uint32_t)(size_t)(lds + ((ring_of_t + t) & (NS - 1)) * 2 * TILE_B + tensor * TILE_B) + (u * 8 + wave) * 1024;
                 return (LDS void*)(size_t)__builtin_amdgcn_readfirstlane(a);
