@@ -7,8 +7,8 @@ Variants (pack_gqa on/off, num_splits, tiled against decode kernel) against each
 The literal "variants agree within 1e-3" cannot hold for every bf16 output: where
 |O| >= 0.25 one bf16 step is 2^-9 = 1.95e-3, and two tilings of a row sum their fp32
 terms in another order, so a value near a rounding boundary can land one step apart.
-Both sides round every probability against an integral running maximum (the kernels'
-raise_max), so the probabilities themselves agree up to the last bit of the exponent
+Both sides round every probability against an integral running maximum (raised lazily,
+to an integer, in every kernel), so the probabilities themselves agree up to the last bit of the exponent
 argument; what remains are fp32 reassociation differences. Enforced:
   * every element: |dO| <= max(1e-3, 2 bf16 steps at max(|a|, |b|));
   * at most 0.1% of the elements differ by more than 1e-3;
